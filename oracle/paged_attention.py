@@ -1,0 +1,256 @@
+"""CPU oracle: batched causal prefill attention over a paged KV cache.
+
+TEST INFRASTRUCTURE.  This module is the slow, plain reference that the GPU
+path is checked against.  Only the test suite, the smoke check and the
+bench's CPU-baseline leg may import or run it; the library itself never
+does, and it shares no code with the HIP path.
+
+Everything is computed in float64 with NumPy, one request and one query head
+at a time, in the order the pages define the operation:
+
+1. decode the stored codes (bf16, or OCP float8 e4m3fn) to real values;
+2. gather each request's pages into a contiguous token-major K and V of
+   shape ``[kv_len, H_kv, D]`` - the VanillaAttention ``_gather_paged_kv``
+   step of the TensorRT-LLM attention-backend article (section "path 1:
+   VanillaAttention"), with a page id from ``block_tables[b, t // P]`` and the
+   slot ``t % P`` (FlashInfer API page, parameters ``kv_cache`` and
+   ``block_tables``; article section "physical meaning of handle -> offset");
+3. for each query head, logits ``bmm1_scale * q . k`` (API page, parameter
+   ``bmm1_scale``);
+4. the causal mask with the new queries at the end of the KV sequence
+   (``kv_len = cached prefix + new tokens``, article section on
+   TrtllmAttentionMetadata, and the chunked-context figure) and the inclusive
+   left window (API page, parameter ``window_left``; -1 means no window);
+5. softmax over the valid keys, with the per-head sink as an extra term of
+   the denominator only (API page, parameter ``sinks``);
+6. the weighted sum of V rows, times ``bmm2_scale`` (API page, parameter
+   ``bmm2_scale``).
+
+Readings taken where the pages are silent (each is listed with its reason in
+the design notes): GQA query head h reads kv head ``h // (H_q / H_kv)``; a
+sink is a logit in the same natural-log units as ``bmm1_scale * q . k``;
+a combined cache with one plane in dim 1 holds K and V in the same storage.
+Parity unpinned: the GQA head mapping and the units of the sink are
+conventions that no page prints a value for; they are pinned only against
+torch's SDPA grouping convention and against closed forms.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple, Union
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# 1. Decoding stored codes
+# ---------------------------------------------------------------------------
+
+
+def decode_bf16(codes: np.ndarray) -> np.ndarray:
+    """bf16 codes (uint16) -> float64.  A bf16 number is the upper half of an
+    IEEE binary32, so shifting the code into the top 16 bits is exact."""
+    c = np.asarray(codes, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):   # NaN codes stay NaN
+        return c.view(np.float32).astype(np.float64)
+
+
+def e4m3fn_value(code: int) -> float:
+    """One OCP float8 e4m3fn code -> its real value (OCP 8-bit floating point
+    specification): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+    exponent field 0 encodes subnormals m/8 * 2^-6; S.1111.111 is NaN; there
+    is no infinity, so the largest magnitude is 1.75 * 2^8 = 448."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    exp = (code >> 3) & 0xF
+    man = code & 0x7
+    if exp == 0xF and man == 0x7:
+        return float("nan")
+    if exp == 0:
+        return sign * (man / 8.0) * 2.0 ** (1 - 7)
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+
+
+E4M3FN_TABLE = np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
+    """float8 e4m3fn codes (uint8) -> float64 by table lookup."""
+    return E4M3FN_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+# ---------------------------------------------------------------------------
+# 2. Page gather
+# ---------------------------------------------------------------------------
+
+
+def _plane(kv_cache, kv_idx: int) -> np.ndarray:
+    """The K (kv_idx 0) or V (kv_idx 1) page pool of a decoded cache.
+
+    A tuple is (K pool, V pool).  A single array has the K/V planes in dim 1;
+    with only one plane there, K and V are read from the same storage."""
+    if isinstance(kv_cache, (tuple, list)):
+        return kv_cache[kv_idx]
+    nplanes = kv_cache.shape[1]
+    return kv_cache[:, kv_idx if nplanes == 2 else 0]
+
+
+def _page_rows(plane: np.ndarray, page_id: int, nslots: int, kv_layout: str) -> np.ndarray:
+    """The first ``nslots`` token rows of one page as ``[nslots, H_kv, D]``.
+    HND pages are ``[H_kv, P, D]``; NHD pages are ``[P, H_kv, D]``."""
+    page = plane[page_id]
+    if kv_layout == "HND":
+        return np.transpose(page[:, :nslots, :], (1, 0, 2))
+    if kv_layout == "NHD":
+        return page[:nslots]
+    raise ValueError(f"kv_layout must be HND or NHD, got {kv_layout!r}")
+
+
+def gather_paged_kv(kv_cache, block_ids: Sequence[int], kv_idx: int, num_tokens: int,
+                    page_size: int, kv_layout: str) -> np.ndarray:
+    """The first ``num_tokens`` logical K or V tokens of one request as a
+    contiguous ``[num_tokens, H_kv, D]`` array: logical token t lives in page
+    ``block_ids[t // page_size]`` at slot ``t % page_size``."""
+    plane = _plane(kv_cache, kv_idx)
+    rows = []
+    npages = (num_tokens + page_size - 1) // page_size
+    for j in range(npages):
+        nslots = min(page_size, num_tokens - j * page_size)
+        rows.append(_page_rows(plane, int(block_ids[j]), nslots, kv_layout))
+    if not rows:
+        return np.zeros((0,) + plane.shape[2:] if kv_layout == "NHD" else
+                        (0, plane.shape[1], plane.shape[3]), dtype=plane.dtype)
+    return np.concatenate(rows, axis=0)
+
+
+# ---------------------------------------------------------------------------
+# 3-6. Attention for one request
+# ---------------------------------------------------------------------------
+
+
+def _kv_head(h: int, num_qo_heads: int, num_kv_heads: int) -> int:
+    """GQA: the kv head that query head h reads (contiguous groups)."""
+    return h // (num_qo_heads // num_kv_heads)
+
+
+def _valid_mask(q_len: int, kv_len: int, window_left: int) -> np.ndarray:
+    """``[q_len, kv_len]`` bool.  Query row i sits at sequence position
+    ``prefix + i`` with ``prefix = kv_len - q_len``; it sees key j when
+    ``j <= prefix + i`` and, for ``window_left >= 0``, ``j >= prefix + i -
+    window_left`` (the left window is inclusive)."""
+    prefix = kv_len - q_len
+    i = np.arange(q_len)[:, None]
+    j = np.arange(kv_len)[None, :]
+    pos = prefix + i
+    valid = j <= pos
+    if window_left >= 0:
+        valid &= j >= pos - window_left
+    return valid
+
+
+def _softmax_weighted_sum(s: np.ndarray, valid: np.ndarray, v: np.ndarray,
+                          sink: Optional[float]) -> np.ndarray:
+    """Softmax of the valid logits of each row, the sink (if any) adding
+    ``exp(sink)`` to the denominator only, then the weighted sum of V rows.
+    The row maximum (taken over the valid logits and the sink) is subtracted
+    before exponentiating; that leaves every ratio unchanged."""
+    s = np.where(valid, s, -np.inf)
+    m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
+    if sink is not None:
+        m = np.maximum(m, sink)
+    p = np.where(valid, np.exp(s - m[:, None]), 0.0)
+    denom = p.sum(axis=1)
+    if sink is not None:
+        denom = denom + np.exp(sink - m)
+    return (p @ v) / denom[:, None]
+
+
+def attention_one_request(q: np.ndarray, k: np.ndarray, v: np.ndarray, bmm1_scale: float,
+                          bmm2_scale: float, window_left: int,
+                          sinks: Optional[np.ndarray], chunk: int = 256) -> np.ndarray:
+    """q ``[q_len, H_q, D]``, contiguous k and v ``[kv_len, H_kv, D]`` ->
+    ``[q_len, H_q, D]``.  Query rows are taken ``chunk`` at a time to bound
+    memory; keys past the chunk's last causal position are masked for every
+    row of the chunk and are left out."""
+    q_len, num_qo_heads, _ = q.shape
+    kv_len, num_kv_heads, head_dim = k.shape
+    out = np.empty((q_len, num_qo_heads, v.shape[2]), dtype=np.float64)
+    prefix = kv_len - q_len
+    full_mask = _valid_mask(q_len, kv_len, window_left)
+    for h in range(num_qo_heads):
+        hk = _kv_head(h, num_qo_heads, num_kv_heads)
+        sink = None if sinks is None else float(sinks[h])
+        for r0 in range(0, q_len, chunk):
+            r1 = min(q_len, r0 + chunk)
+            hi = min(kv_len, prefix + r1)
+            s = bmm1_scale * (q[r0:r1, h, :] @ k[:hi, hk, :].T)
+            o = _softmax_weighted_sum(s, full_mask[r0:r1, :hi], v[:hi, hk, :], sink)
+            out[r0:r1, h, :] = bmm2_scale * o
+    return out
+
+
+def paged_prefill_attention(query: np.ndarray, kv_cache, kv_layout: str,
+                            block_tables: np.ndarray, seq_lens: np.ndarray,
+                            cum_seq_lens_q: np.ndarray, page_size: int,
+                            bmm1_scale: float, bmm2_scale: float,
+                            window_left: int = -1,
+                            sinks: Optional[np.ndarray] = None,
+                            requests: Optional[Sequence[int]] = None,
+                            chunk: int = 256) -> Tuple[np.ndarray, np.ndarray]:
+    """The whole batched call on decoded float64 inputs.
+
+    ``query`` ``[num_tokens, H_q, D]``; ``kv_cache`` a (K, V) tuple of page
+    pools or one array with the K/V planes in dim 1, laid out per
+    ``kv_layout``; ``block_tables`` ``[batch, W]``; ``seq_lens`` the KV length
+    of each request (cached prefix included); ``cum_seq_lens_q``
+    ``[batch + 1]``.  Returns ``(out, written)``: ``out`` ``[num_tokens, H_q,
+    D]`` float64 with NaN in rows no request owns, and ``written`` the bool
+    row mask.  ``requests`` restricts the work to some requests (the other
+    rows stay NaN / unwritten)."""
+    num_tokens, num_qo_heads, head_dim = query.shape
+    batch = len(seq_lens)
+    out = np.full((num_tokens, num_qo_heads, head_dim), np.nan, dtype=np.float64)
+    written = np.zeros(num_tokens, dtype=bool)
+    todo = range(batch) if requests is None else requests
+    for b in todo:
+        q0, q1 = int(cum_seq_lens_q[b]), int(cum_seq_lens_q[b + 1])
+        q_len = q1 - q0
+        kv_len = int(seq_lens[b])
+        if q_len == 0:
+            continue
+        if q_len > kv_len:
+            raise ValueError(f"request {b}: q_len {q_len} > kv_len {kv_len}")
+        k = gather_paged_kv(kv_cache, block_tables[b], 0, kv_len, page_size, kv_layout)
+        v = gather_paged_kv(kv_cache, block_tables[b], 1, kv_len, page_size, kv_layout)
+        out[q0:q1] = attention_one_request(query[q0:q1], k, v, bmm1_scale, bmm2_scale,
+                                           window_left, sinks, chunk)
+        written[q0:q1] = True
+    return out, written
+
+
+def attention_rows(query: np.ndarray, kv_cache, kv_layout: str, block_tables: np.ndarray,
+                   seq_lens: np.ndarray, cum_seq_lens_q: np.ndarray, page_size: int,
+                   bmm1_scale: float, bmm2_scale: float, window_left: int,
+                   sinks: Optional[np.ndarray], rows: Sequence[Tuple[int, int]]) -> np.ndarray:
+    """Selected output rows, one (token, q head) pair at a time: ``[len(rows),
+    D]``.  Used to check full-size runs on a sample of outputs."""
+    num_tokens, num_qo_heads, head_dim = query.shape
+    num_kv_heads = _plane(kv_cache, 0).shape[2 if kv_layout == "NHD" else 1]
+    cu = np.asarray(cum_seq_lens_q)
+    res = np.empty((len(rows), head_dim), dtype=np.float64)
+    cache = {}
+    for n, (t, h) in enumerate(rows):
+        b = int(np.searchsorted(cu, t, side="right") - 1)
+        q0 = int(cu[b])
+        kv_len = int(seq_lens[b])
+        q_len = int(cu[b + 1]) - q0
+        i = t - q0
+        if b not in cache:
+            cache[b] = (gather_paged_kv(kv_cache, block_tables[b], 0, kv_len, page_size, kv_layout),
+                        gather_paged_kv(kv_cache, block_tables[b], 1, kv_len, page_size, kv_layout))
+        k, v = cache[b]
+        hk = _kv_head(h, num_qo_heads, num_kv_heads)
+        valid = _valid_mask(q_len, kv_len, window_left)[i:i + 1]
+        s = bmm1_scale * (query[t:t + 1, h, :] @ k[:, hk, :].T)
+        sink = None if sinks is None else float(sinks[h])
+        res[n] = bmm2_scale * _softmax_weighted_sum(s, valid, v[:, hk, :], sink)[0]
+    return res

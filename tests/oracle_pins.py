@@ -1,0 +1,433 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+an independent fact: a hand-derived closed form, a brute-force evaluation
+that reads pages key by key, torch's SDPA, torch's own number decoders, or an
+invariance the definition implies.  ``test_oracle.py`` runs them all;
+``test_oracle_mutants.py`` plants plausible mistakes in the oracle and checks
+that each one trips at least one pin.
+
+The oracle is reached through its module attributes at call time, so a
+planted mistake (a monkeypatched step) is what the pins see.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle.paged_attention as OA
+from oracle.case_io import decode_tensor, oracle_inputs
+from workloads import make_custom_case
+from workloads.cases import relayout
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _run(case, **over):
+    a = oracle_inputs(case)
+    a.update(over)
+    return OA.paged_prefill_attention(**a)
+
+
+def _tiny(seed, **kw):
+    base = dict(batch=3, num_qo_heads=4, num_kv_heads=2, head_dim=8, page_size=4,
+                q_lens=(5, 1, 7), prefix_lens=(3, 0, 6), kv_layout="HND",
+                kv_form="split", seed=seed, bmm1_scale=0.7, bmm2_scale=1.3)
+    base.update(kw)
+    return make_custom_case(**base)
+
+
+# --------------------------------------------------------------------------
+# number formats
+# --------------------------------------------------------------------------
+
+def _same(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    both_nan = np.isnan(a) & np.isnan(b)
+    eq = (a == b) & (np.signbit(a) == np.signbit(b))
+    return bool(np.all(both_nan | eq))
+
+
+def pin_bf16_decode_all_codes():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = OA.decode_bf16(codes)
+    theirs = torch.from_numpy(codes.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    assert _same(ours, theirs), "bf16 decode differs from torch's cast"
+
+
+def pin_e4m3fn_decode_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = OA.decode_e4m3fn(codes)
+    theirs = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert _same(ours, theirs), "e4m3fn table differs from torch's cast"
+
+
+def pin_number_format_golden():
+    with open(os.path.join(GOLDEN, "number_formats.json")) as f:
+        g = json.load(f)
+    for code, val in g["e4m3fn"].items():
+        got = OA.decode_e4m3fn(np.array([int(code, 16)], dtype=np.uint8))[0]
+        assert _same(got, float(val)), f"e4m3fn {code}: {got} != {val}"
+    for code, val in g["bf16"].items():
+        got = OA.decode_bf16(np.array([int(code, 16)], dtype=np.uint16))[0]
+        assert _same(got, float(val)), f"bf16 {code}: {got} != {val}"
+
+
+# --------------------------------------------------------------------------
+# page gather
+# --------------------------------------------------------------------------
+
+GATHER_VARIANTS = [
+    dict(kv_layout="HND", kv_form="split", page_size=4),
+    dict(kv_layout="NHD", kv_form="split", page_size=4),
+    dict(kv_layout="HND", kv_form="combined", page_size=3),
+    dict(kv_layout="NHD", kv_form="combined", page_size=1),
+    dict(kv_layout="NHD", kv_form="combined1", page_size=5),
+    dict(kv_layout="HND", kv_form="split", page_size=16, kv_dtype="fp8_e4m3fn"),
+]
+
+
+def pin_gather_reproduces_logical_kv():
+    """The generator scatters each request's contiguous K/V into shuffled
+    pages; the oracle's gather must give the same tokens back, bit for bit."""
+    for n, var in enumerate(GATHER_VARIANTS):
+        case = _tiny(100 + n, **var)
+        a = oracle_inputs(case)
+        for b in range(case["batch_size"]):
+            for kv_idx, logical in ((0, case["logical_k"]), (1, case["logical_v"])):
+                got = OA.gather_paged_kv(a["kv_cache"], a["block_tables"][b], kv_idx,
+                                         case["kv_lens"][b], case["page_size"], case["kv_layout"])
+                want = decode_tensor(logical[b])
+                assert got.shape == want.shape, (var, got.shape, want.shape)
+                assert _same(got, want), f"gather mismatch {var} request {b} plane {kv_idx}"
+
+
+# --------------------------------------------------------------------------
+# brute force, key by key
+# --------------------------------------------------------------------------
+
+def _brute_force(case):
+    """Every output element as a plain Python sum over keys.  Each key is
+    fetched straight from its page through the block table (no gathered
+    copy), and the softmax is exp(s) / (sum exp(s) + exp(sink)) with no
+    shift."""
+    a = oracle_inputs(case)
+    q = a["query"]
+    P = a["page_size"]
+    lay = a["kv_layout"]
+    kvc = a["kv_cache"]
+    Hq = q.shape[1]
+    Hkv = case["num_kv_heads"]
+    W = a["window_left"]
+    out = np.full(q.shape, np.nan)
+
+    def fetch(plane_idx, pid, slot, hk):
+        if isinstance(kvc, tuple):
+            pool = kvc[plane_idx]
+            return pool[pid, hk, slot] if lay == "HND" else pool[pid, slot, hk]
+        pi = plane_idx if kvc.shape[1] == 2 else 0
+        return kvc[pid, pi, hk, slot] if lay == "HND" else kvc[pid, pi, slot, hk]
+
+    cu = a["cum_seq_lens_q"]
+    for b in range(len(a["seq_lens"])):
+        kv_len = int(a["seq_lens"][b])
+        q_len = int(cu[b + 1] - cu[b])
+        for i in range(q_len):
+            t = int(cu[b]) + i
+            pos = kv_len - q_len + i
+            for h in range(Hq):
+                hk = h * Hkv // Hq
+                num = np.zeros(q.shape[2])
+                den = 0.0
+                for j in range(kv_len):
+                    if j > pos or (W >= 0 and j < pos - W):
+                        continue
+                    pid = int(a["block_tables"][b][j // P])
+                    kj = fetch(0, pid, j % P, hk)
+                    vj = fetch(1, pid, j % P, hk)
+                    w = math.exp(a["bmm1_scale"] * float(np.dot(q[t, h], kj)))
+                    num = num + w * vj
+                    den += w
+                if a["sinks"] is not None:
+                    den += math.exp(float(a["sinks"][h]))
+                out[t, h] = a["bmm2_scale"] * num / den
+    return out
+
+
+BRUTE_CASES = [
+    dict(),
+    dict(window_left=0),
+    dict(window_left=2, sinks=True),
+    dict(kv_layout="NHD", kv_form="combined", page_size=3, window_left=4),
+    dict(num_qo_heads=6, num_kv_heads=2, sinks=True, page_size=2),
+    dict(num_qo_heads=3, num_kv_heads=3, q_lens=(4, 0, 2), prefix_lens=(0, 5, 1)),
+    dict(kv_form="combined1", kv_layout="HND", page_size=5),
+    dict(kv_dtype="fp8_e4m3fn", page_size=4, sinks=True, window_left=3,
+         bmm1_scale=None, bmm2_scale=None),
+]
+
+
+def pin_brute_force():
+    for n, var in enumerate(BRUTE_CASES):
+        case = _tiny(200 + n, **var)
+        got, written = _run(case)
+        want = _brute_force(case)
+        rows = written
+        assert np.array_equal(rows, ~np.isnan(want).all(axis=(1, 2))), var
+        err = np.max(np.abs(got[rows] - want[rows])) if rows.any() else 0.0
+        assert err <= 1e-12, f"brute force mismatch {var}: {err}"
+
+
+# --------------------------------------------------------------------------
+# torch SDPA (float64, explicit bottom-right mask, grouped kv heads)
+# --------------------------------------------------------------------------
+
+SDPA_CASES = [
+    dict(prefix_lens=(0, 0, 0)),
+    dict(),
+    dict(window_left=3),
+    dict(num_qo_heads=8, num_kv_heads=2, kv_layout="NHD"),
+    dict(num_qo_heads=2, num_kv_heads=2, kv_form="combined", head_dim=16, page_size=8),
+]
+
+
+def pin_torch_sdpa():
+    import torch.nn.functional as F
+    for n, var in enumerate(SDPA_CASES):
+        case = _tiny(300 + n, **var)
+        got, written = _run(case)
+        a = oracle_inputs(case)
+        cu = a["cum_seq_lens_q"]
+        G = case["num_qo_heads"] // case["num_kv_heads"]
+        for b in range(case["batch_size"]):
+            q_len = int(cu[b + 1] - cu[b])
+            kv_len = int(a["seq_lens"][b])
+            if q_len == 0:
+                continue
+            # contiguous K/V from the generator's logical tokens
+            k = torch.from_numpy(decode_tensor(case["logical_k"][b]))      # [kv, Hkv, D]
+            v = torch.from_numpy(decode_tensor(case["logical_v"][b]))
+            q = torch.from_numpy(a["query"][int(cu[b]):int(cu[b + 1])])     # [q, Hq, D]
+            i = torch.arange(q_len)[:, None] + (kv_len - q_len)
+            j = torch.arange(kv_len)[None, :]
+            mask = j <= i
+            if case["window_left"] >= 0:
+                mask &= j >= i - case["window_left"]
+            ref = F.scaled_dot_product_attention(
+                q.permute(1, 0, 2).unsqueeze(0), k.permute(1, 0, 2).unsqueeze(0),
+                v.permute(1, 0, 2).unsqueeze(0), attn_mask=mask,
+                scale=a["bmm1_scale"], enable_gqa=G > 1)[0].permute(1, 0, 2)
+            ref = (a["bmm2_scale"] * ref).numpy()
+            err = np.max(np.abs(got[int(cu[b]):int(cu[b + 1])] - ref))
+            assert err <= 1e-12, f"SDPA mismatch {var} request {b}: {err}"
+
+
+# --------------------------------------------------------------------------
+# closed forms
+# --------------------------------------------------------------------------
+
+def pin_window_zero_is_diagonal():
+    """window_left 0 leaves only key prefix+i: o_i = bmm2 * v_{prefix+i}."""
+    case = _tiny(400, window_left=0)
+    got, written = _run(case)
+    bmm2 = oracle_inputs(case)["bmm2_scale"]
+    cu = case["cum_seq_lens_q"].numpy()
+    G = case["num_qo_heads"] // case["num_kv_heads"]
+    for b in range(case["batch_size"]):
+        v = decode_tensor(case["logical_v"][b])
+        pre = case["prefix_lens"][b]
+        for i in range(case["q_lens"][b]):
+            for h in range(case["num_qo_heads"]):
+                want = bmm2 * v[pre + i, h // G]
+                assert np.max(np.abs(got[cu[b] + i, h] - want)) <= 1e-12
+
+
+def pin_window_zero_with_sink():
+    """window_left 0 plus a sink: o_i = bmm2 * v / (1 + exp(sink - s_ii))."""
+    case = _tiny(401, window_left=0, sinks=True)
+    got, _ = _run(case)
+    a = oracle_inputs(case)
+    cu = a["cum_seq_lens_q"]
+    G = case["num_qo_heads"] // case["num_kv_heads"]
+    for b in range(case["batch_size"]):
+        k = decode_tensor(case["logical_k"][b])
+        v = decode_tensor(case["logical_v"][b])
+        pre = case["prefix_lens"][b]
+        for i in range(case["q_lens"][b]):
+            t = int(cu[b]) + i
+            for h in range(case["num_qo_heads"]):
+                s = a["bmm1_scale"] * float(np.dot(a["query"][t, h], k[pre + i, h // G]))
+                want = a["bmm2_scale"] * v[pre + i, h // G] / (1.0 + math.exp(a["sinks"][h] - s))
+                assert np.max(np.abs(got[t, h] - want)) <= 1e-12
+
+
+def pin_zero_scale_is_mean():
+    """bmm1_scale 0 makes every valid logit 0: o_i = bmm2 * sum_valid v /
+    (n_i + exp(sink)), n_i the number of valid keys."""
+    for sinks in (False, True):
+        case = _tiny(402 + sinks, bmm1_scale=0.0, window_left=3, sinks=sinks)
+        got, _ = _run(case)
+        a = oracle_inputs(case)
+        cu = a["cum_seq_lens_q"]
+        G = case["num_qo_heads"] // case["num_kv_heads"]
+        for b in range(case["batch_size"]):
+            v = decode_tensor(case["logical_v"][b])
+            pre = case["prefix_lens"][b]
+            for i in range(case["q_lens"][b]):
+                lo = max(0, pre + i - 3)
+                hi = pre + i
+                n = hi - lo + 1
+                for h in range(case["num_qo_heads"]):
+                    extra = math.exp(a["sinks"][h]) if sinks else 0.0
+                    want = a["bmm2_scale"] * v[lo:hi + 1, h // G].sum(axis=0) / (n + extra)
+                    assert np.max(np.abs(got[int(cu[b]) + i, h] - want)) <= 1e-12
+
+
+def pin_golden_hand_examples():
+    with open(os.path.join(GOLDEN, "hand_examples.json")) as f:
+        g = json.load(f)
+    env = {"e": math.e, "exp": math.exp, "__builtins__": {}}
+    for ex in g["examples"]:
+        if ex["kv_form"] == "split":
+            kv = (np.array(ex["k_pool"], dtype=np.float64), np.array(ex["v_pool"], dtype=np.float64))
+        else:
+            kv = np.array(ex["kv_pool"], dtype=np.float64)
+        got, written = OA.paged_prefill_attention(
+            query=np.array(ex["query"], dtype=np.float64), kv_cache=kv,
+            kv_layout=ex["kv_layout"], block_tables=np.array(ex["block_tables"]),
+            seq_lens=np.array(ex["seq_lens"]), cum_seq_lens_q=np.array(ex["cum_seq_lens_q"]),
+            page_size=ex["page_size"], bmm1_scale=ex["bmm1_scale"], bmm2_scale=ex["bmm2_scale"],
+            window_left=ex["window_left"],
+            sinks=None if ex["sinks"] is None else np.array(ex["sinks"], dtype=np.float64))
+        for t, row in enumerate(ex["expected"]):
+            if row is None:
+                assert not written[t], f"{ex['name']}: row {t} should be unwritten"
+                continue
+            assert written[t], f"{ex['name']}: row {t} not written"
+            want = np.array([[eval(x, env) for x in head] for head in row])
+            err = np.max(np.abs(got[t] - want))
+            assert err <= 1e-12, f"{ex['name']} row {t}: {got[t]} vs {want}"
+
+
+# --------------------------------------------------------------------------
+# invariances
+# --------------------------------------------------------------------------
+
+def pin_sink_neg_inf_is_no_sink():
+    case = _tiny(500, window_left=2)
+    a = oracle_inputs(case)
+    base, _ = OA.paged_prefill_attention(**a)
+    a["sinks"] = np.full(case["num_qo_heads"], -np.inf)
+    got, _ = OA.paged_prefill_attention(**a)
+    assert np.array_equal(base, got, equal_nan=True), "sink -inf differs from no sink"
+
+
+def pin_full_window_is_no_window():
+    case = _tiny(501, sinks=True)
+    a = oracle_inputs(case)
+    base, _ = OA.paged_prefill_attention(**a)
+    a["window_left"] = max(case["kv_lens"])
+    got, _ = OA.paged_prefill_attention(**a)
+    assert np.array_equal(base, got, equal_nan=True), "window >= kv_len differs from -1"
+
+
+def pin_chunk_equals_tail_of_full_prefill():
+    """A chunk of q new tokens over a p-token prefix equals the last q rows of
+    one prefill of p+q tokens over the same K/V."""
+    full = _tiny(502, batch=1, q_lens=(11,), prefix_lens=(0,), sinks=True, window_left=5)
+    a = oracle_inputs(full)
+    out_full, _ = OA.paged_prefill_attention(**a)
+    for q in (1, 4, 11):
+        c = dict(a)
+        c["query"] = a["query"][11 - q:]
+        c["cum_seq_lens_q"] = np.array([0, q])
+        out_c, _ = OA.paged_prefill_attention(**c)
+        assert np.max(np.abs(out_c - out_full[11 - q:])) <= 1e-14
+
+
+def pin_relayout_invariance():
+    """Same logical tokens, other cache: layout, combined/split, page size and
+    page permutation leave the output bit-identical."""
+    case = _tiny(503, sinks=True, window_left=4)
+    base, _ = _run(case)
+    for lay, form, P, seed in (("NHD", "split", 4, 1), ("HND", "combined", 2, 2),
+                               ("NHD", "combined", 7, 3), ("HND", "split", 1, 4)):
+        other = relayout(case, kv_layout=lay, kv_form=form, page_size=P, permute_seed=seed)
+        got, _ = _run(other)
+        assert np.array_equal(base, got, equal_nan=True), (lay, form, P)
+
+
+def pin_poison_invariance():
+    a_case = _tiny(504, poison="finite")
+    b_case = _tiny(504, poison="nan")
+    a, _ = _run(a_case)
+    b, _ = _run(b_case)
+    assert np.array_equal(a, b, equal_nan=True), "unused pages or slots leaked"
+    assert not np.isnan(a[:sum(a_case["q_lens"])]).any()
+
+
+def pin_request_permutation():
+    case = _tiny(505, window_left=3)
+    base, _ = _run(case)
+    a = oracle_inputs(case)
+    order = [2, 0, 1]
+    cu = a["cum_seq_lens_q"]
+    qs = [a["query"][cu[b]:cu[b + 1]] for b in order]
+    new_cu = np.concatenate([[0], np.cumsum([len(x) for x in qs])])
+    got, _ = OA.paged_prefill_attention(
+        query=np.concatenate(qs), kv_cache=a["kv_cache"], kv_layout=a["kv_layout"],
+        block_tables=a["block_tables"][order], seq_lens=a["seq_lens"][order],
+        cum_seq_lens_q=new_cu, page_size=a["page_size"], bmm1_scale=a["bmm1_scale"],
+        bmm2_scale=a["bmm2_scale"], window_left=a["window_left"], sinks=None)
+    want = np.concatenate([base[cu[b]:cu[b + 1]] for b in order])
+    assert np.array_equal(got, want, equal_nan=True)
+
+
+def pin_bmm2_linear():
+    case = _tiny(506, sinks=True)
+    a = oracle_inputs(case)
+    a["bmm2_scale"] = 1.0
+    one, _ = OA.paged_prefill_attention(**a)
+    a["bmm2_scale"] = -2.5
+    two, _ = OA.paged_prefill_attention(**a)
+    assert np.max(np.abs(two - (-2.5) * one)) <= 1e-12
+
+
+def pin_gqa_equals_repeated_mha():
+    """G query heads sharing one kv head equal an MHA run whose kv heads are
+    the shared ones repeated G times in order."""
+    case = _tiny(507, num_qo_heads=6, num_kv_heads=2, kv_layout="NHD")
+    base, _ = _run(case)
+    a = oracle_inputs(case)
+    k, v = a["kv_cache"]
+    rep = (np.repeat(k, 3, axis=2), np.repeat(v, 3, axis=2))
+    a["kv_cache"] = rep
+    got, _ = OA.paged_prefill_attention(**a)
+    assert np.array_equal(base, got, equal_nan=True)
+
+
+ALL_PINS = [
+    pin_bf16_decode_all_codes,
+    pin_e4m3fn_decode_all_codes,
+    pin_number_format_golden,
+    pin_gather_reproduces_logical_kv,
+    pin_brute_force,
+    pin_torch_sdpa,
+    pin_window_zero_is_diagonal,
+    pin_window_zero_with_sink,
+    pin_zero_scale_is_mean,
+    pin_golden_hand_examples,
+    pin_sink_neg_inf_is_no_sink,
+    pin_full_window_is_no_window,
+    pin_chunk_equals_tail_of_full_prefill,
+    pin_relayout_invariance,
+    pin_poison_invariance,
+    pin_request_permutation,
+    pin_bmm2_linear,
+    pin_gqa_equals_repeated_mha,
+]

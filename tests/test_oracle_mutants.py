@@ -1,0 +1,130 @@
+"""Planted mistakes in the CPU oracle must each trip at least one pin.
+
+Every mutant below swaps one step of the oracle (on the CPU, via
+monkeypatch) for a plausible wrong version: an off-by-one in the mask, the
+wrong causal alignment, a wrong GQA mapping, a mishandled sink, a wrong page
+slot or layout, V read from the K plane, a wrong number decoder, a dropped
+scale.  The test runs every pin against the mutated oracle and requires at
+least one to fail, so the pins are shown to constrain each step.
+"""
+import numpy as np
+import pytest
+
+import oracle.paged_attention as OA
+import oracle_pins
+
+_orig_mask = OA._valid_mask
+_orig_softmax = OA._softmax_weighted_sum
+_orig_attn = OA.attention_one_request
+_orig_rows = OA._page_rows
+_orig_plane = OA._plane
+
+
+def _mask_variant(cond):
+    def f(q_len, kv_len, window_left):
+        prefix = kv_len - q_len
+        i = np.arange(q_len)[:, None]
+        j = np.arange(kv_len)[None, :]
+        return cond(i, j, prefix, window_left)
+    return f
+
+
+MUTANTS = {
+    "top_left_causal": ("_valid_mask", _mask_variant(
+        lambda i, j, p, w: (j <= i) & ((w < 0) | (j >= i - w)))),
+    "strict_causal": ("_valid_mask", _mask_variant(
+        lambda i, j, p, w: (j < p + i) & ((w < 0) | (j >= p + i - w)))),
+    "window_exclusive": ("_valid_mask", _mask_variant(
+        lambda i, j, p, w: (j <= p + i) & ((w < 0) | (j > p + i - w)))),
+    "window_one_wider": ("_valid_mask", _mask_variant(
+        lambda i, j, p, w: (j <= p + i) & ((w < 0) | (j >= p + i - w - 1)))),
+    "gqa_modulo": ("_kv_head", lambda h, hq, hkv: h % hkv),
+    "sink_ignored": ("_softmax_weighted_sum",
+                     lambda s, valid, v, sink: _orig_softmax(s, valid, v, None)),
+    "sink_unshifted": ("_softmax_weighted_sum", None),   # filled below
+    "sink_as_value_row": ("_softmax_weighted_sum", None),
+    "bmm2_dropped": ("attention_one_request",
+                     lambda q, k, v, b1, b2, w, s, chunk=256: _orig_attn(q, k, v, b1, 1.0, w, s, chunk)),
+    "bmm1_dropped": ("attention_one_request",
+                     lambda q, k, v, b1, b2, w, s, chunk=256: _orig_attn(q, k, v, 1.0, b2, w, s, chunk)),
+    "slot_shift": ("_page_rows", None),
+    "hnd_reshaped_not_transposed": ("_page_rows", None),
+    "v_from_k_plane": ("_plane", lambda kv, idx: _orig_plane(kv, 0)),
+    "e4m3_bias_8": ("E4M3FN_TABLE", None),
+    "bf16_shift_15": ("decode_bf16", None),
+}
+
+
+def _sink_unshifted(s, valid, v, sink):
+    s = np.where(valid, s, -np.inf)
+    m = s.max(axis=1)
+    p = np.where(valid, np.exp(s - m[:, None]), 0.0)
+    den = p.sum(axis=1) + (np.exp(sink) if sink is not None else 0.0)
+    return (p @ v) / den[:, None]
+
+
+def _sink_as_value_row(s, valid, v, sink):
+    if sink is None:
+        return _orig_softmax(s, valid, v, None)
+    s2 = np.concatenate([s, np.full((s.shape[0], 1), sink)], axis=1)
+    valid2 = np.concatenate([valid, np.ones((s.shape[0], 1), dtype=bool)], axis=1)
+    v2 = np.concatenate([v, np.ones((1, v.shape[1]))], axis=0)
+    return _orig_softmax(s2, valid2, v2, None)
+
+
+def _slot_shift(plane, page_id, nslots, kv_layout):
+    page = plane[page_id]
+    P = page.shape[1] if kv_layout == "HND" else page.shape[0]
+    idx = (np.arange(nslots) + 1) % P
+    if kv_layout == "HND":
+        return np.transpose(page[:, idx, :], (1, 0, 2))
+    return page[idx]
+
+
+def _hnd_reshaped(plane, page_id, nslots, kv_layout):
+    page = plane[page_id]
+    if kv_layout == "HND":
+        H, P, D = page.shape
+        return page.reshape(P, H, D)[:nslots]
+    return page[:nslots]
+
+
+def _bad_table():
+    t = []
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 0xF, c & 7
+        if e == 15 and m == 7:
+            t.append(np.nan)
+        elif e == 0:
+            t.append(sign * m / 8 * 2.0 ** -7)
+        else:
+            t.append(sign * (1 + m / 8) * 2.0 ** (e - 8))
+    return np.array(t)
+
+
+def _bf16_shift_15(codes):
+    c = np.asarray(codes, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+    with np.errstate(invalid="ignore"):
+        return c.view(np.float32).astype(np.float64)
+
+
+MUTANTS["sink_unshifted"] = ("_softmax_weighted_sum", _sink_unshifted)
+MUTANTS["sink_as_value_row"] = ("_softmax_weighted_sum", _sink_as_value_row)
+MUTANTS["slot_shift"] = ("_page_rows", _slot_shift)
+MUTANTS["hnd_reshaped_not_transposed"] = ("_page_rows", _hnd_reshaped)
+MUTANTS["e4m3_bias_8"] = ("E4M3FN_TABLE", _bad_table())
+MUTANTS["bf16_shift_15"] = ("decode_bf16", _bf16_shift_15)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, repl = MUTANTS[name]
+    monkeypatch.setattr(OA, attr, repl)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except Exception as exc:  # an AssertionError, or the mutant breaking outright
+            caught.append((pin.__name__, type(exc).__name__))
+    assert caught, f"no pin detects the planted mistake {name!r}"

@@ -1,0 +1,354 @@
+"""Seeded synthetic workloads for batched paged prefill attention.
+
+Every tensor is drawn from a seeded ``numpy.random.Generator`` in a fixed
+order (lengths, Q, logical K and V, sinks, page permutation, poison) and then
+laid out as the arguments of the FlashInfer API page for
+``trtllm_batch_context_with_kv_cache`` (section "Parameters"):
+
+* ``query``  ``[num_tokens, num_qo_heads, head_dim]``, ragged by
+  ``cum_seq_lens_q``;
+* ``kv_cache`` either one tensor ``[num_pages, 1 or 2, H_kv, P, D]`` (HND) /
+  ``[num_pages, 1 or 2, P, H_kv, D]`` (NHD), or a ``(K, V)`` tuple of
+  ``[num_pages, H_kv, P, D]`` (HND) / ``[num_pages, P, H_kv, D]`` (NHD);
+* ``block_tables`` ``[batch_size, W]`` int32 page ids, ``seq_lens`` (the full
+  KV length including any cached prefix, as in the chunked-context figure of
+  the TensorRT-LLM attention-backend article), ``cum_seq_lens_q`` and
+  ``cum_seq_lens_kv`` ``[batch_size + 1]``.
+
+Each request's KV tokens are drawn as one contiguous ``[kv_len, H_kv, D]``
+block (the "logical" K/V) and scattered into physical pages chosen by a random
+permutation of the pool.  Pages no request uses, table columns past a
+request's last page (set to page 0, the padding convention of the TokenSpeed
+backend source) and page slots past ``kv_len`` hold poison, so a consumer that
+reads outside the valid range shows it.
+
+Values are N(0, 1) in fp32, rounded to bf16 by torch's round-to-nearest-even
+cast.  For an fp8 cache, K and V are drawn in fp32, divided by a per-tensor
+scale ``amax / 448`` and cast by torch to ``float8_e4m3fn``; the caller-side
+scale folding of the TokenSpeed backend's ``_compute_scales`` then gives
+``bmm1_scale = k_scale / sqrt(D)`` and ``bmm2_scale = v_scale``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+FP8_E4M3FN_MAX = 448.0
+
+
+@dataclass(frozen=True)
+class Spec:
+    """A workload recipe.  Lengths are either explicit or drawn uniformly
+    (inclusive bounds) from the seed."""
+
+    name: str
+    batch: int
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    kv_layout: str = "HND"          # "HND" | "NHD"
+    kv_form: str = "split"          # "split" | "combined" | "combined1"
+    kv_dtype: str = "bf16"          # "bf16" | "fp8_e4m3fn"
+    q_lens: Optional[tuple] = None
+    q_range: Optional[tuple] = None
+    prefix_lens: Optional[tuple] = None
+    prefix_range: Optional[tuple] = None
+    window_left: int = -1
+    sinks: bool = False
+    bmm1_scale: Optional[float] = None   # None: 1/sqrt(head_dim) (times k_scale for fp8)
+    bmm2_scale: Optional[float] = None   # None: 1 (v_scale for fp8)
+    pool_pages: Optional[int] = None     # None: pages used + spare_pages
+    spare_pages: int = 8
+    table_cols: Optional[int] = None     # None: ceil(max_kv_len / page_size)
+    max_kv_len: Optional[int] = None     # None: the batch maximum
+    max_q_len: Optional[int] = None      # None: the batch maximum
+    extra_tokens: int = 0                # query/out rows past cum_seq_lens_q[-1]
+    seed: int = 0
+    poison: str = "finite"               # "finite" | "nan"
+
+    def replace(self, **kw) -> "Spec":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads, in order.  Seeds are 1000 + the 1-based position.
+SPECS = {
+    "tiny": Spec(
+        name="tiny", batch=2, num_qo_heads=4, num_kv_heads=2, head_dim=64,
+        page_size=16, kv_layout="HND", kv_form="split",
+        q_lens=(37, 64), prefix_lens=(0, 0), pool_pages=16,
+        bmm1_scale=1.0 / 8.0, bmm2_scale=1.0, seed=1001),
+    "chunked": Spec(
+        name="chunked", batch=8, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+        page_size=32, kv_layout="HND", kv_form="combined",
+        q_range=(128, 1024), prefix_range=(0, 512), seed=1002),
+    "llama3_8b": Spec(
+        name="llama3_8b", batch=16, num_qo_heads=32, num_kv_heads=8,
+        head_dim=128, page_size=64, kv_layout="HND", kv_form="split",
+        q_lens=(2048,) * 16, prefix_lens=(0,) * 16,
+        bmm1_scale=1.0 / math.sqrt(128.0), seed=1003),
+    "swa_sinks": Spec(
+        name="swa_sinks", batch=8, num_qo_heads=64, num_kv_heads=8, head_dim=64,
+        page_size=16, kv_layout="NHD", kv_form="split",
+        q_range=(512, 4096), prefix_range=(0, 1024), window_left=127,
+        sinks=True, seed=1004),
+    "fp8_long_prefix": Spec(
+        name="fp8_long_prefix", batch=1, num_qo_heads=64, num_kv_heads=8,
+        head_dim=128, page_size=64, kv_layout="HND", kv_form="split",
+        kv_dtype="fp8_e4m3fn", q_lens=(8192,), prefix_lens=(24576,),
+        seed=1005),
+}
+SPEC_ORDER = ["tiny", "chunked", "llama3_8b", "swa_sinks", "fp8_long_prefix"]
+
+
+def spec_by_index(i: int) -> Spec:
+    """0-based position in the workload list."""
+    return SPECS[SPEC_ORDER[i]]
+
+
+def _poison_values(shape, mode: str, kv_dtype: str) -> torch.Tensor:
+    """Alternating +-big finite values, or all-NaN, in the cache dtype."""
+    n = int(np.prod(shape))
+    if mode == "nan":
+        if kv_dtype == "bf16":
+            return torch.full(shape, float("nan"), dtype=torch.bfloat16)
+        # 0x7F is a NaN code of e4m3fn (S.1111.111)
+        return torch.full(shape, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn)
+    big = 1.0e4 if kv_dtype == "bf16" else FP8_E4M3FN_MAX
+    sign = np.where(np.arange(n) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    vals = torch.from_numpy((sign * big).reshape(shape))
+    if kv_dtype == "bf16":
+        return vals.to(torch.bfloat16)
+    return vals.to(torch.float8_e4m3fn)
+
+
+def _draw_lengths(spec: Spec, rng: np.random.Generator):
+    if spec.q_lens is not None:
+        q = np.asarray(spec.q_lens, dtype=np.int64)
+    else:
+        lo, hi = spec.q_range
+        q = rng.integers(lo, hi + 1, size=spec.batch, dtype=np.int64)
+    if spec.prefix_lens is not None:
+        pre = np.asarray(spec.prefix_lens, dtype=np.int64)
+    elif spec.prefix_range is not None:
+        lo, hi = spec.prefix_range
+        pre = rng.integers(lo, hi + 1, size=spec.batch, dtype=np.int64)
+    else:
+        pre = np.zeros(spec.batch, dtype=np.int64)
+    assert q.shape == (spec.batch,) and pre.shape == (spec.batch,)
+    return q, pre
+
+
+def make_case(spec, seed: Optional[int] = None, **overrides) -> dict:
+    """Build one workload.  ``spec`` is a Spec or the name of one in SPECS;
+    keyword overrides replace Spec fields."""
+    if isinstance(spec, str):
+        spec = SPECS[spec]
+    if overrides:
+        spec = spec.replace(**overrides)
+    if seed is not None:
+        spec = spec.replace(seed=seed)
+    return _build(spec)
+
+
+def make_custom_case(**fields) -> dict:
+    """Build a workload from Spec fields alone (edge-case sweeps)."""
+    fields.setdefault("name", "custom")
+    return _build(Spec(**fields))
+
+
+def _build(spec: Spec) -> dict:
+    rng = np.random.default_rng(spec.seed)
+    B, Hq, Hkv, D, P = (spec.batch, spec.num_qo_heads, spec.num_kv_heads,
+                        spec.head_dim, spec.page_size)
+    # 1. lengths
+    q_lens, prefix = _draw_lengths(spec, rng)
+    kv_lens = q_lens + prefix
+    cu_q = np.zeros(B + 1, dtype=np.int64)
+    cu_q[1:] = np.cumsum(q_lens)
+    cu_kv = np.zeros(B + 1, dtype=np.int64)
+    cu_kv[1:] = np.cumsum(kv_lens)
+    num_tokens = int(cu_q[-1]) + spec.extra_tokens
+
+    # 2. Q
+    q32 = rng.standard_normal((num_tokens, Hq, D), dtype=np.float32)
+    query = torch.from_numpy(q32).to(torch.bfloat16)
+
+    # 3. logical K and V, one contiguous [kv_len, H_kv, D] block per request
+    total_kv = int(cu_kv[-1])
+    k32 = rng.standard_normal((total_kv, Hkv, D), dtype=np.float32)
+    v32 = rng.standard_normal((total_kv, Hkv, D), dtype=np.float32)
+    k_scale = v_scale = 1.0
+    if spec.kv_dtype == "bf16":
+        k_all = torch.from_numpy(k32).to(torch.bfloat16)
+        v_all = torch.from_numpy(v32).to(torch.bfloat16)
+        cache_dtype = torch.bfloat16
+    elif spec.kv_dtype == "fp8_e4m3fn":
+        k_scale = float(np.float32(np.abs(k32).max()) / np.float32(FP8_E4M3FN_MAX)) if total_kv else 1.0
+        v_scale = float(np.float32(np.abs(v32).max()) / np.float32(FP8_E4M3FN_MAX)) if total_kv else 1.0
+        k_all = torch.from_numpy(k32 / np.float32(k_scale)).clamp(
+            -FP8_E4M3FN_MAX, FP8_E4M3FN_MAX).to(torch.float8_e4m3fn)
+        v_all = torch.from_numpy(v32 / np.float32(v_scale)).clamp(
+            -FP8_E4M3FN_MAX, FP8_E4M3FN_MAX).to(torch.float8_e4m3fn)
+        cache_dtype = torch.float8_e4m3fn
+    else:
+        raise ValueError(f"unknown kv_dtype {spec.kv_dtype}")
+    if spec.kv_form == "combined1":
+        v_all = k_all  # one plane: V is read from the same storage as K
+    logical_k = [k_all[int(cu_kv[b]):int(cu_kv[b + 1])] for b in range(B)]
+    logical_v = [v_all[int(cu_kv[b]):int(cu_kv[b + 1])] for b in range(B)]
+
+    # 4. sinks
+    sinks = None
+    if spec.sinks:
+        sinks = torch.from_numpy(rng.standard_normal(Hq, dtype=np.float32))
+
+    # 5. page placement
+    pages_per_req = [(int(kv) + P - 1) // P for kv in kv_lens]
+    used = sum(pages_per_req)
+    pool = spec.pool_pages if spec.pool_pages is not None else used + spec.spare_pages
+    if pool < used:
+        raise ValueError(f"pool of {pool} pages cannot hold {used} pages")
+    pool = max(pool, 1)
+    max_kv_len = spec.max_kv_len if spec.max_kv_len is not None else int(kv_lens.max(initial=0))
+    max_q_len = spec.max_q_len if spec.max_q_len is not None else int(q_lens.max(initial=0))
+    cols = spec.table_cols if spec.table_cols is not None else max(1, (max_kv_len + P - 1) // P)
+    perm = rng.permutation(pool)
+    block_tables = np.zeros((B, cols), dtype=np.int32)   # padding column value: page 0
+    off = 0
+    for b in range(B):
+        n = pages_per_req[b]
+        block_tables[b, :n] = perm[off:off + n]
+        off += n
+
+    # 6. poison, then scatter the logical tokens into their pages
+    if spec.kv_layout == "HND":
+        plane = (pool, Hkv, P, D)
+    elif spec.kv_layout == "NHD":
+        plane = (pool, P, Hkv, D)
+    else:
+        raise ValueError(f"unknown kv_layout {spec.kv_layout}")
+    nplanes = {"split": 2, "combined": 2, "combined1": 1}[spec.kv_form]
+    planes = [_poison_values(plane, spec.poison, spec.kv_dtype) for _ in range(nplanes)]
+    sources = [logical_k, logical_v][:nplanes]
+    for plane_t, src in zip(planes, sources):
+        for b in range(B):
+            kv = int(kv_lens[b])
+            if kv == 0:
+                continue
+            t = torch.arange(kv)
+            pid = torch.from_numpy(block_tables[b])[t // P].long()
+            slot = t % P
+            if spec.kv_layout == "HND":
+                plane_t[pid, :, slot, :] = src[b]
+            else:
+                plane_t[pid, slot, :, :] = src[b]
+    if spec.kv_form == "split":
+        kv_cache = (planes[0], planes[1])
+    else:
+        kv_cache = torch.stack(planes, dim=1)
+
+    if spec.kv_dtype == "fp8_e4m3fn":
+        bmm1 = spec.bmm1_scale if spec.bmm1_scale is not None else k_scale / math.sqrt(D)
+        bmm2 = spec.bmm2_scale if spec.bmm2_scale is not None else v_scale
+    else:
+        bmm1 = spec.bmm1_scale if spec.bmm1_scale is not None else 1.0 / math.sqrt(D)
+        bmm2 = spec.bmm2_scale if spec.bmm2_scale is not None else 1.0
+
+    return dict(
+        spec=spec,
+        query=query,
+        kv_cache=kv_cache,
+        kv_layout=spec.kv_layout,
+        kv_form=spec.kv_form,
+        kv_dtype=spec.kv_dtype,
+        cache_dtype=cache_dtype,
+        block_tables=torch.from_numpy(block_tables),
+        seq_lens=torch.from_numpy(kv_lens.astype(np.int32)),
+        cum_seq_lens_q=torch.from_numpy(cu_q.astype(np.int32)),
+        cum_seq_lens_kv=torch.from_numpy(cu_kv.astype(np.int32)),
+        batch_size=B,
+        max_q_len=max_q_len,
+        max_kv_len=max_kv_len,
+        num_tokens=num_tokens,
+        num_qo_heads=Hq,
+        num_kv_heads=Hkv,
+        head_dim=D,
+        page_size=P,
+        num_pages=pool,
+        bmm1_scale=float(bmm1),
+        bmm2_scale=float(bmm2),
+        window_left=spec.window_left,
+        sinks=sinks,
+        k_scale=k_scale,
+        v_scale=v_scale,
+        q_lens=[int(x) for x in q_lens],
+        kv_lens=[int(x) for x in kv_lens],
+        prefix_lens=[int(x) for x in prefix],
+        logical_k=logical_k,
+        logical_v=logical_v,
+    )
+
+
+def relayout(case: dict, kv_layout: Optional[str] = None, kv_form: Optional[str] = None,
+             page_size: Optional[int] = None, permute_seed: Optional[int] = None) -> dict:
+    """The same logical K/V placed in a different cache: another layout,
+    combined/split form, page size or page permutation.  Q, lengths, scales
+    and sinks are unchanged."""
+    spec = case["spec"]
+    lay = kv_layout or case["kv_layout"]
+    form = kv_form or case["kv_form"]
+    P = page_size or case["page_size"]
+    B, Hkv, D = case["batch_size"], case["num_kv_heads"], case["head_dim"]
+    kv_lens = case["kv_lens"]
+    rng = np.random.default_rng(permute_seed if permute_seed is not None else spec.seed + 7919)
+    pages_per_req = [(kv + P - 1) // P for kv in kv_lens]
+    used = sum(pages_per_req)
+    pool = max(used + spec.spare_pages, 1)
+    cols = max(1, (case["max_kv_len"] + P - 1) // P)
+    perm = rng.permutation(pool)
+    block_tables = np.zeros((B, cols), dtype=np.int32)
+    off = 0
+    for b in range(B):
+        n = pages_per_req[b]
+        block_tables[b, :n] = perm[off:off + n]
+        off += n
+    plane = (pool, Hkv, P, D) if lay == "HND" else (pool, P, Hkv, D)
+    if form == "combined1" and case["kv_form"] != "combined1":
+        raise ValueError("combined1 needs V == K in the source case")
+    nplanes = {"split": 2, "combined": 2, "combined1": 1}[form]
+    planes = [_poison_values(plane, spec.poison, spec.kv_dtype) for _ in range(nplanes)]
+    sources = [case["logical_k"], case["logical_v"]][:nplanes]
+    for plane_t, src in zip(planes, sources):
+        for b in range(B):
+            kv = kv_lens[b]
+            if kv == 0:
+                continue
+            t = torch.arange(kv)
+            pid = torch.from_numpy(block_tables[b])[t // P].long()
+            slot = t % P
+            if lay == "HND":
+                plane_t[pid, :, slot, :] = src[b]
+            else:
+                plane_t[pid, slot, :, :] = src[b]
+    kv_cache = (planes[0], planes[1]) if form == "split" else torch.stack(planes, dim=1)
+    out = dict(case)
+    out.update(kv_cache=kv_cache, kv_layout=lay, kv_form=form, page_size=P,
+               num_pages=pool, block_tables=torch.from_numpy(block_tables))
+    return out
+
+
+def as_codes(t: torch.Tensor) -> np.ndarray:
+    """Raw storage codes of a bf16 / fp8 tensor as unsigned numpy integers
+    (uint16 / uint8).  This is how values cross to the oracle, which decodes
+    them itself."""
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.contiguous().view(torch.uint8).numpy()
+    raise TypeError(f"no code view for {t.dtype}")

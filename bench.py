@@ -1,0 +1,210 @@
+"""Bench: batched paged prefill attention on one MI355X.
+
+One step = one call of the whole path (ppa_paged_prefill_attention through
+the C ABI) over one synthetic batch already resident in HBM.  The default
+workload is the chunked-context batch (8 requests, q_len U[128,1024] over a
+U[0,512] cached prefix, 32 q / 8 kv heads, head_dim 128, page 32, HND
+combined cache, seed 1002).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill attention TFLOP/s (causal FLOPs), % bf16/fp8 MFMA peak; tokens/s"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 dense bf16 FLOP/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2
+PEAK_HBM_GBS = 8000.0
+
+WORKLOAD_TEXT = {
+    "tiny": "tiny: batch 2, q=kv=(37,64), 4 q / 2 kv heads, head_dim 64, page 16, HND split, seed 1001",
+    "chunked": ("chunked context: batch 8, q_len U[128,1024] over prefix U[0,512], 32 q / 8 kv heads, "
+                "head_dim 128, page 32, HND combined [pages,2,H,P,D], causal, seed 1002"),
+    "llama3_8b": ("Llama-3-8B-shaped layer prefill: batch 16 x q=kv=2048, 32 q / 8 kv heads, head_dim 128, "
+                  "page 64, HND split, causal, seed 1003"),
+    "swa_sinks": ("sliding window 127 + sinks: batch 8, q_len U[512,4096] over prefix U[0,1024], 64 q / 8 kv "
+                  "heads, head_dim 64, page 16, NHD split, seed 1004"),
+    "fp8_long_prefix": ("long-prefix fp8 KV: batch 1, q 8192 over kv 32768, 64 q / 8 kv heads, head_dim 128, "
+                        "page 64, HND split, e4m3fn K/V with per-tensor scales, seed 1005"),
+}
+
+
+def causal_pairs(case) -> int:
+    """Number of (query row, key) pairs that pass the causal / window mask, per q head."""
+    W = case["window_left"]
+    total = 0
+    for q, kv in zip(case["q_lens"], case["kv_lens"]):
+        pre = kv - q
+        pos = pre + np.arange(q, dtype=np.int64)
+        n = pos + 1 if W < 0 else np.minimum(pos, W) + 1
+        total += int(n.sum())
+    return total
+
+
+def algorithmic_bytes(case) -> int:
+    """Compulsory HBM bytes: Q read + O written + every KV token some query reaches, once."""
+    D, Hq, Hkv = case["head_dim"], case["num_qo_heads"], case["num_kv_heads"]
+    eb = 1 if case["kv_dtype"] != "bf16" else 2
+    W = case["window_left"]
+    tokens = sum(case["q_lens"])
+    kv_reach = 0
+    for q, kv in zip(case["q_lens"], case["kv_lens"]):
+        if q == 0:
+            continue
+        lo = 0 if W < 0 else max(0, kv - q - W)
+        kv_reach += kv - lo
+    return tokens * Hq * D * 2 * 2 + kv_reach * Hkv * D * eb * 2
+
+
+def cpu_baseline(case, budget_s: float = 20.0):
+    """Time the CPU oracle (as it stands) on whole requests of the same batch,
+    taken in order until about budget_s of work; report causal TFLOP/s."""
+    from threadpoolctl import threadpool_info
+
+    from oracle.case_io import oracle_inputs
+    from oracle.paged_attention import paged_prefill_attention
+
+    a = oracle_inputs(case)
+    done = []
+    t_total = 0.0
+    for b in range(case["batch_size"]):
+        t = time.perf_counter()
+        paged_prefill_attention(requests=[b], **a)
+        t_total += time.perf_counter() - t
+        done.append(b)
+        if t_total >= budget_s:
+            break
+    sub = dict(case)
+    sub["q_lens"] = [case["q_lens"][b] for b in done]
+    sub["kv_lens"] = [case["kv_lens"][b] for b in done]
+    flops = 4.0 * case["head_dim"] * case["num_qo_heads"] * causal_pairs(sub)
+    threads = 0
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 0)))
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads or len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": (f"float64 NumPy oracle on requests {done} of the same batch "
+                   f"({sum(sub['q_lens'])} query tokens, {t_total:.1f} s)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="chunked", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the kernel shards by kv head or request with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_prefill_varlen_amd as ppa
+    from workloads import make_case
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = make_case(args.config)
+    q = case["query"].to(dev)
+    kv = case["kv_cache"]
+    kv = tuple(t.to(dev) for t in kv) if isinstance(kv, tuple) else kv.to(dev)
+    bt = case["block_tables"].to(dev)
+    sl = case["seq_lens"].to(dev)
+    cuq = case["cum_seq_lens_q"].to(dev)
+    cukv = case["cum_seq_lens_kv"].to(dev)
+    sinks = None if case["sinks"] is None else case["sinks"].to(dev)
+    out = torch.empty_like(q)
+    p = ppa.make_params(q, kv, None, bt, sl, case["max_q_len"], case["max_kv_len"], case["bmm1_scale"],
+                        case["bmm2_scale"], case["batch_size"], cuq, cukv, case["window_left"], out,
+                        case["kv_layout"], sinks)
+    st, msg = ppa.ppa_validate_metadata_host(p, case["cum_seq_lens_q"], case["cum_seq_lens_kv"],
+                                             case["seq_lens"], case["block_tables"])
+    if st != 0:
+        raise SystemExit(f"workload metadata invalid: {msg}")
+    stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream
+
+    for _ in range(args.warmup):
+        ppa.ppa_paged_prefill_attention(p, handle)
+    torch.cuda.synchronize(dev)
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t_begin.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        ppa.ppa_paged_prefill_attention(p, handle)
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize(dev)
+    total_ms = t_begin.elapsed_time(t_end)
+    launch_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    ms_per_step = total_ms / args.steps
+
+    flops = 4.0 * case["head_dim"] * case["num_qo_heads"] * causal_pairs(case)
+    tokens = sum(case["q_lens"])
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    kernel_tflops = flops / (launch_ms * 1e-3) / 1e12
+    fp8 = case["kv_dtype"] != "bf16"
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config,
+                   "query_tokens": tokens, "causal_gflop": round(flops / 1e9, 3),
+                   "parallelism": "none (one GPU)"},
+        "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(kernel_tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_bytes": algorithmic_bytes(case),
+            "kernel_ms": round(launch_ms, 5),
+            "kernel": "paged_prefill_kernel<%d,%s>" % (case["head_dim"], "fp8" if fp8 else "bf16"),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,236 @@
+/*
+ * ppa.h - C ABI of the MI355X (gfx950) paged prefill attention library.
+ *
+ * One call computes batched causal context ("prefill") attention over a
+ * paged KV cache, with the semantics of trtllm_batch_context_with_kv_cache as
+ * the FlashInfer API page describes it (section "Parameters"):
+ *
+ *   for request b:  q rows    query[cum_seq_lens_q[b] .. cum_seq_lens_q[b+1])
+ *                   kv_len    seq_lens[b]  (cached prefix + new tokens)
+ *                   prefix    kv_len - q_len; query row i sits at position
+ *                             prefix + i (the chunked-context figure of the
+ *                             TensorRT-LLM attention-backend article)
+ *                   KV token t  page block_tables[b][t / page_size],
+ *                               slot t % page_size; the page's address is the
+ *                               pool base + page id x page stride (article
+ *                               section "physical meaning of handle -> offset")
+ *   logit           s_ij = bmm1_scale * <q_i, k_j>
+ *   valid           j <= prefix + i  and  (window_left == -1  or
+ *                   j >= prefix + i - window_left)   (inclusive left window)
+ *   out_i           bmm2_scale * sum_valid e^{s_ij} v_j /
+ *                   (sum_valid e^{s_ij} + [sinks] e^{sinks[h]})
+ *   GQA             query head h reads kv head h / (num_qo_heads / num_kv_heads)
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers unless a parameter says "host".
+ *     The caller owns every buffer; the library allocates nothing and keeps
+ *     no state between calls.
+ *   - Strides are in ELEMENTS of the tensor they describe.  The innermost
+ *     (head_dim) stride must be 1.  The stride of a dimension of size 1 is
+ *     ignored.
+ *   - Functions return PPA_OK (0) or a negative ppa_status; when `msg` is not
+ *     NULL a human-readable reason is written there (NUL-terminated, at most
+ *     msg_len bytes).  Invalid input is rejected, never clamped or guessed.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Launches are
+ *     asynchronous; a device fault surfaces at the caller's next
+ *     synchronisation.
+ */
+#ifndef PPA_H
+#define PPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PPA_ABI_VERSION 1
+
+typedef enum ppa_status {
+  PPA_OK = 0,
+  PPA_ERR_NULL_POINTER = -1,   /* a required pointer is NULL                        */
+  PPA_ERR_DTYPE = -2,          /* unsupported dtype combination                     */
+  PPA_ERR_LAYOUT = -3,         /* kv_layout / kv_form / kv_planes out of range      */
+  PPA_ERR_SHAPE = -4,          /* a size is negative or inconsistent                */
+  PPA_ERR_STRIDE = -5,         /* innermost stride != 1, or a row not 16-B aligned  */
+  PPA_ERR_HEADS = -6,          /* num_qo_heads not a multiple of num_kv_heads       */
+  PPA_ERR_HEAD_DIM = -7,       /* head_dim not 64 or 128                            */
+  PPA_ERR_PAGE_SIZE = -8,      /* page_size not a power of two in [1, 65536]        */
+  PPA_ERR_WINDOW = -9,         /* window_left < -1                                  */
+  PPA_ERR_LENGTHS = -10,       /* a length exceeds max_q_len / max_kv_len, or q > kv */
+  PPA_ERR_TABLE = -11,         /* block table too narrow, or a page id out of range */
+  PPA_ERR_METADATA = -12,      /* cum_seq_lens not monotone / not matching seq_lens */
+  PPA_ERR_ALIGNMENT = -13,     /* a tensor base pointer not 16-byte aligned         */
+  PPA_ERR_WORKSPACE = -14,     /* workspace smaller than ppa_workspace_bytes()      */
+  PPA_ERR_ABI = -15,           /* abi_version / struct_size mismatch                */
+  PPA_ERR_HIP = -16            /* the HIP runtime reported an error at launch       */
+} ppa_status;
+
+typedef enum ppa_dtype {
+  PPA_DTYPE_BF16 = 1,          /* bfloat16                                          */
+  PPA_DTYPE_FP8_E4M3FN = 2,    /* OCP float8 e4m3fn (no infinities, max 448)        */
+  PPA_DTYPE_FP32 = 3
+} ppa_dtype;
+
+typedef enum ppa_kv_layout {
+  PPA_KV_LAYOUT_HND = 0,       /* page = [num_kv_heads, page_size, head_dim]        */
+  PPA_KV_LAYOUT_NHD = 1        /* page = [page_size, num_kv_heads, head_dim]        */
+} ppa_kv_layout;
+
+typedef enum ppa_kv_form {
+  PPA_KV_SPLIT = 0,            /* two tensors: K pool and V pool                    */
+  PPA_KV_COMBINED = 1          /* one tensor with K/V planes in dim 1               */
+} ppa_kv_form;
+
+/*
+ * Arguments of one batched call.  Field names follow the API page.
+ * Fill abi_version = PPA_ABI_VERSION and struct_size = sizeof(ppa_params).
+ */
+typedef struct ppa_params {
+  uint32_t abi_version;
+  uint32_t struct_size;
+
+  /* query [num_tokens, num_qo_heads, head_dim], dtype query_dtype (bf16).
+     Rows past cum_seq_lens_q[batch_size] are neither read for output nor
+     written. */
+  const void* query;
+  int32_t query_dtype;
+  int32_t num_tokens;
+  int32_t num_qo_heads;
+  int32_t head_dim;
+  int64_t query_strides[3];
+
+  /* Paged KV cache, dtype kv_dtype (bf16 or fp8 e4m3fn).
+       kv_form = PPA_KV_COMBINED: kv_cache is
+         [num_pages, kv_planes, num_kv_heads, page_size, head_dim]   (HND)
+         [num_pages, kv_planes, page_size, num_kv_heads, head_dim]   (NHD)
+         with kv_cache_strides[5]; plane 0 is K, plane 1 is V; with
+         kv_planes == 1, K and V are read from the same plane.
+       kv_form = PPA_KV_SPLIT: k_cache and v_cache are each
+         [num_pages, num_kv_heads, page_size, head_dim]              (HND)
+         [num_pages, page_size, num_kv_heads, head_dim]              (NHD)
+         with k_cache_strides[4] / v_cache_strides[4]. */
+  int32_t kv_form;
+  int32_t kv_layout;
+  int32_t kv_dtype;
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t page_size;
+  const void* kv_cache;
+  int32_t kv_planes;
+  int64_t kv_cache_strides[5];
+  const void* k_cache;
+  const void* v_cache;
+  int64_t k_cache_strides[4];
+  int64_t v_cache_strides[4];
+
+  /* Scratch owned by the caller; must hold ppa_workspace_bytes() bytes and be
+     zero on first use (API page, parameter workspace_buffer).  The library
+     leaves it as it found it. */
+  void* workspace;
+  size_t workspace_bytes;
+
+  /* Metadata, all int32 device arrays.
+       block_tables     [batch_size, block_tables_cols], row stride
+                        block_tables_row_stride; entries are page ids in
+                        [0, num_pages).  Columns past ceil(seq_lens[b] /
+                        page_size) are never read.
+       seq_lens         [batch_size]  KV length of each request (prefix included)
+       cum_seq_lens_q   [batch_size + 1]  ragged query offsets, starting at 0
+       cum_seq_lens_kv  [batch_size + 1]  may be NULL; only the host checker
+                        reads it (it must equal the running sum of seq_lens).
+     max_q_len / max_kv_len are upper bounds of the per-request lengths (they
+     size the launch); batch_size may be 0. */
+  const int32_t* block_tables;
+  int32_t block_tables_cols;
+  int64_t block_tables_row_stride;
+  const int32_t* seq_lens;
+  const int32_t* cum_seq_lens_q;
+  const int32_t* cum_seq_lens_kv;
+  int32_t batch_size;
+  int32_t max_q_len;
+  int32_t max_kv_len;
+
+  /* Fused scales (API page, bmm1_scale / bmm2_scale).  When a *_ptr field is
+     not NULL it points to one fp32 DEVICE scalar that replaces the value. */
+  float bmm1_scale;
+  float bmm2_scale;
+  const float* bmm1_scale_ptr;
+  const float* bmm2_scale_ptr;
+
+  /* Inclusive left window; -1 = the whole sequence. */
+  int32_t window_left;
+
+  /* Per-query-head fp32 sink logits [num_qo_heads], or NULL for none. */
+  const float* sinks;
+
+  /* out [num_tokens, num_qo_heads, head_dim], dtype out_dtype (bf16).  Only
+     rows [cum_seq_lens_q[0], cum_seq_lens_q[batch_size]) are written. */
+  void* out;
+  int32_t out_dtype;
+  int64_t out_strides[3];
+} ppa_params;
+
+/* ABI guards for bindings: the version this library was built with and
+   sizeof(ppa_params). */
+int32_t ppa_abi_version(void);
+size_t ppa_params_size(void);
+
+/* Static description of a status code (never NULL). */
+const char* ppa_strerror(int32_t status);
+
+/*
+ * Host-only check of everything the call can be checked for without reading
+ * device memory: pointers, dtypes, enums, head counts, head_dim, page size,
+ * window, strides and alignment, block-table width >= ceil(max_kv_len /
+ * page_size) (the table-width rule of the article's TrtllmAttentionMetadata
+ * section), workspace size.  Cheap; ppa_paged_prefill_attention runs it on
+ * every call.
+ */
+int32_t ppa_validate_shapes(const ppa_params* p, char* msg, size_t msg_len);
+
+/*
+ * The deep metadata check, on HOST copies of the device metadata (the
+ * debug page-table validation of the article's FlashInfer section):
+ * cum_seq_lens_q starts at 0, is non-decreasing and ends <= num_tokens;
+ * 0 <= q_len <= kv_len for every request (a query row with an empty causal
+ * span has no defined output); q_len <= max_q_len, kv_len <= max_kv_len;
+ * cum_seq_lens_kv (if not NULL) is the running sum of seq_lens; every table
+ * entry a request reaches lies in [0, num_pages).  block_tables uses the
+ * row stride of p->block_tables_row_stride.  Pure function of its inputs.
+ */
+int32_t ppa_validate_metadata_host(const ppa_params* p, const int32_t* cum_seq_lens_q,
+                                   const int32_t* cum_seq_lens_kv, const int32_t* seq_lens,
+                                   const int32_t* block_tables, char* msg, size_t msg_len);
+
+/* Bytes of workspace a call with these arguments needs (0 at present). */
+size_t ppa_workspace_bytes(const ppa_params* p);
+
+/*
+ * The batched paged prefill attention call.  Runs ppa_validate_shapes, then
+ * enqueues the kernel on `stream` and returns without waiting.  No host
+ * synchronisation, no allocation.  Metadata values are trusted to pass
+ * ppa_validate_metadata_host; if they do not, the output is unspecified but
+ * every memory access stays inside the tensors the shapes describe (page ids
+ * and table columns are clamped, query rows are bounded by num_tokens).
+ */
+int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream);
+
+/*
+ * Address-unit check: copies the first seq_lens[b] K (kv_idx 0) or V
+ * (kv_idx 1) tokens of every request out of the pages into `dst`, a
+ * contiguous [dst_rows, num_kv_heads, head_dim] device tensor of the cache
+ * dtype, request b at rows [cum_seq_lens_kv[b], cum_seq_lens_kv[b] +
+ * seq_lens[b]) - the contiguous token-major gather of the article's
+ * VanillaAttention path.  Rows at or past dst_rows are not written.
+ * Needs cum_seq_lens_kv.
+ */
+int32_t ppa_gather_paged_kv(const ppa_params* p, int32_t kv_idx, void* dst, int64_t dst_rows,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PPA_H */

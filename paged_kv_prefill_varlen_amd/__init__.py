@@ -1,0 +1,14 @@
+"""MI355X (gfx950) paged prefill attention.
+
+A thin binding over the C ABI declared in ``include/ppa.h`` (library
+``_lib/libppa.so``).  The functions named ``ppa_*`` mirror the C entry
+points one to one; ``batch_context_with_kv_cache`` mirrors the argument list
+of the FlashInfer API page for ``trtllm_batch_context_with_kv_cache`` and
+only marshals torch tensors into ``ppa_params``.  Every step of the
+attention runs in the HIP kernels; there is no fallback: importing this
+package without the built library raises ImportError.
+"""
+from .binding import (PPA_ABI_VERSION, PpaError, PpaParams, batch_context_with_kv_cache,  # noqa: F401
+                      library_path, make_params, ppa_abi_version, ppa_gather_paged_kv,
+                      ppa_paged_prefill_attention, ppa_params_size, ppa_strerror,
+                      ppa_validate_metadata_host, ppa_validate_shapes, ppa_workspace_bytes)

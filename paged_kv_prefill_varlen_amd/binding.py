@@ -1,0 +1,338 @@
+"""ctypes binding of ``include/ppa.h``: argument marshalling only.
+
+``PpaParams`` mirrors ``struct ppa_params`` field for field; its size is
+checked against the library's ``ppa_params_size()`` when the library loads.
+Torch is used for device pointers, strides and the current stream only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint32, c_void_p
+from typing import Optional, Sequence, Tuple, Union
+
+import numpy as np
+import torch
+
+PPA_ABI_VERSION = 1
+
+# enums of ppa.h
+PPA_DTYPE_BF16 = 1
+PPA_DTYPE_FP8_E4M3FN = 2
+PPA_DTYPE_FP32 = 3
+PPA_KV_LAYOUT_HND = 0
+PPA_KV_LAYOUT_NHD = 1
+PPA_KV_SPLIT = 0
+PPA_KV_COMBINED = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.environ.get("PPA_LIBRARY", os.path.join(_HERE, "_lib", "libppa.so"))
+
+
+class PpaParams(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", c_uint32),
+        ("struct_size", c_uint32),
+        ("query", c_void_p),
+        ("query_dtype", c_int32),
+        ("num_tokens", c_int32),
+        ("num_qo_heads", c_int32),
+        ("head_dim", c_int32),
+        ("query_strides", c_int64 * 3),
+        ("kv_form", c_int32),
+        ("kv_layout", c_int32),
+        ("kv_dtype", c_int32),
+        ("num_pages", c_int32),
+        ("num_kv_heads", c_int32),
+        ("page_size", c_int32),
+        ("kv_cache", c_void_p),
+        ("kv_planes", c_int32),
+        ("kv_cache_strides", c_int64 * 5),
+        ("k_cache", c_void_p),
+        ("v_cache", c_void_p),
+        ("k_cache_strides", c_int64 * 4),
+        ("v_cache_strides", c_int64 * 4),
+        ("workspace", c_void_p),
+        ("workspace_bytes", c_size_t),
+        ("block_tables", c_void_p),
+        ("block_tables_cols", c_int32),
+        ("block_tables_row_stride", c_int64),
+        ("seq_lens", c_void_p),
+        ("cum_seq_lens_q", c_void_p),
+        ("cum_seq_lens_kv", c_void_p),
+        ("batch_size", c_int32),
+        ("max_q_len", c_int32),
+        ("max_kv_len", c_int32),
+        ("bmm1_scale", c_float),
+        ("bmm2_scale", c_float),
+        ("bmm1_scale_ptr", c_void_p),
+        ("bmm2_scale_ptr", c_void_p),
+        ("window_left", c_int32),
+        ("sinks", c_void_p),
+        ("out", c_void_p),
+        ("out_dtype", c_int32),
+        ("out_strides", c_int64 * 3),
+    ]
+
+
+class PpaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        self.status = status
+        super().__init__(f"ppa status {status} ({ppa_strerror(status)}): {msg}")
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"HIP library {_LIB_PATH} is not built; run `python -m paged_kv_prefill_varlen_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER(PpaParams)
+    sigs = {
+        "ppa_abi_version": (c_int32, []),
+        "ppa_params_size": (c_size_t, []),
+        "ppa_strerror": (c_char_p, [c_int32]),
+        "ppa_validate_shapes": (c_int32, [P, c_char_p, c_size_t]),
+        "ppa_validate_metadata_host": (c_int32, [P, c_void_p, c_void_p, c_void_p, c_void_p, c_char_p, c_size_t]),
+        "ppa_workspace_bytes": (c_size_t, [P]),
+        "ppa_paged_prefill_attention": (c_int32, [P, c_void_p]),
+        "ppa_gather_paged_kv": (c_int32, [P, c_int32, c_void_p, c_int64, c_void_p]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.ppa_abi_version() != PPA_ABI_VERSION:
+        raise ImportError(f"{_LIB_PATH}: ABI version {lib.ppa_abi_version()}, binding expects {PPA_ABI_VERSION}")
+    if lib.ppa_params_size() != ctypes.sizeof(PpaParams):
+        raise ImportError(f"{_LIB_PATH}: sizeof(ppa_params) {lib.ppa_params_size()} != binding's "
+                          f"{ctypes.sizeof(PpaParams)}")
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+# --------------------------------------------------------------------------
+# one-to-one wrappers of the C entry points
+# --------------------------------------------------------------------------
+
+def ppa_abi_version() -> int:
+    return int(_lib.ppa_abi_version())
+
+
+def ppa_params_size() -> int:
+    return int(_lib.ppa_params_size())
+
+
+def ppa_strerror(status: int) -> str:
+    return _lib.ppa_strerror(int(status)).decode()
+
+
+def ppa_validate_shapes(params: PpaParams) -> Tuple[int, str]:
+    buf = ctypes.create_string_buffer(512)
+    st = _lib.ppa_validate_shapes(ctypes.byref(params), buf, len(buf))
+    return int(st), buf.value.decode()
+
+
+def _host_i32(x) -> Optional[np.ndarray]:
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def ppa_validate_metadata_host(params: PpaParams, cum_seq_lens_q, cum_seq_lens_kv, seq_lens,
+                               block_tables) -> Tuple[int, str]:
+    """Deep check on host copies (torch tensors are copied to the host)."""
+    cu_q = _host_i32(cum_seq_lens_q)
+    cu_kv = _host_i32(cum_seq_lens_kv)
+    sl = _host_i32(seq_lens)
+    bt = _host_i32(block_tables)
+    if bt is not None and bt.ndim != 2:
+        raise ValueError("block_tables must be 2-D")
+    # the host copy is dense: describe it with its own row stride
+    hp = PpaParams.from_buffer_copy(params)
+    if bt is not None:
+        hp.block_tables_row_stride = bt.shape[1]
+    ptr = lambda a: None if a is None else a.ctypes.data_as(c_void_p)  # noqa: E731
+    buf = ctypes.create_string_buffer(512)
+    st = _lib.ppa_validate_metadata_host(ctypes.byref(hp), ptr(cu_q), ptr(cu_kv), ptr(sl), ptr(bt),
+                                         buf, len(buf))
+    return int(st), buf.value.decode()
+
+
+def ppa_workspace_bytes(params: PpaParams) -> int:
+    return int(_lib.ppa_workspace_bytes(ctypes.byref(params)))
+
+
+def _stream_handle(device: torch.device, stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def ppa_paged_prefill_attention(params: PpaParams, stream: Union[int, "torch.cuda.Stream", None] = None,
+                                device: Optional[torch.device] = None) -> None:
+    h = _stream_handle(device or torch.device("cuda"), stream)
+    st = _lib.ppa_paged_prefill_attention(ctypes.byref(params), c_void_p(h))
+    if st != 0:
+        _, msg = ppa_validate_shapes(params)
+        raise PpaError(st, msg)
+
+
+def ppa_gather_paged_kv(params: PpaParams, kv_idx: int, dst: torch.Tensor, stream=None) -> None:
+    if not dst.is_contiguous():
+        raise ValueError("dst must be contiguous")
+    h = _stream_handle(dst.device, stream)
+    st = _lib.ppa_gather_paged_kv(ctypes.byref(params), int(kv_idx), c_void_p(dst.data_ptr()),
+                                  int(dst.shape[0]), c_void_p(h))
+    if st != 0:
+        _, msg = ppa_validate_shapes(params)
+        raise PpaError(st, msg)
+
+
+# --------------------------------------------------------------------------
+# marshalling torch tensors -> ppa_params
+# --------------------------------------------------------------------------
+
+_DTYPES = {torch.bfloat16: PPA_DTYPE_BF16, torch.float8_e4m3fn: PPA_DTYPE_FP8_E4M3FN,
+           torch.float32: PPA_DTYPE_FP32}
+
+
+def _dt(t: torch.Tensor) -> int:
+    return _DTYPES.get(t.dtype, 0)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype not in (torch.int32, torch.uint32):
+        raise TypeError(f"{name} must be int32, got {t.dtype}")
+    if t.dim() == 1 and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def make_params(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.Tensor],
+                block_tables: torch.Tensor, seq_lens: torch.Tensor, max_q_len: int, max_kv_len: int,
+                bmm1_scale, bmm2_scale, batch_size: int, cum_seq_lens_q: torch.Tensor,
+                cum_seq_lens_kv: Optional[torch.Tensor], window_left: int, out: torch.Tensor,
+                kv_layout: str = "HND", sinks=None) -> PpaParams:
+    """Fill a PpaParams from torch tensors (the FlashInfer API page's argument
+    list).  Keeps no reference to the tensors: the caller keeps them alive."""
+    p = PpaParams()
+    p.abi_version = PPA_ABI_VERSION
+    p.struct_size = ctypes.sizeof(PpaParams)
+    if query.dim() != 3:
+        raise ValueError("query must be [num_tokens, num_qo_heads, head_dim]")
+    p.query = _ptr(query)
+    p.query_dtype = _dt(query)
+    p.num_tokens, p.num_qo_heads, p.head_dim = (int(x) for x in query.shape)
+    p.query_strides[:] = list(query.stride())
+
+    layout = kv_layout.upper()
+    if layout not in ("HND", "NHD"):
+        raise ValueError(f"kv_layout must be 'HND' or 'NHD', got {kv_layout!r}")
+    p.kv_layout = PPA_KV_LAYOUT_HND if layout == "HND" else PPA_KV_LAYOUT_NHD
+    if isinstance(kv_cache, (tuple, list)):
+        if len(kv_cache) != 2:
+            raise ValueError("a kv_cache tuple must be (k_cache, v_cache)")
+        k, v = kv_cache
+        if k.dim() != 4 or v.dim() != 4 or k.shape != v.shape or k.dtype != v.dtype:
+            raise ValueError("k_cache and v_cache must be 4-D tensors of one shape and dtype")
+        p.kv_form = PPA_KV_SPLIT
+        p.kv_dtype = _dt(k)
+        p.k_cache, p.v_cache = _ptr(k), _ptr(v)
+        p.k_cache_strides[:] = list(k.stride())
+        p.v_cache_strides[:] = list(v.stride())
+        n, a1, a2, d = (int(x) for x in k.shape)
+        heads, page = (a1, a2) if layout == "HND" else (a2, a1)
+    else:
+        if kv_cache.dim() != 5:
+            raise ValueError("a single kv_cache must be 5-D [num_pages, 1 or 2, ...]")
+        p.kv_form = PPA_KV_COMBINED
+        p.kv_dtype = _dt(kv_cache)
+        p.kv_cache = _ptr(kv_cache)
+        p.kv_cache_strides[:] = list(kv_cache.stride())
+        n, planes, a1, a2, d = (int(x) for x in kv_cache.shape)
+        p.kv_planes = planes
+        heads, page = (a1, a2) if layout == "HND" else (a2, a1)
+    if d != p.head_dim:
+        raise ValueError(f"cache head_dim {d} != query head_dim {p.head_dim}")
+    p.num_pages, p.num_kv_heads, p.page_size = n, heads, page
+
+    if workspace_buffer is not None:
+        p.workspace = _ptr(workspace_buffer)
+        p.workspace_bytes = workspace_buffer.numel() * workspace_buffer.element_size()
+
+    bt = _i32(block_tables, "block_tables")
+    if bt.dim() != 2 or bt.stride(1) != 1:
+        raise ValueError("block_tables must be [batch_size, cols] with unit column stride")
+    p.block_tables = _ptr(bt)
+    p.block_tables_cols = int(bt.shape[1])
+    p.block_tables_row_stride = int(bt.stride(0))
+    p.seq_lens = _ptr(_i32(seq_lens, "seq_lens"))
+    p.cum_seq_lens_q = _ptr(_i32(cum_seq_lens_q, "cum_seq_lens_q"))
+    p.cum_seq_lens_kv = None if cum_seq_lens_kv is None else _ptr(_i32(cum_seq_lens_kv, "cum_seq_lens_kv"))
+    p.batch_size = int(batch_size)
+    p.max_q_len = int(max_q_len)
+    p.max_kv_len = int(max_kv_len)
+
+    for name, val in (("bmm1", bmm1_scale), ("bmm2", bmm2_scale)):
+        if isinstance(val, torch.Tensor):
+            if val.dtype != torch.float32 or val.numel() != 1:
+                raise TypeError(f"{name}_scale tensor must be one float32 element")
+            setattr(p, f"{name}_scale_ptr", _ptr(val))
+            setattr(p, f"{name}_scale", 0.0)
+        else:
+            setattr(p, f"{name}_scale", float(val))
+    p.window_left = int(window_left)
+
+    if sinks is not None:
+        if isinstance(sinks, (list, tuple)):
+            if len(sinks) != 1:
+                raise ValueError("sinks: pass one float32 tensor of num_qo_heads values")
+            sinks = sinks[0]
+        if sinks.dtype != torch.float32 or sinks.numel() != p.num_qo_heads or not sinks.is_contiguous():
+            raise ValueError("sinks must be a contiguous float32 tensor of num_qo_heads values")
+        p.sinks = _ptr(sinks)
+
+    if out.dim() != 3 or tuple(out.shape) != tuple(query.shape):
+        raise ValueError("out must have the shape of query")
+    p.out = _ptr(out)
+    p.out_dtype = _dt(out)
+    p.out_strides[:] = list(out.stride())
+    return p
+
+
+def batch_context_with_kv_cache(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.Tensor],
+                                block_tables: torch.Tensor, seq_lens: torch.Tensor, max_q_len: int,
+                                max_kv_len: int, bmm1_scale, bmm2_scale, batch_size: int,
+                                cum_seq_lens_q: torch.Tensor, cum_seq_lens_kv: Optional[torch.Tensor],
+                                window_left: int = -1, out: Optional[torch.Tensor] = None,
+                                out_dtype=None, kv_layout: str = "HND", sinks=None,
+                                validate: bool = False, stream=None) -> torch.Tensor:
+    """Batched paged prefill attention; argument list of the API page
+    (without the nvfp4 output and PDL options).  ``validate=True`` also runs
+    the deep metadata check on host copies (a device-to-host sync)."""
+    if out is None:
+        dt = query.dtype if out_dtype is None else out_dtype
+        out = torch.empty(query.shape, dtype=dt, device=query.device)
+    p = make_params(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_q_len, max_kv_len,
+                    bmm1_scale, bmm2_scale, batch_size, cum_seq_lens_q, cum_seq_lens_kv, window_left,
+                    out, kv_layout, sinks)
+    if validate:
+        st, msg = ppa_validate_metadata_host(p, cum_seq_lens_q, cum_seq_lens_kv, seq_lens, block_tables)
+        if st != 0:
+            raise PpaError(st, msg)
+    ppa_paged_prefill_attention(p, stream, query.device)
+    return out

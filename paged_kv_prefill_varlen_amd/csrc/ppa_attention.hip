@@ -1,0 +1,612 @@
+// Batched causal prefill attention over a paged KV cache, for gfx950 (CDNA4).
+//
+// Operation (FlashInfer API page for trtllm_batch_context_with_kv_cache,
+// section "Parameters"): for request b, the q_len new query rows sit at the
+// end of a kv_len-token sequence (prefix = kv_len - q_len, the chunked-context
+// figure of the TensorRT-LLM attention-backend article); row i sees key j
+// when j <= prefix + i and, with window_left >= 0, j >= prefix + i -
+// window_left.  out = bmm2_scale * softmax(bmm1_scale * q k^T) v, where a
+// per-head sink adds e^{sink} to the softmax denominator only.
+//
+// Work decomposition
+//   One workgroup = 4 waves = 256 "rows"; a row is one (token, q head) pair of
+//   one request and one kv head.  The GW = min(G, 16) query heads of a GQA
+//   group that share the kv head are interleaved (row = token * GW + head), so
+//   a K/V tile staged once in LDS serves every head of the group and the
+//   causal boundary of a 32-row MFMA tile spans only 32 / GW tokens.
+//   Each wave owns 64 rows = two 32-column MFMA tiles.
+//   The grid is 1-D and ordered heaviest-first: blockIdx / R picks the query
+//   tile from the last (longest causal span) to the first, blockIdx % R picks
+//   (request, kv head, head group).  With R a multiple of 8, every tile of one
+//   (request, kv head) lands on the same XCD (blocks go round-robin over the
+//   8 XCDs), so its K/V stays in one L2.
+//
+// Per 64-key tile
+//   1. page ids -> K rows (natural layout) and V rows (transposed in
+//      registers) into double-buffered LDS; fp8 codes are widened to bf16 on
+//      the way (exact: every e4m3fn value is a bf16 value);
+//   2. S^T = K Q^T on v_mfma_f32_32x32x16_bf16: keys along M, rows along N,
+//      so a lane holds 32 keys of one row and its partner lane (lane ^ 32) the
+//      other 32: row max / sum need one cross-lane step;
+//   3. mask (boundary tiles only), online softmax in the exp2 domain with
+//      the running maximum moved only when a row's maximum grows by more than
+//      2^8 (exact: softmax does not depend on the subtracted constant);
+//   4. O^T += V^T P^T on the same MFMA; P goes from the S accumulator straight
+//      into the B operand, because the K rows are fed to the first MFMA in an
+//      order (bits 2 and 3 of the row index swapped) that leaves each lane half
+//      holding 8 consecutive keys.
+//   Tiles wholly outside a wave's causal/window band are skipped; only tiles
+//   cut by the band are masked.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ppa.h"
+#include "ppa_internal.h"
+#include "ppa_page_addr.hpp"
+
+namespace ppa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 256;      // rows per workgroup
+constexpr int kBK = 64;         // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleThreshold = 8.0f;   // log2 units
+constexpr float kNegInf = -__builtin_inff();
+
+struct AttnArgs {
+  const uint16_t* q;
+  int64_t q_tok, q_head;
+  uint16_t* out;
+  int64_t o_tok, o_head;
+  PagedPlane k, v;
+  const int32_t* block_tables;
+  int64_t bt_row_stride;
+  int32_t bt_cols;
+  int32_t num_pages;
+  int32_t page_shift;
+  const int32_t* seq_lens;
+  const int32_t* cu_q;
+  int32_t num_tokens;
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t group;       // q heads per kv head
+  int32_t gw;          // q heads per workgroup
+  int32_t n_hg;        // head groups per kv head
+  int32_t tq;          // tokens per workgroup
+  int32_t n_qt;        // query tiles per request (upper bound)
+  int32_t window_left;
+  float bmm1, bmm2;
+  const float* bmm1_ptr;
+  const float* bmm2_ptr;
+  const float* sinks;
+};
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);   // v_cvt_pk_bf16_f32, round to nearest even
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// 4 fp8 e4m3fn codes -> 4 bf16 (two packed dwords).  Exact.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  return u32x2{pack_bf16(lo[0], lo[1]), pack_bf16(hi[0], hi[1])};
+}
+
+// Row index fed to the A operand of the S^T MFMA: bits 2 and 3 swapped.  With
+// this order, accumulator element v of lane half h holds key
+// 16 * (v / 8) + 8 * h + v % 8 of its 32-key block.
+__device__ __forceinline__ int swap_bits23(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+template <int D, bool FP8>
+struct Tile {
+  static constexpr int EB = FP8 ? 1 : 2;              // bytes per cache element
+  // K: 16-byte loads, natural layout
+  static constexpr int K_CHUNK = 16 / EB;              // elements per load
+  static constexpr int K_TPR = D / K_CHUNK;            // threads per key row
+  static constexpr int K_RPP = kThreads / K_TPR;       // rows per pass
+  static constexpr int K_PASSES = kBK / K_RPP;
+  // V: thread = 4 consecutive keys x V_DPT head-dim values, transposed in regs
+  static constexpr int V_DPT = D / 16;
+  static constexpr int V_LOAD_BYTES = V_DPT * EB;      // per key
+  static constexpr int V_DW = V_LOAD_BYTES / 4;        // dwords per key (raw)
+  // LDS row strides in bf16 elements (padded to keep the MFMA operand reads
+  // and the transposed writes free of bank conflicts)
+  static constexpr int KS = D + 8;
+  static constexpr int VS = (D == 128) ? kBK + 8 : kBK + 16;
+  static constexpr int K_ELEMS = kBK * KS;
+  static constexpr int V_ELEMS = D * VS;
+  static_assert(K_PASSES * K_RPP == kBK, "K tile mapping");
+  static_assert(V_DW >= 1, "V load");
+};
+
+template <int D, bool FP8>
+struct Loader {
+  using T = Tile<D, FP8>;
+  u32x4 kreg[T::K_PASSES];
+  uint32_t vreg[4][T::V_DW];
+  int kpid[T::K_PASSES];
+  int vpid[4];
+
+  __device__ __forceinline__ void fetch_ids(const PageTable& pt, int k0, int tid) {
+    const int krow0 = tid / T::K_TPR;
+    for (int p = 0; p < T::K_PASSES; ++p) kpid[p] = page_id(pt, k0 + krow0 + p * T::K_RPP);
+    const int kg = tid & 15;
+    for (int r = 0; r < 4; ++r) vpid[r] = page_id(pt, k0 + 4 * kg + r);
+  }
+
+  __device__ __forceinline__ void fetch_rows(const AttnArgs& a, int hk, int k0, int kv_len,
+                                             int page_mask, int tid) {
+    const int krow0 = tid / T::K_TPR;
+    const int kchunk = tid % T::K_TPR;
+    for (int p = 0; p < T::K_PASSES; ++p) {
+      const int key = k0 + krow0 + p * T::K_RPP;
+      if (key < kv_len) {
+        const uint8_t* src = token_row<T::EB>(a.k, kpid[p], page_mask, key, hk, kchunk * T::K_CHUNK);
+        kreg[p] = *reinterpret_cast<const u32x4*>(src);
+      } else {
+        kreg[p] = u32x4{0, 0, 0, 0};
+      }
+    }
+    const int kg = tid & 15;
+    const int dg = tid >> 4;
+    for (int r = 0; r < 4; ++r) {
+      const int key = k0 + 4 * kg + r;
+      if (key < kv_len) {
+        const uint8_t* src = token_row<T::EB>(a.v, vpid[r], page_mask, key, hk, dg * T::V_DPT);
+        if constexpr (T::V_DW == 4) {
+          u32x4 x = *reinterpret_cast<const u32x4*>(src);
+          for (int i = 0; i < 4; ++i) vreg[r][i] = x[i];
+        } else if constexpr (T::V_DW == 2) {
+          u32x2 x = *reinterpret_cast<const u32x2*>(src);
+          vreg[r][0] = x[0];
+          vreg[r][1] = x[1];
+        } else {
+          vreg[r][0] = *reinterpret_cast<const uint32_t*>(src);
+        }
+      } else {
+        for (int i = 0; i < T::V_DW; ++i) vreg[r][i] = 0;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(__bf16* klds, __bf16* vlds, int tid) const {
+    const int krow0 = tid / T::K_TPR;
+    const int kchunk = tid % T::K_TPR;
+    for (int p = 0; p < T::K_PASSES; ++p) {
+      __bf16* dst = klds + (krow0 + p * T::K_RPP) * T::KS + kchunk * T::K_CHUNK;
+      if constexpr (!FP8) {
+        *reinterpret_cast<u32x4*>(dst) = kreg[p];
+      } else {
+        u32x2 a0 = fp8x4_to_bf16x4(kreg[p][0]);
+        u32x2 a1 = fp8x4_to_bf16x4(kreg[p][1]);
+        u32x2 a2 = fp8x4_to_bf16x4(kreg[p][2]);
+        u32x2 a3 = fp8x4_to_bf16x4(kreg[p][3]);
+        reinterpret_cast<u32x4*>(dst)[0] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+        reinterpret_cast<u32x4*>(dst)[1] = u32x4{a2[0], a2[1], a3[0], a3[1]};
+      }
+    }
+    // V: widen to bf16 pairs, then 4 keys x V_DPT values -> V_DPT rows of 4 keys
+    constexpr int PAIRS = T::V_DPT / 2;
+    uint32_t w[4][PAIRS];
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (!FP8) {
+        for (int i = 0; i < PAIRS; ++i) w[r][i] = vreg[r][i];
+      } else {
+        for (int i = 0; i < T::V_DW; ++i) {
+          u32x2 x = fp8x4_to_bf16x4(vreg[r][i]);
+          w[r][2 * i] = x[0];
+          w[r][2 * i + 1] = x[1];
+        }
+      }
+    }
+    const int kg = tid & 15;
+    const int dg = tid >> 4;
+    for (int i = 0; i < PAIRS; ++i) {
+      // even head-dim value: low halves; odd: high halves
+      const uint32_t lo01 = __builtin_amdgcn_perm(w[1][i], w[0][i], 0x05040100u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(w[3][i], w[2][i], 0x05040100u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(w[1][i], w[0][i], 0x07060302u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(w[3][i], w[2][i], 0x07060302u);
+      const int d = dg * T::V_DPT + 2 * i;
+      *reinterpret_cast<u32x2*>(vlds + d * T::VS + 4 * kg) = u32x2{lo01, lo23};
+      *reinterpret_cast<u32x2*>(vlds + (d + 1) * T::VS + 4 * kg) = u32x2{hi01, hi23};
+    }
+  }
+};
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(kThreads) void paged_prefill_kernel(AttnArgs a) {
+  using T = Tile<D, FP8>;
+  constexpr int KSTEPS = D / 16;   // MFMA K-steps over head_dim
+  constexpr int MD = D / 32;       // 32-wide head_dim tiles of O^T
+  __shared__ __attribute__((aligned(16))) __bf16 klds[2][T::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) __bf16 vlds[2][T::V_ELEMS];
+
+  // ---- which work item --------------------------------------------------
+  const int R = a.batch * a.num_kv_heads * a.n_hg;
+  const int L = blockIdx.x;
+  const int qt = a.n_qt - 1 - L / R;
+  const int rest = L % R;
+  const int b = rest / (a.num_kv_heads * a.n_hg);
+  const int hk = (rest / a.n_hg) % a.num_kv_heads;
+  const int hg = rest % a.n_hg;
+
+  int q1 = a.cu_q[b + 1];
+  int q0 = a.cu_q[b];
+  q1 = q1 < a.num_tokens ? q1 : a.num_tokens;
+  q0 = q0 < 0 ? 0 : (q0 < q1 ? q0 : q1);
+  const int q_len = q1 - q0;
+  int kv_len = a.seq_lens[b];
+  kv_len = kv_len < 0 ? 0 : kv_len;
+  const int t0 = qt * a.tq;
+  if (t0 >= q_len) return;
+  const int ntok = q_len - t0 < a.tq ? q_len - t0 : a.tq;
+  const int prefix = kv_len - q_len;
+  const int h0 = hk * a.group + hg * a.gw;
+  const int nheads = a.group - hg * a.gw < a.gw ? a.group - hg * a.gw : a.gw;
+  const int W = a.window_left;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  float c = (a.bmm1_ptr ? *a.bmm1_ptr : a.bmm1) * kLog2e;
+  const float bmm2 = a.bmm2_ptr ? *a.bmm2_ptr : a.bmm2;
+  const bool negate_q = c < 0.f;   // fold the sign into Q (exact for bf16)
+  c = negate_q ? -c : c;
+
+  // ---- the wave's rows ----------------------------------------------------
+  int tok[2], hd[2], pos[2];
+  bool rvalid[2];
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = wave * 64 + nt * 32 + col;
+    tok[nt] = r / a.gw;
+    hd[nt] = r % a.gw;
+    rvalid[nt] = tok[nt] < ntok && hd[nt] < nheads;
+    pos[nt] = prefix + t0 + tok[nt];
+  }
+  const int wtok_first = (wave * 64) / a.gw;
+  int wtok_last = (wave * 64 + 63) / a.gw;
+  wtok_last = wtok_last < ntok - 1 ? wtok_last : ntok - 1;
+  const bool wave_active = wtok_first < ntok;
+  const int wpos_first = prefix + t0 + wtok_first;
+  const int wpos_last = prefix + t0 + wtok_last;
+  const int wkey_hi = wpos_last < kv_len - 1 ? wpos_last : kv_len - 1;
+  const int wkey_lo = W >= 0 ? (wpos_first - W > 0 ? wpos_first - W : 0) : 0;
+
+  // ---- Q into registers (B operand of S^T = K Q^T) ------------------------
+  bf16x8 qf[2][KSTEPS];
+  for (int nt = 0; nt < 2; ++nt) {
+    const uint16_t* qrow = a.q + static_cast<int64_t>(q0 + t0 + tok[nt]) * a.q_tok +
+                           static_cast<int64_t>(h0 + hd[nt]) * a.q_head;
+    for (int s = 0; s < KSTEPS; ++s) {
+      u32x4 x = u32x4{0, 0, 0, 0};
+      if (rvalid[nt]) x = *reinterpret_cast<const u32x4*>(qrow + s * 16 + half * 8);
+      if (negate_q) x ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      qf[nt][s] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  f32x16 oacc[2][MD];
+  for (int nt = 0; nt < 2; ++nt)
+    for (int md = 0; md < MD; ++md) oacc[nt][md] = f32x16{};
+  float m_run[2] = {kNegInf, kNegInf};
+  float l_part[2] = {0.f, 0.f};
+
+  // ---- K/V tile range of the workgroup -------------------------------------
+  const int pos_first = prefix + t0;
+  const int pos_last = prefix + t0 + ntok - 1;
+  const int key_hi = pos_last < kv_len - 1 ? pos_last : kv_len - 1;
+  const int key_lo = W >= 0 ? (pos_first - W > 0 ? pos_first - W : 0) : 0;
+  const int tile_lo = key_lo / kBK;
+  const int tile_hi = key_hi >= 0 ? key_hi / kBK : -1;
+
+  PageTable pt;
+  pt.row = a.block_tables + static_cast<int64_t>(b) * a.bt_row_stride;
+  pt.cols = a.bt_cols;
+  pt.num_pages = a.num_pages;
+  pt.page_shift = a.page_shift;
+  const int page_mask = (1 << a.page_shift) - 1;
+
+  Loader<D, FP8> ld;
+  Loader<D, FP8> ld_next_ids;   // page ids one tile further ahead
+  if (tile_lo <= tile_hi) {
+    ld.fetch_ids(pt, tile_lo * kBK, tid);
+    ld.fetch_rows(a, hk, tile_lo * kBK, kv_len, page_mask, tid);
+    if (tile_lo + 1 <= tile_hi) ld_next_ids.fetch_ids(pt, (tile_lo + 1) * kBK, tid);
+    ld.store(klds[0], vlds[0], tid);
+  }
+  __syncthreads();
+
+  const int krow_lane = swap_bits23(col);
+
+  for (int tile = tile_lo; tile <= tile_hi; ++tile) {
+    const int buf = (tile - tile_lo) & 1;
+    const int k0 = tile * kBK;
+    const bool more = tile + 1 <= tile_hi;
+    if (more) {
+      for (int p = 0; p < Tile<D, FP8>::K_PASSES; ++p) ld.kpid[p] = ld_next_ids.kpid[p];
+      for (int r = 0; r < 4; ++r) ld.vpid[r] = ld_next_ids.vpid[r];
+      ld.fetch_rows(a, hk, k0 + kBK, kv_len, page_mask, tid);
+      if (tile + 2 <= tile_hi) ld_next_ids.fetch_ids(pt, k0 + 2 * kBK, tid);
+    }
+
+    const bool wave_tile = wave_active && k0 <= wkey_hi && k0 + kBK - 1 >= wkey_lo;
+    if (wave_tile) {
+      // S^T = K Q^T over head_dim
+      f32x16 sacc[2][2];
+      for (int mt = 0; mt < 2; ++mt)
+        for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = f32x16{};
+      const __bf16* kb = klds[buf];
+      for (int s = 0; s < KSTEPS; ++s) {
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x8 kf =
+              *reinterpret_cast<const bf16x8*>(kb + (mt * 32 + krow_lane) * T::KS + s * 16 + half * 8);
+          for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = mfma32(kf, qf[nt][s], sacc[mt][nt]);
+        }
+      }
+
+      // masking: only tiles cut by the causal / window / length bounds
+      const bool need_mask = (k0 + kBK - 1 > wpos_first) || (W >= 0 && k0 < wpos_last - W) ||
+                             (k0 + kBK > kv_len);
+      float mx[2];
+      for (int nt = 0; nt < 2; ++nt) {
+        float m = kNegInf;
+        if (need_mask) {
+          const int hi = pos[nt] < kv_len - 1 ? pos[nt] : kv_len - 1;
+          const int lo = W >= 0 ? pos[nt] - W : -1;
+          for (int mt = 0; mt < 2; ++mt)
+            for (int v = 0; v < 16; ++v) {
+              const int key = k0 + mt * 32 + 16 * (v >> 3) + 8 * half + (v & 7);
+              const bool ok = key <= hi && key >= lo;
+              sacc[mt][nt][v] = ok ? sacc[mt][nt][v] : kNegInf;
+              m = fmaxf(m, sacc[mt][nt][v]);
+            }
+        } else {
+          for (int mt = 0; mt < 2; ++mt)
+            for (int v = 0; v < 16; ++v) m = fmaxf(m, sacc[mt][nt][v]);
+        }
+        mx[nt] = fmaxf(m, __shfl_xor(m, 32));
+      }
+
+      // lazy rescale of the running maximum (log2 domain)
+      bool need[2];
+      float mtile[2];
+      for (int nt = 0; nt < 2; ++nt) {
+        mtile[nt] = mx[nt] == kNegInf ? kNegInf : mx[nt] * c;
+        need[nt] = mtile[nt] > m_run[nt] + kRescaleThreshold;
+      }
+      if (__ballot(need[0] || need[1]) != 0ull) {
+        for (int nt = 0; nt < 2; ++nt) {
+          const float m_new = need[nt] ? mtile[nt] : m_run[nt];
+          const float alpha = need[nt] ? __builtin_amdgcn_exp2f(m_run[nt] - m_new) : 1.f;
+          m_run[nt] = m_new;
+          l_part[nt] *= alpha;
+          for (int md = 0; md < MD; ++md) oacc[nt][md] *= alpha;
+        }
+      }
+
+      // P = exp2(c s - m), row partial sums, bf16 B operands of O^T += V^T P^T
+      bf16x8 pb[2][4];
+      for (int nt = 0; nt < 2; ++nt) {
+        const float mb = m_run[nt] == kNegInf ? 0.f : m_run[nt];
+        float sum = 0.f;
+        for (int mt = 0; mt < 2; ++mt) {
+          float p[16];
+          for (int v = 0; v < 16; ++v) {
+            p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][nt][v], c, -mb));
+            if (need_mask) p[v] = sacc[mt][nt][v] == kNegInf ? 0.f : p[v];
+            sum += p[v];
+          }
+          for (int sh = 0; sh < 2; ++sh) {
+            u32x4 w;
+            for (int e = 0; e < 4; ++e) w[e] = pack_bf16(p[8 * sh + 2 * e], p[8 * sh + 2 * e + 1]);
+            pb[nt][2 * mt + sh] = __builtin_bit_cast(bf16x8, w);
+          }
+        }
+        l_part[nt] += sum;
+      }
+
+      const __bf16* vb = vlds[buf];
+      for (int ks = 0; ks < 4; ++ks) {
+        for (int md = 0; md < MD; ++md) {
+          const bf16x8 vf =
+              *reinterpret_cast<const bf16x8*>(vb + (md * 32 + col) * T::VS + ks * 16 + half * 8);
+          for (int nt = 0; nt < 2; ++nt) oacc[nt][md] = mfma32(vf, pb[nt][ks], oacc[nt][md]);
+        }
+      }
+    }
+
+    if (more) ld.store(klds[buf ^ 1], vlds[buf ^ 1], tid);
+    __syncthreads();
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+  if (!wave_active) return;
+  for (int nt = 0; nt < 2; ++nt) {
+    float l = l_part[nt] + __shfl_xor(l_part[nt], 32);
+    if (!rvalid[nt]) continue;
+    const int h = h0 + hd[nt];
+    const float mb = m_run[nt] == kNegInf ? 0.f : m_run[nt];
+    if (a.sinks) l += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - mb);
+    const float inv = bmm2 / l;
+    uint16_t* orow = a.out + static_cast<int64_t>(q0 + t0 + tok[nt]) * a.o_tok +
+                     static_cast<int64_t>(h) * a.o_head;
+    for (int md = 0; md < MD; ++md) {
+      for (int g = 0; g < 4; ++g) {
+        const int d = md * 32 + 8 * g + 4 * half;
+        const u32x2 w = u32x2{pack_bf16(oacc[nt][md][4 * g] * inv, oacc[nt][md][4 * g + 1] * inv),
+                              pack_bf16(oacc[nt][md][4 * g + 2] * inv, oacc[nt][md][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + d) = w;
+      }
+    }
+  }
+}
+
+// ---- address-unit check: paged K or V -> contiguous [tokens, H_kv, D] ------
+struct GatherArgs {
+  PagedPlane plane;
+  const int32_t* block_tables;
+  int64_t bt_row_stride;
+  int32_t bt_cols, num_pages, page_shift;
+  const int32_t* seq_lens;
+  const int32_t* cu_kv;
+  int32_t num_kv_heads, head_dim, elem_bytes;
+  uint8_t* dst;
+  int64_t dst_rows;
+};
+
+constexpr int kGatherTokens = 64;
+
+__global__ __launch_bounds__(256) void gather_kernel(GatherArgs g) {
+  const int b = blockIdx.y;
+  const int kv_len = g.seq_lens[b];
+  const int t0 = blockIdx.x * kGatherTokens;
+  if (t0 >= kv_len) return;
+  PageTable pt;
+  pt.row = g.block_tables + static_cast<int64_t>(b) * g.bt_row_stride;
+  pt.cols = g.bt_cols;
+  pt.num_pages = g.num_pages;
+  pt.page_shift = g.page_shift;
+  const int page_mask = (1 << g.page_shift) - 1;
+  const int row_bytes = g.head_dim * g.elem_bytes;
+  const int chunks = row_bytes / 16;                   // 16-byte chunks per (token, head)
+  const int per_token = chunks * g.num_kv_heads;
+  const int64_t dst0 = g.cu_kv[b];
+  for (int i = threadIdx.x; i < kGatherTokens * per_token; i += blockDim.x) {
+    const int t = t0 + i / per_token;
+    if (t >= kv_len) break;
+    const int hk = (i % per_token) / chunks;
+    const int ch = i % chunks;
+    const int64_t row = dst0 + t;
+    if (row < 0 || row >= g.dst_rows) continue;
+    const int id = page_id(pt, t);
+    const int elem = ch * 16 / g.elem_bytes;
+    const uint8_t* src = g.elem_bytes == 2 ? token_row<2>(g.plane, id, page_mask, t, hk, elem)
+                                           : token_row<1>(g.plane, id, page_mask, t, hk, elem);
+    uint8_t* dst = g.dst + ((row * g.num_kv_heads + hk) * static_cast<int64_t>(row_bytes)) + ch * 16;
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+  }
+}
+
+int log2_exact(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+template <int D, bool FP8>
+hipError_t launch(const AttnArgs& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((paged_prefill_kernel<D, FP8>), dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace ppa
+
+using namespace ppa;
+
+extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream) {
+  char msg[8];
+  int32_t st = ppa_validate_shapes(p, msg, sizeof msg);
+  if (st != PPA_OK) return st;
+  if (p->batch_size == 0 || p->max_q_len == 0 || p->num_tokens == 0) return PPA_OK;
+
+  CacheView cv;
+  resolve_cache(p, &cv);
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(p->query);
+  a.q_tok = p->num_tokens > 1 ? p->query_strides[0] : 0;
+  a.q_head = p->num_qo_heads > 1 ? p->query_strides[1] : 0;
+  a.out = static_cast<uint16_t*>(p->out);
+  a.o_tok = p->num_tokens > 1 ? p->out_strides[0] : 0;
+  a.o_head = p->num_qo_heads > 1 ? p->out_strides[1] : 0;
+  a.k = PagedPlane{static_cast<const uint8_t*>(cv.k_base), cv.k_page, cv.k_head, cv.k_tok};
+  a.v = PagedPlane{static_cast<const uint8_t*>(cv.v_base), cv.v_page, cv.v_head, cv.v_tok};
+  a.block_tables = p->block_tables;
+  a.bt_row_stride = p->batch_size > 1 ? p->block_tables_row_stride : 0;
+  a.bt_cols = p->block_tables_cols;
+  a.num_pages = p->num_pages;
+  a.page_shift = log2_exact(p->page_size);
+  a.seq_lens = p->seq_lens;
+  a.cu_q = p->cum_seq_lens_q;
+  a.num_tokens = p->num_tokens;
+  a.batch = p->batch_size;
+  a.num_kv_heads = p->num_kv_heads;
+  a.group = p->num_qo_heads / p->num_kv_heads;
+  a.gw = a.group < 16 ? a.group : 16;
+  a.n_hg = (a.group + a.gw - 1) / a.gw;
+  a.tq = kRows / a.gw;
+  a.n_qt = (p->max_q_len + a.tq - 1) / a.tq;
+  a.window_left = p->window_left;
+  a.bmm1 = p->bmm1_scale;
+  a.bmm2 = p->bmm2_scale;
+  a.bmm1_ptr = p->bmm1_scale_ptr;
+  a.bmm2_ptr = p->bmm2_scale_ptr;
+  a.sinks = p->sinks;
+
+  const int64_t grid = static_cast<int64_t>(a.n_qt) * a.batch * a.num_kv_heads * a.n_hg;
+  if (grid > 0x7fffffff) return PPA_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  const bool fp8 = p->kv_dtype == PPA_DTYPE_FP8_E4M3FN;
+  if (p->head_dim == 128)
+    e = fp8 ? launch<128, true>(a, static_cast<int>(grid), s) : launch<128, false>(a, static_cast<int>(grid), s);
+  else
+    e = fp8 ? launch<64, true>(a, static_cast<int>(grid), s) : launch<64, false>(a, static_cast<int>(grid), s);
+  return e == hipSuccess ? PPA_OK : PPA_ERR_HIP;
+}
+
+extern "C" int32_t ppa_gather_paged_kv(const ppa_params* p, int32_t kv_idx, void* dst, int64_t dst_rows,
+                                       void* stream) {
+  char msg[8];
+  int32_t st = ppa_validate_shapes(p, msg, sizeof msg);
+  if (st != PPA_OK) return st;
+  if (kv_idx != 0 && kv_idx != 1) return PPA_ERR_SHAPE;
+  if (p->batch_size == 0 || p->max_kv_len == 0) return PPA_OK;
+  if (p->cum_seq_lens_kv == nullptr || dst == nullptr) return PPA_ERR_NULL_POINTER;
+  if (dst_rows < 0) return PPA_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(dst) & 15u) != 0) return PPA_ERR_ALIGNMENT;
+  if (p->kv_form == PPA_KV_SPLIT ? (p->k_cache == nullptr || p->v_cache == nullptr)
+                                 : p->kv_cache == nullptr)
+    return PPA_ERR_NULL_POINTER;
+  CacheView cv;
+  resolve_cache(p, &cv);
+  GatherArgs g{};
+  g.plane = kv_idx == 0 ? PagedPlane{static_cast<const uint8_t*>(cv.k_base), cv.k_page, cv.k_head, cv.k_tok}
+                        : PagedPlane{static_cast<const uint8_t*>(cv.v_base), cv.v_page, cv.v_head, cv.v_tok};
+  g.block_tables = p->block_tables;
+  g.bt_row_stride = p->batch_size > 1 ? p->block_tables_row_stride : 0;
+  g.bt_cols = p->block_tables_cols;
+  g.num_pages = p->num_pages;
+  g.page_shift = log2_exact(p->page_size);
+  g.seq_lens = p->seq_lens;
+  g.cu_kv = p->cum_seq_lens_kv;
+  g.num_kv_heads = p->num_kv_heads;
+  g.head_dim = p->head_dim;
+  g.elem_bytes = dtype_bytes(p->kv_dtype);
+  g.dst = static_cast<uint8_t*>(dst);
+  g.dst_rows = dst_rows;
+  dim3 grid((p->max_kv_len + kGatherTokens - 1) / kGatherTokens, p->batch_size);
+  hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), g);
+  return hipGetLastError() == hipSuccess ? PPA_OK : PPA_ERR_HIP;
+}

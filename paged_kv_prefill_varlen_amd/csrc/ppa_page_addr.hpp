@@ -1,0 +1,57 @@
+// Page-table address unit (device side).
+//
+// A request's logical KV token t lives in page block_tables[b][t >> log2(P)]
+// at slot t & (P - 1); the page's first element is the pool base plus
+// page id x page stride (FlashInfer API page, parameters kv_cache and
+// block_tables; TensorRT-LLM attention-backend article, section "physical
+// meaning of handle -> offset": tables hold ids, the kernel multiplies by the
+// stride).  Because only strides differ between HND and NHD, and between a
+// split and a combined cache, one formula serves all of them:
+//
+//   row(t, hk) = base + id * page_stride + hk * head_stride + slot * token_stride
+//
+// Ids are int32; the products are int64 so pools above 4 GiB work.  The
+// column index is clamped to the table width and the id to [0, num_pages),
+// so metadata that the host checker would reject can never send a read
+// outside the pool.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ppa {
+
+struct PagedPlane {
+  const uint8_t* base;   // first byte of the plane (K or V)
+  int64_t page_stride;   // elements
+  int64_t head_stride;   // elements
+  int64_t tok_stride;    // elements
+};
+
+struct PageTable {
+  const int32_t* row;    // block_tables + b * row_stride
+  int32_t cols;          // table width
+  int32_t num_pages;
+  int32_t page_shift;    // log2(page_size)
+};
+
+__device__ __forceinline__ int page_id(const PageTable& pt, int token) {
+  int col = token >> pt.page_shift;
+  col = col < pt.cols - 1 ? col : pt.cols - 1;
+  int id = pt.row[col];
+  id = id < 0 ? 0 : id;
+  id = id < pt.num_pages ? id : pt.num_pages - 1;
+  return id;
+}
+
+// Byte address of element `elem` of token `token` (page `id`) for kv head hk.
+template <int ELEM_BYTES>
+__device__ __forceinline__ const uint8_t* token_row(const PagedPlane& pl, int id, int page_mask,
+                                                    int token, int hk, int elem) {
+  const int64_t off = static_cast<int64_t>(id) * pl.page_stride +
+                      static_cast<int64_t>(hk) * pl.head_stride +
+                      static_cast<int64_t>(token & page_mask) * pl.tok_stride + elem;
+  return pl.base + off * ELEM_BYTES;
+}
+
+}  // namespace ppa

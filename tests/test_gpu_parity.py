@@ -1,0 +1,255 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Small and edge-case workloads are compared element by element over every
+written row; the full-size workloads are compared on sampled rows that the
+oracle computes one at a time, plus properties that hold at any size (no
+NaN, untouched guard rows).  Tolerances: bf16 output max |err| <= 2e-2 and
+mean |err| <= 2e-3; fp8 KV max |err| <= 6e-2.
+"""
+from __future__ import annotations
+
+import math
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (assert_close, errors, guard_rows_untouched, run_gpu, to_device)
+from oracle.case_io import decode_tensor, oracle_inputs, run_oracle, run_oracle_rows
+from workloads import make_case, make_custom_case
+from workloads.cases import relayout
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# --------------------------------------------------------------------------
+# the address unit: paged K/V gathered on the GPU == the generator's tokens
+# --------------------------------------------------------------------------
+
+GATHER_CASES = [
+    dict(kv_layout="HND", kv_form="split", page_size=16, head_dim=64),
+    dict(kv_layout="NHD", kv_form="split", page_size=16, head_dim=64),
+    dict(kv_layout="HND", kv_form="combined", page_size=32, head_dim=128),
+    dict(kv_layout="NHD", kv_form="combined", page_size=1, head_dim=128),
+    dict(kv_layout="NHD", kv_form="combined1", page_size=8, head_dim=64),
+    dict(kv_layout="HND", kv_form="split", page_size=64, head_dim=128, kv_dtype="fp8_e4m3fn"),
+    dict(kv_layout="NHD", kv_form="split", page_size=128, head_dim=64, kv_dtype="fp8_e4m3fn"),
+]
+
+
+@pytest.mark.parametrize("var", GATHER_CASES, ids=lambda v: "-".join(str(x) for x in v.values()))
+def test_gather_bitwise(var):
+    import paged_kv_prefill_varlen_amd as ppa
+    case = make_custom_case(batch=3, num_qo_heads=4, num_kv_heads=2, q_lens=(40, 0, 130),
+                            prefix_lens=(100, 7, 3), seed=11, **var)
+    _say("gather", var)
+    d = to_device(case)
+    out = torch.empty_like(d["query"])
+    p = ppa.make_params(d["query"], d["kv_cache"], None, d["block_tables"], d["seq_lens"],
+                        d["max_q_len"], d["max_kv_len"], 1.0, 1.0, d["batch_size"],
+                        d["cum_seq_lens_q"], d["cum_seq_lens_kv"], -1, out, d["kv_layout"], None)
+    rows = sum(case["kv_lens"])
+    for kv_idx, logical in ((0, case["logical_k"]), (1, case["logical_v"])):
+        dst = torch.zeros((rows, case["num_kv_heads"], case["head_dim"]), dtype=case["cache_dtype"],
+                          device="cuda")
+        ppa.ppa_gather_paged_kv(p, kv_idx, dst)
+        torch.cuda.synchronize()
+        want = torch.cat(logical, dim=0)
+        g = dst.cpu().view(torch.uint8).numpy()
+        w = want.contiguous().view(torch.uint8).numpy()
+        assert np.array_equal(g, w), f"gather mismatch plane {kv_idx}"
+
+
+# --------------------------------------------------------------------------
+# small and edge-case workloads, every row
+# --------------------------------------------------------------------------
+
+EDGE = {
+    "mha_d128_p16": dict(num_qo_heads=2, num_kv_heads=2, head_dim=128, page_size=16,
+                         q_lens=(300,), prefix_lens=(100,)),
+    "g2_d64_nhd_combined": dict(num_qo_heads=4, num_kv_heads=2, head_dim=64, page_size=8,
+                                kv_layout="NHD", kv_form="combined",
+                                q_lens=(130, 1, 65), prefix_lens=(0, 70, 3)),
+    "g3_combined1": dict(num_qo_heads=6, num_kv_heads=2, head_dim=128, page_size=32,
+                         kv_form="combined1", q_lens=(200,), prefix_lens=(50,)),
+    "g8_window0_sinks": dict(num_qo_heads=16, num_kv_heads=2, head_dim=64, page_size=16,
+                             kv_layout="NHD", window_left=0, sinks=True,
+                             q_lens=(100, 37), prefix_lens=(0, 20)),
+    "g16_window63_sinks": dict(num_qo_heads=16, num_kv_heads=1, head_dim=128, page_size=64,
+                               window_left=63, sinks=True, q_lens=(90,), prefix_lens=(200,)),
+    "g32_two_head_groups": dict(num_qo_heads=64, num_kv_heads=2, head_dim=64, page_size=4,
+                                q_lens=(20, 5), prefix_lens=(10, 0)),
+    "empty_requests": dict(num_qo_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
+                           q_lens=(0, 50, 0, 3), prefix_lens=(30, 0, 0, 0), extra_tokens=5),
+    "page_size_1": dict(num_qo_heads=8, num_kv_heads=2, head_dim=64, page_size=1,
+                        q_lens=(70,), prefix_lens=(10,)),
+    "page_size_128": dict(num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=128,
+                          q_lens=(129,), prefix_lens=(300,)),
+    "single_token": dict(num_qo_heads=4, num_kv_heads=4, head_dim=128, page_size=16,
+                         q_lens=(1,), prefix_lens=(0,)),
+    "bounds_loose": dict(num_qo_heads=8, num_kv_heads=2, head_dim=64, page_size=16,
+                         q_lens=(33, 64), prefix_lens=(5, 64), max_q_len=500, max_kv_len=900),
+    "long_prefix": dict(num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=32,
+                        q_lens=(1000,), prefix_lens=(3000,)),
+    "window_many_tiles": dict(num_qo_heads=8, num_kv_heads=1, head_dim=64, page_size=16,
+                              window_left=200, sinks=True, q_lens=(700,), prefix_lens=(500,)),
+    "nan_poison": dict(num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                       poison="nan", q_lens=(77, 150), prefix_lens=(19, 0)),
+    "neg_bmm1": dict(num_qo_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
+                     bmm1_scale=-0.2, bmm2_scale=0.5, q_lens=(90,), prefix_lens=(40,)),
+    "zero_bmm1": dict(num_qo_heads=4, num_kv_heads=2, head_dim=128, page_size=16,
+                      bmm1_scale=0.0, q_lens=(90,), prefix_lens=(40,), window_left=20),
+    "fp8_d128": dict(num_qo_heads=16, num_kv_heads=2, head_dim=128, page_size=64,
+                     kv_dtype="fp8_e4m3fn", q_lens=(150,), prefix_lens=(600,)),
+    "fp8_d64_nhd_window_sinks": dict(num_qo_heads=8, num_kv_heads=2, head_dim=64, page_size=16,
+                                     kv_layout="NHD", kv_dtype="fp8_e4m3fn", window_left=31,
+                                     sinks=True, q_lens=(77, 33), prefix_lens=(10, 200)),
+    "fp8_nan_poison": dict(num_qo_heads=8, num_kv_heads=1, head_dim=128, page_size=16,
+                           kv_dtype="fp8_e4m3fn", poison="nan", q_lens=(65,), prefix_lens=(63,)),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_case_parity(name):
+    case = make_custom_case(name=name, batch=len(EDGE[name]["q_lens"]), seed=zlib.crc32(name.encode()) % 10000,
+                            **EDGE[name])
+    _say("edge", name, case["q_lens"], case["kv_lens"])
+    want, written = run_oracle(case)
+    out = run_gpu(to_device(case))
+    torch.cuda.synchronize()
+    assert guard_rows_untouched(out, written), "rows outside the requests were written"
+    mx, mean = assert_close(out, want, written, fp8=case["kv_dtype"] != "bf16", what=name)
+    _say(f"  max {mx:.2e} mean {mean:.2e}")
+
+
+def test_tiny_config_full():
+    case = make_case("tiny")
+    want, written = run_oracle(case)
+    out = run_gpu(to_device(case))
+    torch.cuda.synchronize()
+    assert guard_rows_untouched(out, written)
+    assert_close(out, want, written, what="tiny")
+
+
+def test_chunked_config_full():
+    case = make_case("chunked")
+    _say("chunked", case["q_lens"], case["kv_lens"])
+    want, written = run_oracle(case)
+    out = run_gpu(to_device(case))
+    torch.cuda.synchronize()
+    assert guard_rows_untouched(out, written)
+    mx, mean = assert_close(out, want, written, what="chunked")
+    _say(f"  max {mx:.2e} mean {mean:.2e}")
+
+
+def _sample_rows(case, n_random=96, seed=0):
+    rng = np.random.default_rng(seed)
+    cu = case["cum_seq_lens_q"].numpy()
+    Hq = case["num_qo_heads"]
+    rows = []
+    for b in range(case["batch_size"]):
+        q0, q1 = int(cu[b]), int(cu[b + 1])
+        if q1 == q0:
+            continue
+        for t in {q0, q1 - 1, q0 + (q1 - q0) // 2, min(q1 - 1, q0 + 63), min(q1 - 1, q0 + 64)}:
+            rows.append((t, int(rng.integers(Hq))))
+    tot = int(cu[-1])
+    for _ in range(n_random):
+        rows.append((int(rng.integers(tot)), int(rng.integers(Hq))))
+    return rows
+
+
+@pytest.mark.parametrize("name", ["llama3_8b", "swa_sinks", "fp8_long_prefix"])
+def test_full_size_config_sampled(name):
+    case = make_case(name)
+    _say("full", name, "tokens", sum(case["q_lens"]))
+    d = to_device(case)
+    out = run_gpu(d)
+    torch.cuda.synchronize()
+    written = np.zeros(case["num_tokens"], dtype=bool)
+    written[:int(case["cum_seq_lens_q"][-1])] = True
+    assert guard_rows_untouched(out, written)
+    o = out.float()
+    assert not torch.isnan(o[:int(written.sum())]).any(), "NaN in output"
+    rows = _sample_rows(case)
+    want = run_oracle_rows(case, rows)
+    got = decode_tensor(out.cpu())
+    g = np.stack([got[t, h] for t, h in rows])
+    err = np.abs(g - want)
+    tol = 6e-2 if case["kv_dtype"] != "bf16" else 2e-2
+    _say(f"  sampled max {err.max():.2e} mean {err.mean():.2e}")
+    assert err.max() <= tol
+    if case["kv_dtype"] == "bf16":
+        assert err.mean() <= 2e-3
+
+
+# --------------------------------------------------------------------------
+# invariances: bit-identical outputs
+# --------------------------------------------------------------------------
+
+def _base_case():
+    return make_custom_case(name="inv", batch=3, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                            page_size=16, q_lens=(100, 7, 260), prefix_lens=(30, 200, 0),
+                            sinks=True, window_left=150, seed=77)
+
+
+def test_relayout_bitwise():
+    case = _base_case()
+    base = run_gpu(to_device(case)).cpu()
+    for lay, form, P, seed in (("NHD", "split", 16, 1), ("HND", "combined", 32, 2),
+                               ("NHD", "combined", 4, 3), ("HND", "split", 64, 4)):
+        other = relayout(case, kv_layout=lay, kv_form=form, page_size=P, permute_seed=seed)
+        got = run_gpu(to_device(other)).cpu()
+        assert torch.equal(base.view(torch.int16), got.view(torch.int16)), (lay, form, P)
+
+
+def test_poison_bitwise_and_determinism():
+    a = _base_case()
+    b = make_custom_case(**{**a["spec"].__dict__, "poison": "nan"})
+    ra = run_gpu(to_device(a)).cpu()
+    ra2 = run_gpu(to_device(a)).cpu()
+    rb = run_gpu(to_device(b)).cpu()
+    assert torch.equal(ra.view(torch.int16), ra2.view(torch.int16)), "two launches differ"
+    assert torch.equal(ra.view(torch.int16), rb.view(torch.int16)), "poisoned pages leaked"
+
+
+def test_full_window_and_neg_inf_sink_bitwise():
+    case = _base_case()
+    d = to_device(case)
+    d_nowin = dict(d, window_left=-1)
+    d_bigwin = dict(d, window_left=max(case["kv_lens"]) + 5)
+    a = run_gpu(d_nowin).cpu()
+    b = run_gpu(d_bigwin).cpu()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    d_nosink = dict(d, sinks=None)
+    d_infsink = dict(d, sinks=torch.full_like(d["sinks"], -math.inf))
+    c = run_gpu(d_nosink).cpu()
+    e = run_gpu(d_infsink).cpu()
+    assert torch.equal(c.view(torch.int16), e.view(torch.int16))
+
+
+def test_device_tensor_scales():
+    case = _base_case()
+    d = to_device(case)
+    a = run_gpu(d).cpu()
+    b1 = torch.tensor([d["bmm1_scale"]], dtype=torch.float32, device="cuda")
+    b2 = torch.tensor([d["bmm2_scale"]], dtype=torch.float32, device="cuda")
+    b = run_gpu(d, bmm1=b1, bmm2=b2).cpu()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_rejects_bad_metadata_without_launch():
+    import paged_kv_prefill_varlen_amd as ppa
+    case = _base_case()
+    d = to_device(case)
+    bad = d["seq_lens"].clone()
+    bad[1] = 3  # q_len 7 > kv_len 3
+    with pytest.raises(ppa.PpaError):
+        run_gpu(dict(d, seq_lens=bad), validate=True)

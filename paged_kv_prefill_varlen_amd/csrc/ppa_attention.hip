@@ -39,6 +39,7 @@
 //   cut by the band are masked.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "ppa.h"
 #include "ppa_internal.h"
@@ -54,10 +55,8 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRows = 256;      // rows per workgroup
 constexpr int kBK = 64;         // keys per tile
+constexpr int kLoadThreads = 256;   // threads that stage one operand (K or V) of a tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 constexpr float kNegInf = -__builtin_inff();
@@ -114,128 +113,145 @@ __device__ __forceinline__ int swap_bits23(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
+// Tile geometry.  K and V of a 64-key tile are each staged by 256 threads:
+// K rows with 16-byte loads in natural [key][dim] layout; V as 4 consecutive
+// keys x V_DPT dims per thread, transposed in registers to [dim][key].  Both
+// need RAW dwords of prefetch per thread.
 template <int D, bool FP8>
 struct Tile {
-  static constexpr int EB = FP8 ? 1 : 2;              // bytes per cache element
-  // K: 16-byte loads, natural layout
-  static constexpr int K_CHUNK = 16 / EB;              // elements per load
+  static constexpr int EB = FP8 ? 1 : 2;               // bytes per cache element
+  static constexpr int K_CHUNK = 16 / EB;              // elements per 16-byte load
   static constexpr int K_TPR = D / K_CHUNK;            // threads per key row
-  static constexpr int K_RPP = kThreads / K_TPR;       // rows per pass
+  static constexpr int K_RPP = kLoadThreads / K_TPR;   // rows per pass
   static constexpr int K_PASSES = kBK / K_RPP;
-  // V: thread = 4 consecutive keys x V_DPT head-dim values, transposed in regs
-  static constexpr int V_DPT = D / 16;
-  static constexpr int V_LOAD_BYTES = V_DPT * EB;      // per key
-  static constexpr int V_DW = V_LOAD_BYTES / 4;        // dwords per key (raw)
-  // LDS row strides in bf16 elements (padded to keep the MFMA operand reads
-  // and the transposed writes free of bank conflicts)
+  static constexpr int V_DPT = D / 16;                 // head-dim values per thread
+  static constexpr int V_DW = V_DPT * EB / 4;          // raw dwords per key
+  static constexpr int RAW = D * EB / 16;              // raw dwords per thread and operand
+  static constexpr int IDS = K_PASSES > 4 ? K_PASSES : 4;
+  // LDS row strides in bf16 elements, padded so the MFMA operand reads and the
+  // transposed V writes are free of bank conflicts
   static constexpr int KS = D + 8;
   static constexpr int VS = (D == 128) ? kBK + 8 : kBK + 16;
   static constexpr int K_ELEMS = kBK * KS;
   static constexpr int V_ELEMS = D * VS;
   static_assert(K_PASSES * K_RPP == kBK, "K tile mapping");
+  static_assert(K_PASSES * 4 == RAW && 4 * V_DW == RAW, "K and V prefetch sizes");
   static_assert(V_DW >= 1, "V load");
 };
 
+// ---- K staging ---------------------------------------------------------------
 template <int D, bool FP8>
-struct Loader {
+__device__ __forceinline__ void k_ids(int* ids, const PageTable& pt, int k0, int lt) {
   using T = Tile<D, FP8>;
-  u32x4 kreg[T::K_PASSES];
-  uint32_t vreg[4][T::V_DW];
-  int kpid[T::K_PASSES];
-  int vpid[4];
-
-  __device__ __forceinline__ void fetch_ids(const PageTable& pt, int k0, int tid) {
-    const int krow0 = tid / T::K_TPR;
-    for (int p = 0; p < T::K_PASSES; ++p) kpid[p] = page_id(pt, k0 + krow0 + p * T::K_RPP);
-    const int kg = tid & 15;
-    for (int r = 0; r < 4; ++r) vpid[r] = page_id(pt, k0 + 4 * kg + r);
-  }
-
-  __device__ __forceinline__ void fetch_rows(const AttnArgs& a, int hk, int k0, int kv_len,
-                                             int page_mask, int tid) {
-    const int krow0 = tid / T::K_TPR;
-    const int kchunk = tid % T::K_TPR;
-    for (int p = 0; p < T::K_PASSES; ++p) {
-      const int key = k0 + krow0 + p * T::K_RPP;
-      if (key < kv_len) {
-        const uint8_t* src = token_row<T::EB>(a.k, kpid[p], page_mask, key, hk, kchunk * T::K_CHUNK);
-        kreg[p] = *reinterpret_cast<const u32x4*>(src);
-      } else {
-        kreg[p] = u32x4{0, 0, 0, 0};
-      }
-    }
-    const int kg = tid & 15;
-    const int dg = tid >> 4;
-    for (int r = 0; r < 4; ++r) {
-      const int key = k0 + 4 * kg + r;
-      if (key < kv_len) {
-        const uint8_t* src = token_row<T::EB>(a.v, vpid[r], page_mask, key, hk, dg * T::V_DPT);
-        if constexpr (T::V_DW == 4) {
-          u32x4 x = *reinterpret_cast<const u32x4*>(src);
-          for (int i = 0; i < 4; ++i) vreg[r][i] = x[i];
-        } else if constexpr (T::V_DW == 2) {
-          u32x2 x = *reinterpret_cast<const u32x2*>(src);
-          vreg[r][0] = x[0];
-          vreg[r][1] = x[1];
-        } else {
-          vreg[r][0] = *reinterpret_cast<const uint32_t*>(src);
-        }
-      } else {
-        for (int i = 0; i < T::V_DW; ++i) vreg[r][i] = 0;
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(__bf16* klds, __bf16* vlds, int tid) const {
-    const int krow0 = tid / T::K_TPR;
-    const int kchunk = tid % T::K_TPR;
-    for (int p = 0; p < T::K_PASSES; ++p) {
-      __bf16* dst = klds + (krow0 + p * T::K_RPP) * T::KS + kchunk * T::K_CHUNK;
-      if constexpr (!FP8) {
-        *reinterpret_cast<u32x4*>(dst) = kreg[p];
-      } else {
-        u32x2 a0 = fp8x4_to_bf16x4(kreg[p][0]);
-        u32x2 a1 = fp8x4_to_bf16x4(kreg[p][1]);
-        u32x2 a2 = fp8x4_to_bf16x4(kreg[p][2]);
-        u32x2 a3 = fp8x4_to_bf16x4(kreg[p][3]);
-        reinterpret_cast<u32x4*>(dst)[0] = u32x4{a0[0], a0[1], a1[0], a1[1]};
-        reinterpret_cast<u32x4*>(dst)[1] = u32x4{a2[0], a2[1], a3[0], a3[1]};
-      }
-    }
-    // V: widen to bf16 pairs, then 4 keys x V_DPT values -> V_DPT rows of 4 keys
-    constexpr int PAIRS = T::V_DPT / 2;
-    uint32_t w[4][PAIRS];
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (!FP8) {
-        for (int i = 0; i < PAIRS; ++i) w[r][i] = vreg[r][i];
-      } else {
-        for (int i = 0; i < T::V_DW; ++i) {
-          u32x2 x = fp8x4_to_bf16x4(vreg[r][i]);
-          w[r][2 * i] = x[0];
-          w[r][2 * i + 1] = x[1];
-        }
-      }
-    }
-    const int kg = tid & 15;
-    const int dg = tid >> 4;
-    for (int i = 0; i < PAIRS; ++i) {
-      // even head-dim value: low halves; odd: high halves
-      const uint32_t lo01 = __builtin_amdgcn_perm(w[1][i], w[0][i], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(w[3][i], w[2][i], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(w[1][i], w[0][i], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(w[3][i], w[2][i], 0x07060302u);
-      const int d = dg * T::V_DPT + 2 * i;
-      *reinterpret_cast<u32x2*>(vlds + d * T::VS + 4 * kg) = u32x2{lo01, lo23};
-      *reinterpret_cast<u32x2*>(vlds + (d + 1) * T::VS + 4 * kg) = u32x2{hi01, hi23};
-    }
-  }
-};
+  const int krow0 = lt / T::K_TPR;
+  for (int p = 0; p < T::K_PASSES; ++p) ids[p] = page_id(pt, k0 + krow0 + p * T::K_RPP);
+}
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(kThreads) void paged_prefill_kernel(AttnArgs a) {
+__device__ __forceinline__ void k_fetch(uint32_t* raw, const int* ids, const PagedPlane& pl, int hk,
+                                        int k0, int kv_len, int page_mask, int lt) {
+  using T = Tile<D, FP8>;
+  const int krow0 = lt / T::K_TPR;
+  const int kchunk = lt % T::K_TPR;
+  for (int p = 0; p < T::K_PASSES; ++p) {
+    const int key = k0 + krow0 + p * T::K_RPP;
+    u32x4 x = u32x4{0, 0, 0, 0};
+    if (key < kv_len)
+      x = *reinterpret_cast<const u32x4*>(token_row<T::EB>(pl, ids[p], page_mask, key, hk, kchunk * T::K_CHUNK));
+    for (int i = 0; i < 4; ++i) raw[4 * p + i] = x[i];
+  }
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void k_store(const uint32_t* raw, __bf16* klds, int lt) {
+  using T = Tile<D, FP8>;
+  const int krow0 = lt / T::K_TPR;
+  const int kchunk = lt % T::K_TPR;
+  for (int p = 0; p < T::K_PASSES; ++p) {
+    __bf16* dst = klds + (krow0 + p * T::K_RPP) * T::KS + kchunk * T::K_CHUNK;
+    if constexpr (!FP8) {
+      *reinterpret_cast<u32x4*>(dst) = u32x4{raw[4 * p], raw[4 * p + 1], raw[4 * p + 2], raw[4 * p + 3]};
+    } else {
+      const u32x2 a0 = fp8x4_to_bf16x4(raw[4 * p]);
+      const u32x2 a1 = fp8x4_to_bf16x4(raw[4 * p + 1]);
+      const u32x2 a2 = fp8x4_to_bf16x4(raw[4 * p + 2]);
+      const u32x2 a3 = fp8x4_to_bf16x4(raw[4 * p + 3]);
+      reinterpret_cast<u32x4*>(dst)[0] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+      reinterpret_cast<u32x4*>(dst)[1] = u32x4{a2[0], a2[1], a3[0], a3[1]};
+    }
+  }
+}
+
+// ---- V staging (transposed) ---------------------------------------------------
+template <int D, bool FP8>
+__device__ __forceinline__ void v_ids(int* ids, const PageTable& pt, int k0, int lt) {
+  const int kg = lt & 15;
+  for (int r = 0; r < 4; ++r) ids[r] = page_id(pt, k0 + 4 * kg + r);
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void v_fetch(uint32_t* raw, const int* ids, const PagedPlane& pl, int hk,
+                                        int k0, int kv_len, int page_mask, int lt) {
+  using T = Tile<D, FP8>;
+  const int kg = lt & 15;
+  const int dg = lt >> 4;
+  for (int r = 0; r < 4; ++r) {
+    const int key = k0 + 4 * kg + r;
+    const uint8_t* src = token_row<T::EB>(pl, ids[r], page_mask, key, hk, dg * T::V_DPT);
+    const bool ok = key < kv_len;
+    if constexpr (T::V_DW == 4) {
+      u32x4 x = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
+      for (int i = 0; i < 4; ++i) raw[4 * r + i] = x[i];
+    } else if constexpr (T::V_DW == 2) {
+      u32x2 x = ok ? *reinterpret_cast<const u32x2*>(src) : u32x2{0, 0};
+      raw[2 * r] = x[0];
+      raw[2 * r + 1] = x[1];
+    } else {
+      raw[r] = ok ? *reinterpret_cast<const uint32_t*>(src) : 0u;
+    }
+  }
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void v_store(const uint32_t* raw, __bf16* vlds, int lt) {
+  using T = Tile<D, FP8>;
+  constexpr int PAIRS = T::V_DPT / 2;   // bf16 pairs per key
+  uint32_t w[4][PAIRS];
+  for (int r = 0; r < 4; ++r) {
+    if constexpr (!FP8) {
+      for (int i = 0; i < PAIRS; ++i) w[r][i] = raw[T::V_DW * r + i];
+    } else {
+      for (int i = 0; i < T::V_DW; ++i) {
+        const u32x2 x = fp8x4_to_bf16x4(raw[T::V_DW * r + i]);
+        w[r][2 * i] = x[0];
+        w[r][2 * i + 1] = x[1];
+      }
+    }
+  }
+  const int kg = lt & 15;
+  const int dg = lt >> 4;
+  for (int i = 0; i < PAIRS; ++i) {
+    // head-dim 2i: low halves of the 4 keys; head-dim 2i+1: high halves
+    const uint32_t lo01 = (w[0][i] & 0xffffu) | (w[1][i] << 16);
+    const uint32_t lo23 = (w[2][i] & 0xffffu) | (w[3][i] << 16);
+    const uint32_t hi01 = (w[0][i] >> 16) | (w[1][i] & 0xffff0000u);
+    const uint32_t hi23 = (w[2][i] >> 16) | (w[3][i] & 0xffff0000u);
+    const int d = dg * T::V_DPT + 2 * i;
+    *reinterpret_cast<u32x2*>(vlds + d * T::VS + 4 * kg) = u32x2{lo01, lo23};
+    *reinterpret_cast<u32x2*>(vlds + (d + 1) * T::VS + 4 * kg) = u32x2{hi01, hi23};
+  }
+}
+
+// NT: 32-row MFMA column tiles per wave; NW: waves per workgroup.  Every
+// configuration has 256 rows per workgroup.  With NW = 8, waves 0-3 stage K
+// and waves 4-7 stage V; with NW = 4, every thread stages both.
+template <int D, bool FP8, int NT, int NW>
+__global__ __launch_bounds__(64 * NW) void paged_prefill_kernel(AttnArgs a) {
   using T = Tile<D, FP8>;
   constexpr int KSTEPS = D / 16;   // MFMA K-steps over head_dim
   constexpr int MD = D / 32;       // 32-wide head_dim tiles of O^T
+  constexpr bool SPLIT_STAGING = NW == 8;
+  static_assert(NT * NW * 32 == 256, "256 rows per workgroup");
   __shared__ __attribute__((aligned(16))) __bf16 klds[2][T::K_ELEMS];
   __shared__ __attribute__((aligned(16))) __bf16 vlds[2][T::V_ELEMS];
 
@@ -275,17 +291,18 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(AttnArgs a) {
   c = negate_q ? -c : c;
 
   // ---- the wave's rows ----------------------------------------------------
-  int tok[2], hd[2], pos[2];
-  bool rvalid[2];
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = wave * 64 + nt * 32 + col;
+  constexpr int WROWS = 32 * NT;
+  int tok[NT], hd[NT], pos[NT];
+  bool rvalid[NT];
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = wave * WROWS + nt * 32 + col;
     tok[nt] = r / a.gw;
     hd[nt] = r % a.gw;
     rvalid[nt] = tok[nt] < ntok && hd[nt] < nheads;
     pos[nt] = prefix + t0 + tok[nt];
   }
-  const int wtok_first = (wave * 64) / a.gw;
-  int wtok_last = (wave * 64 + 63) / a.gw;
+  const int wtok_first = (wave * WROWS) / a.gw;
+  int wtok_last = (wave * WROWS + WROWS - 1) / a.gw;
   wtok_last = wtok_last < ntok - 1 ? wtok_last : ntok - 1;
   const bool wave_active = wtok_first < ntok;
   const int wpos_first = prefix + t0 + wtok_first;
@@ -294,8 +311,8 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(AttnArgs a) {
   const int wkey_lo = W >= 0 ? (wpos_first - W > 0 ? wpos_first - W : 0) : 0;
 
   // ---- Q into registers (B operand of S^T = K Q^T) ------------------------
-  bf16x8 qf[2][KSTEPS];
-  for (int nt = 0; nt < 2; ++nt) {
+  bf16x8 qf[NT][KSTEPS];
+  for (int nt = 0; nt < NT; ++nt) {
     const uint16_t* qrow = a.q + static_cast<int64_t>(q0 + t0 + tok[nt]) * a.q_tok +
                            static_cast<int64_t>(h0 + hd[nt]) * a.q_head;
     for (int s = 0; s < KSTEPS; ++s) {
@@ -306,11 +323,14 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(AttnArgs a) {
     }
   }
 
-  f32x16 oacc[2][MD];
-  for (int nt = 0; nt < 2; ++nt)
+  f32x16 oacc[NT][MD];
+  for (int nt = 0; nt < NT; ++nt)
     for (int md = 0; md < MD; ++md) oacc[nt][md] = f32x16{};
-  float m_run[2] = {kNegInf, kNegInf};
-  float l_part[2] = {0.f, 0.f};
+  float m_run[NT], l_part[NT];
+  for (int nt = 0; nt < NT; ++nt) {
+    m_run[nt] = kNegInf;
+    l_part[nt] = 0.f;
+  }
 
   // ---- K/V tile range of the workgroup -------------------------------------
   const int pos_first = prefix + t0;
@@ -327,13 +347,33 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(AttnArgs a) {
   pt.page_shift = a.page_shift;
   const int page_mask = (1 << a.page_shift) - 1;
 
-  Loader<D, FP8> ld;
-  Loader<D, FP8> ld_next_ids;   // page ids one tile further ahead
+  // staging roles: which operand(s) this thread stages, as loader index lt
+  const int lt = tid & (kLoadThreads - 1);
+  const bool stage_k = !SPLIT_STAGING || wave < 4;
+  const bool stage_v = !SPLIT_STAGING || wave >= 4;
+  constexpr int NRAW = SPLIT_STAGING ? 1 : 2;
+  uint32_t raw[NRAW][T::RAW];
+  int ids[NRAW][T::IDS];
+  int ids_next[NRAW][T::IDS];
+
+  auto fetch_ids = [&](int (*dst)[T::IDS], int k0) {
+    if (stage_k) k_ids<D, FP8>(dst[0], pt, k0, lt);
+    if (stage_v) v_ids<D, FP8>(dst[NRAW - 1], pt, k0, lt);
+  };
+  auto fetch_rows = [&](int k0) {
+    if (stage_k) k_fetch<D, FP8>(raw[0], ids[0], a.k, hk, k0, kv_len, page_mask, lt);
+    if (stage_v) v_fetch<D, FP8>(raw[NRAW - 1], ids[NRAW - 1], a.v, hk, k0, kv_len, page_mask, lt);
+  };
+  auto store_rows = [&](int buf) {
+    if (stage_k) k_store<D, FP8>(raw[0], klds[buf], lt);
+    if (stage_v) v_store<D, FP8>(raw[NRAW - 1], vlds[buf], lt);
+  };
+
   if (tile_lo <= tile_hi) {
-    ld.fetch_ids(pt, tile_lo * kBK, tid);
-    ld.fetch_rows(a, hk, tile_lo * kBK, kv_len, page_mask, tid);
-    if (tile_lo + 1 <= tile_hi) ld_next_ids.fetch_ids(pt, (tile_lo + 1) * kBK, tid);
-    ld.store(klds[0], vlds[0], tid);
+    fetch_ids(ids, tile_lo * kBK);
+    fetch_rows(tile_lo * kBK);
+    if (tile_lo + 1 <= tile_hi) fetch_ids(ids_next, (tile_lo + 1) * kBK);
+    store_rows(0);
   }
   __syncthreads();
 
@@ -344,32 +384,32 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(AttnArgs a) {
     const int k0 = tile * kBK;
     const bool more = tile + 1 <= tile_hi;
     if (more) {
-      for (int p = 0; p < Tile<D, FP8>::K_PASSES; ++p) ld.kpid[p] = ld_next_ids.kpid[p];
-      for (int r = 0; r < 4; ++r) ld.vpid[r] = ld_next_ids.vpid[r];
-      ld.fetch_rows(a, hk, k0 + kBK, kv_len, page_mask, tid);
-      if (tile + 2 <= tile_hi) ld_next_ids.fetch_ids(pt, k0 + 2 * kBK, tid);
+      for (int r = 0; r < NRAW; ++r)
+        for (int i = 0; i < T::IDS; ++i) ids[r][i] = ids_next[r][i];
+      fetch_rows(k0 + kBK);
+      if (tile + 2 <= tile_hi) fetch_ids(ids_next, k0 + 2 * kBK);
     }
 
     const bool wave_tile = wave_active && k0 <= wkey_hi && k0 + kBK - 1 >= wkey_lo;
     if (wave_tile) {
       // S^T = K Q^T over head_dim
-      f32x16 sacc[2][2];
+      f32x16 sacc[2][NT];
       for (int mt = 0; mt < 2; ++mt)
-        for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = f32x16{};
+        for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = f32x16{};
       const __bf16* kb = klds[buf];
       for (int s = 0; s < KSTEPS; ++s) {
         for (int mt = 0; mt < 2; ++mt) {
           const bf16x8 kf =
               *reinterpret_cast<const bf16x8*>(kb + (mt * 32 + krow_lane) * T::KS + s * 16 + half * 8);
-          for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = mfma32(kf, qf[nt][s], sacc[mt][nt]);
+          for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = mfma32(kf, qf[nt][s], sacc[mt][nt]);
         }
       }
 
       // masking: only tiles cut by the causal / window / length bounds
       const bool need_mask = (k0 + kBK - 1 > wpos_first) || (W >= 0 && k0 < wpos_last - W) ||
                              (k0 + kBK > kv_len);
-      float mx[2];
-      for (int nt = 0; nt < 2; ++nt) {
+      float mx[NT];
+      for (int nt = 0; nt < NT; ++nt) {
         float m = kNegInf;
         if (need_mask) {
           const int hi = pos[nt] < kv_len - 1 ? pos[nt] : kv_len - 1;
@@ -389,14 +429,16 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(AttnArgs a) {
       }
 
       // lazy rescale of the running maximum (log2 domain)
-      bool need[2];
-      float mtile[2];
-      for (int nt = 0; nt < 2; ++nt) {
+      bool need[NT];
+      float mtile[NT];
+      bool any = false;
+      for (int nt = 0; nt < NT; ++nt) {
         mtile[nt] = mx[nt] == kNegInf ? kNegInf : mx[nt] * c;
         need[nt] = mtile[nt] > m_run[nt] + kRescaleThreshold;
+        any = any || need[nt];
       }
-      if (__ballot(need[0] || need[1]) != 0ull) {
-        for (int nt = 0; nt < 2; ++nt) {
+      if (__ballot(any) != 0ull) {
+        for (int nt = 0; nt < NT; ++nt) {
           const float m_new = need[nt] ? mtile[nt] : m_run[nt];
           const float alpha = need[nt] ? __builtin_amdgcn_exp2f(m_run[nt] - m_new) : 1.f;
           m_run[nt] = m_new;
@@ -406,8 +448,8 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(AttnArgs a) {
       }
 
       // P = exp2(c s - m), row partial sums, bf16 B operands of O^T += V^T P^T
-      bf16x8 pb[2][4];
-      for (int nt = 0; nt < 2; ++nt) {
+      bf16x8 pb[NT][4];
+      for (int nt = 0; nt < NT; ++nt) {
         const float mb = m_run[nt] == kNegInf ? 0.f : m_run[nt];
         float sum = 0.f;
         for (int mt = 0; mt < 2; ++mt) {
@@ -431,18 +473,18 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(AttnArgs a) {
         for (int md = 0; md < MD; ++md) {
           const bf16x8 vf =
               *reinterpret_cast<const bf16x8*>(vb + (md * 32 + col) * T::VS + ks * 16 + half * 8);
-          for (int nt = 0; nt < 2; ++nt) oacc[nt][md] = mfma32(vf, pb[nt][ks], oacc[nt][md]);
+          for (int nt = 0; nt < NT; ++nt) oacc[nt][md] = mfma32(vf, pb[nt][ks], oacc[nt][md]);
         }
       }
     }
 
-    if (more) ld.store(klds[buf ^ 1], vlds[buf ^ 1], tid);
+    if (more) store_rows(buf ^ 1);
     __syncthreads();
   }
 
   // ---- epilogue -------------------------------------------------------------
   if (!wave_active) return;
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     float l = l_part[nt] + __shfl_xor(l_part[nt], 32);
     if (!rvalid[nt]) continue;
     const int h = h0 + hd[nt];
@@ -514,10 +556,24 @@ int log2_exact(int x) {
   return s;
 }
 
+// Kernel shape: 8 waves x 32 rows (two waves per SIMD) unless PPA_WAVES=4
+// asks for 4 waves x 64 rows (one wave per SIMD).
 template <int D, bool FP8>
-hipError_t launch(const AttnArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((paged_prefill_kernel<D, FP8>), dim3(grid), dim3(kThreads), 0, stream, a);
+hipError_t launch(const AttnArgs& a, int grid, hipStream_t stream, int waves) {
+  if (waves == 4) {
+    hipLaunchKernelGGL((paged_prefill_kernel<D, FP8, 2, 4>), dim3(grid), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((paged_prefill_kernel<D, FP8, 1, 8>), dim3(grid), dim3(512), 0, stream, a);
+  }
   return hipGetLastError();
+}
+
+int waves_setting() {
+  static int w = [] {
+    const char* s = getenv("PPA_WAVES");
+    return (s != nullptr && atoi(s) == 4) ? 4 : 8;
+  }();
+  return w;
 }
 
 }  // namespace
@@ -555,7 +611,7 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
   a.group = p->num_qo_heads / p->num_kv_heads;
   a.gw = a.group < 16 ? a.group : 16;
   a.n_hg = (a.group + a.gw - 1) / a.gw;
-  a.tq = kRows / a.gw;
+  a.tq = 256 / a.gw;
   a.n_qt = (p->max_q_len + a.tq - 1) / a.tq;
   a.window_left = p->window_left;
   a.bmm1 = p->bmm1_scale;
@@ -569,10 +625,12 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   const bool fp8 = p->kv_dtype == PPA_DTYPE_FP8_E4M3FN;
+  const int w = waves_setting();
+  const int g = static_cast<int>(grid);
   if (p->head_dim == 128)
-    e = fp8 ? launch<128, true>(a, static_cast<int>(grid), s) : launch<128, false>(a, static_cast<int>(grid), s);
+    e = fp8 ? launch<128, true>(a, g, s, w) : launch<128, false>(a, g, s, w);
   else
-    e = fp8 ? launch<64, true>(a, static_cast<int>(grid), s) : launch<64, false>(a, static_cast<int>(grid), s);
+    e = fp8 ? launch<64, true>(a, g, s, w) : launch<64, false>(a, g, s, w);
   return e == hipSuccess ? PPA_OK : PPA_ERR_HIP;
 }
 

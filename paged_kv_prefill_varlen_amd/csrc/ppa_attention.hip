@@ -55,11 +55,12 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-constexpr int kBK = 64;         // keys per tile
-constexpr int kLoadThreads = 256;   // threads that stage one operand (K or V) of a tile
+constexpr int kBK = 64;            // keys per tile
+constexpr int kLoadWaves = 4;      // waves of threads that stage one operand (K or V) of a tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kMinScale = 1.17549435e-38f;  // FLT_MIN
 
 struct AttnArgs {
   const uint16_t* q;
@@ -113,62 +114,126 @@ __device__ __forceinline__ int swap_bits23(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-// Tile geometry.  K and V of a 64-key tile are each staged by 256 threads:
-// K rows with 16-byte loads in natural [key][dim] layout; V as 4 consecutive
-// keys x V_DPT dims per thread, transposed in registers to [dim][key].  Both
-// need RAW dwords of prefetch per thread.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Tile geometry.  K and V of a 64-key tile are each staged by 4 loader waves;
+// loader wave lw owns the 16 consecutive keys [16 lw, 16 lw + 16) of the tile,
+// so with pages of >= 16 tokens its keys lie in one page and the page id and
+// base address are wave-uniform.  K goes to LDS in natural [key][dim] layout
+// with 16-byte loads; V goes as 4 consecutive keys x V_DPT dims per lane,
+// transposed in registers to [dim][key].  Both need RAW dwords per lane.
 template <int D, bool FP8>
 struct Tile {
-  static constexpr int EB = FP8 ? 1 : 2;               // bytes per cache element
-  static constexpr int K_CHUNK = 16 / EB;              // elements per 16-byte load
-  static constexpr int K_TPR = D / K_CHUNK;            // threads per key row
-  static constexpr int K_RPP = kLoadThreads / K_TPR;   // rows per pass
-  static constexpr int K_PASSES = kBK / K_RPP;
-  static constexpr int V_DPT = D / 16;                 // head-dim values per thread
-  static constexpr int V_DW = V_DPT * EB / 4;          // raw dwords per key
-  static constexpr int RAW = D * EB / 16;              // raw dwords per thread and operand
-  static constexpr int IDS = K_PASSES > 4 ? K_PASSES : 4;
-  // LDS row strides in bf16 elements, padded so the MFMA operand reads and the
-  // transposed V writes are free of bank conflicts
+  static constexpr int EB = FP8 ? 1 : 2;        // bytes per cache element
+  static constexpr int K_CHUNK = 16 / EB;       // elements per 16-byte load
+  static constexpr int K_TPR = D / K_CHUNK;     // lanes per key row
+  static constexpr int K_RPI = 64 / K_TPR;      // key rows per wave instruction
+  static constexpr int K_PASSES = 16 / K_RPI;   // instructions per loader wave
+  static constexpr int V_DPT = D / 16;          // head-dim values per lane
+  static constexpr int V_DW = V_DPT * EB / 4;   // raw dwords per key
+  static constexpr int RAW = D * EB / 16;       // raw dwords per lane and operand
+  // LDS row strides in bf16 elements.  K rows are padded by 16 bytes; V rows
+  // by 16 bytes plus an XOR swizzle of their 16-byte key chunks by
+  // (dim >> 4) & 7, which together keep the MFMA operand reads and the
+  // transposed V writes free of bank conflicts.
   static constexpr int KS = D + 8;
-  static constexpr int VS = (D == 128) ? kBK + 8 : kBK + 16;
+  static constexpr int VS = kBK + 8;
   static constexpr int K_ELEMS = kBK * KS;
   static constexpr int V_ELEMS = D * VS;
-  static_assert(K_PASSES * K_RPP == kBK, "K tile mapping");
+  static_assert(K_PASSES * K_RPI == 16, "K tile mapping");
   static_assert(K_PASSES * 4 == RAW && 4 * V_DW == RAW, "K and V prefetch sizes");
   static_assert(V_DW >= 1, "V load");
 };
 
-// ---- K staging ---------------------------------------------------------------
-template <int D, bool FP8>
-__device__ __forceinline__ void k_ids(int* ids, const PageTable& pt, int k0, int lt) {
-  using T = Tile<D, FP8>;
-  const int krow0 = lt / T::K_TPR;
-  for (int p = 0; p < T::K_PASSES; ++p) ids[p] = page_id(pt, k0 + krow0 + p * T::K_RPP);
+__device__ __forceinline__ int vt_offset(int d, int key, int vs) {
+  // element offset of V^T[d][key] in the swizzled layout
+  const int chunk = (key >> 3) ^ ((d >> 4) & 7);
+  return d * vs + chunk * 8 + (key & 7);
 }
 
-template <int D, bool FP8>
-__device__ __forceinline__ void k_fetch(uint32_t* raw, const int* ids, const PagedPlane& pl, int hk,
-                                        int k0, int kv_len, int page_mask, int lt) {
+// ---- staging: global -> registers ---------------------------------------------
+// UPAGE: the loader wave's 16 keys share one page (page_size >= 16 and the tile
+// is not the last one of the request).  Otherwise every lane resolves its own
+// keys, clamped to the sequence, and zero-fills keys past kv_len.
+template <int D, bool FP8, bool UPAGE>
+__device__ __forceinline__ void fetch_k(uint32_t* raw, const PagedPlane& pl, const PageTable& pt,
+                                        int hk, int kb, int kv_len, int page_mask, int lane,
+                                        bool tail) {
   using T = Tile<D, FP8>;
-  const int krow0 = lt / T::K_TPR;
-  const int kchunk = lt % T::K_TPR;
-  for (int p = 0; p < T::K_PASSES; ++p) {
-    const int key = k0 + krow0 + p * T::K_RPP;
-    u32x4 x = u32x4{0, 0, 0, 0};
-    if (key < kv_len)
-      x = *reinterpret_cast<const u32x4*>(token_row<T::EB>(pl, ids[p], page_mask, key, hk, kchunk * T::K_CHUNK));
-    for (int i = 0; i < 4; ++i) raw[4 * p + i] = x[i];
+  const int kchunk = lane % T::K_TPR;
+  const int r0 = lane / T::K_TPR;
+  if (UPAGE && !tail) {
+    const int id = uniform(page_id(pt, kb));
+    const uint8_t* base = pl.base + (static_cast<int64_t>(id) * pl.page_stride +
+                                     static_cast<int64_t>(hk) * pl.head_stride) * T::EB;
+    const int slot0 = kb & page_mask;
+    for (int p = 0; p < T::K_PASSES; ++p) {
+      const uint32_t off = static_cast<uint32_t>(
+          ((slot0 + p * T::K_RPI + r0) * static_cast<int>(pl.tok_stride) + kchunk * T::K_CHUNK) * T::EB);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(base + off);
+      for (int i = 0; i < 4; ++i) raw[4 * p + i] = x[i];
+    }
+  } else {
+    for (int p = 0; p < T::K_PASSES; ++p) {
+      const int key = kb + p * T::K_RPI + r0;
+      const bool ok = key < kv_len;
+      const int kc = ok ? key : kv_len - 1;
+      const int id = page_id(pt, kc);
+      u32x4 x = *reinterpret_cast<const u32x4*>(token_row<T::EB>(pl, id, page_mask, kc, hk, kchunk * T::K_CHUNK));
+      for (int i = 0; i < 4; ++i) raw[4 * p + i] = ok ? x[i] : 0u;
+    }
   }
 }
 
-template <int D, bool FP8>
-__device__ __forceinline__ void k_store(const uint32_t* raw, __bf16* klds, int lt) {
+template <int D, bool FP8, bool UPAGE>
+__device__ __forceinline__ void fetch_v(uint32_t* raw, const PagedPlane& pl, const PageTable& pt,
+                                        int hk, int kb, int kv_len, int page_mask, int lane,
+                                        bool tail) {
   using T = Tile<D, FP8>;
-  const int krow0 = lt / T::K_TPR;
-  const int kchunk = lt % T::K_TPR;
+  const int kgl = lane >> 4;   // 4 keys: kb + 4 kgl .. + 3
+  const int dg = lane & 15;
+  auto load = [&](const uint8_t* src, uint32_t* dst, bool ok) {
+    if constexpr (T::V_DW == 4) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+      for (int i = 0; i < 4; ++i) dst[i] = ok ? x[i] : 0u;
+    } else if constexpr (T::V_DW == 2) {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(src);
+      dst[0] = ok ? x[0] : 0u;
+      dst[1] = ok ? x[1] : 0u;
+    } else {
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(src);
+      dst[0] = ok ? x : 0u;
+    }
+  };
+  if (UPAGE && !tail) {
+    const int id = uniform(page_id(pt, kb));
+    const uint8_t* base = pl.base + (static_cast<int64_t>(id) * pl.page_stride +
+                                     static_cast<int64_t>(hk) * pl.head_stride) * T::EB;
+    const int slot0 = (kb & page_mask) + 4 * kgl;
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t off = static_cast<uint32_t>(
+          ((slot0 + r) * static_cast<int>(pl.tok_stride) + dg * T::V_DPT) * T::EB);
+      load(base + off, raw + T::V_DW * r, true);
+    }
+  } else {
+    for (int r = 0; r < 4; ++r) {
+      const int key = kb + 4 * kgl + r;
+      const bool ok = key < kv_len;
+      const int kc = ok ? key : kv_len - 1;
+      const int id = page_id(pt, kc);
+      load(token_row<T::EB>(pl, id, page_mask, kc, hk, dg * T::V_DPT), raw + T::V_DW * r, ok);
+    }
+  }
+}
+
+// ---- staging: registers -> LDS ---------------------------------------------------
+template <int D, bool FP8>
+__device__ __forceinline__ void store_k(const uint32_t* raw, __bf16* klds, int lw, int lane) {
+  using T = Tile<D, FP8>;
+  const int kchunk = lane % T::K_TPR;
+  const int r0 = lane / T::K_TPR;
   for (int p = 0; p < T::K_PASSES; ++p) {
-    __bf16* dst = klds + (krow0 + p * T::K_RPP) * T::KS + kchunk * T::K_CHUNK;
+    __bf16* dst = klds + (16 * lw + p * T::K_RPI + r0) * T::KS + kchunk * T::K_CHUNK;
     if constexpr (!FP8) {
       *reinterpret_cast<u32x4*>(dst) = u32x4{raw[4 * p], raw[4 * p + 1], raw[4 * p + 2], raw[4 * p + 3]};
     } else {
@@ -182,38 +247,8 @@ __device__ __forceinline__ void k_store(const uint32_t* raw, __bf16* klds, int l
   }
 }
 
-// ---- V staging (transposed) ---------------------------------------------------
 template <int D, bool FP8>
-__device__ __forceinline__ void v_ids(int* ids, const PageTable& pt, int k0, int lt) {
-  const int kg = lt & 15;
-  for (int r = 0; r < 4; ++r) ids[r] = page_id(pt, k0 + 4 * kg + r);
-}
-
-template <int D, bool FP8>
-__device__ __forceinline__ void v_fetch(uint32_t* raw, const int* ids, const PagedPlane& pl, int hk,
-                                        int k0, int kv_len, int page_mask, int lt) {
-  using T = Tile<D, FP8>;
-  const int kg = lt & 15;
-  const int dg = lt >> 4;
-  for (int r = 0; r < 4; ++r) {
-    const int key = k0 + 4 * kg + r;
-    const uint8_t* src = token_row<T::EB>(pl, ids[r], page_mask, key, hk, dg * T::V_DPT);
-    const bool ok = key < kv_len;
-    if constexpr (T::V_DW == 4) {
-      u32x4 x = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
-      for (int i = 0; i < 4; ++i) raw[4 * r + i] = x[i];
-    } else if constexpr (T::V_DW == 2) {
-      u32x2 x = ok ? *reinterpret_cast<const u32x2*>(src) : u32x2{0, 0};
-      raw[2 * r] = x[0];
-      raw[2 * r + 1] = x[1];
-    } else {
-      raw[r] = ok ? *reinterpret_cast<const uint32_t*>(src) : 0u;
-    }
-  }
-}
-
-template <int D, bool FP8>
-__device__ __forceinline__ void v_store(const uint32_t* raw, __bf16* vlds, int lt) {
+__device__ __forceinline__ void store_v(const uint32_t* raw, __bf16* vlds, int lw, int lane) {
   using T = Tile<D, FP8>;
   constexpr int PAIRS = T::V_DPT / 2;   // bf16 pairs per key
   uint32_t w[4][PAIRS];
@@ -228,8 +263,8 @@ __device__ __forceinline__ void v_store(const uint32_t* raw, __bf16* vlds, int l
       }
     }
   }
-  const int kg = lt & 15;
-  const int dg = lt >> 4;
+  const int key0 = 16 * lw + 4 * (lane >> 4);
+  const int dg = lane & 15;
   for (int i = 0; i < PAIRS; ++i) {
     // head-dim 2i: low halves of the 4 keys; head-dim 2i+1: high halves
     const uint32_t lo01 = (w[0][i] & 0xffffu) | (w[1][i] << 16);
@@ -237,16 +272,18 @@ __device__ __forceinline__ void v_store(const uint32_t* raw, __bf16* vlds, int l
     const uint32_t hi01 = (w[0][i] >> 16) | (w[1][i] & 0xffff0000u);
     const uint32_t hi23 = (w[2][i] >> 16) | (w[3][i] & 0xffff0000u);
     const int d = dg * T::V_DPT + 2 * i;
-    *reinterpret_cast<u32x2*>(vlds + d * T::VS + 4 * kg) = u32x2{lo01, lo23};
-    *reinterpret_cast<u32x2*>(vlds + (d + 1) * T::VS + 4 * kg) = u32x2{hi01, hi23};
+    *reinterpret_cast<u32x2*>(vlds + vt_offset(d, key0, T::VS)) = u32x2{lo01, lo23};
+    *reinterpret_cast<u32x2*>(vlds + vt_offset(d + 1, key0, T::VS)) = u32x2{hi01, hi23};
   }
 }
 
 // NT: 32-row MFMA column tiles per wave; NW: waves per workgroup.  Every
-// configuration has 256 rows per workgroup.  With NW = 8, waves 0-3 stage K
-// and waves 4-7 stage V; with NW = 4, every thread stages both.
-template <int D, bool FP8, int NT, int NW>
-__global__ __launch_bounds__(64 * NW) void paged_prefill_kernel(AttnArgs a) {
+// configuration has 256 rows per workgroup.  With NW = 8 (two waves per
+// SIMD), waves 0-3 stage K and waves 4-7 stage V; with NW = 4 every wave
+// stages both.
+template <int D, bool FP8, int NT, int NW, bool UPAGE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+void paged_prefill_kernel(AttnArgs a) {
   using T = Tile<D, FP8>;
   constexpr int KSTEPS = D / 16;   // MFMA K-steps over head_dim
   constexpr int MD = D / 32;       // 32-wide head_dim tiles of O^T
@@ -280,15 +317,20 @@ __global__ __launch_bounds__(64 * NW) void paged_prefill_kernel(AttnArgs a) {
   const int W = a.window_left;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
 
+  // logits in log2 units: s * c with c = |bmm1| log2(e); the sign of bmm1 is
+  // folded into Q (exact for bf16).  c is kept >= FLT_MIN so that a masked
+  // logit (-inf) times c stays -inf; with bmm1 = 0 every valid weight is then
+  // exp2(0) = 1 exactly, as it should be.
   float c = (a.bmm1_ptr ? *a.bmm1_ptr : a.bmm1) * kLog2e;
   const float bmm2 = a.bmm2_ptr ? *a.bmm2_ptr : a.bmm2;
-  const bool negate_q = c < 0.f;   // fold the sign into Q (exact for bf16)
+  const bool negate_q = c < 0.f;
   c = negate_q ? -c : c;
+  c = c > kMinScale ? c : kMinScale;
 
   // ---- the wave's rows ----------------------------------------------------
   constexpr int WROWS = 32 * NT;
@@ -347,84 +389,73 @@ __global__ __launch_bounds__(64 * NW) void paged_prefill_kernel(AttnArgs a) {
   pt.page_shift = a.page_shift;
   const int page_mask = (1 << a.page_shift) - 1;
 
-  // staging roles: which operand(s) this thread stages, as loader index lt
-  const int lt = tid & (kLoadThreads - 1);
-  const bool stage_k = !SPLIT_STAGING || wave < 4;
-  const bool stage_v = !SPLIT_STAGING || wave >= 4;
+  // staging roles
+  const int lw = wave & (kLoadWaves - 1);
+  const bool stage_k = !SPLIT_STAGING || wave < kLoadWaves;
+  const bool stage_v = !SPLIT_STAGING || wave >= kLoadWaves;
   constexpr int NRAW = SPLIT_STAGING ? 1 : 2;
   uint32_t raw[NRAW][T::RAW];
-  int ids[NRAW][T::IDS];
-  int ids_next[NRAW][T::IDS];
 
-  auto fetch_ids = [&](int (*dst)[T::IDS], int k0) {
-    if (stage_k) k_ids<D, FP8>(dst[0], pt, k0, lt);
-    if (stage_v) v_ids<D, FP8>(dst[NRAW - 1], pt, k0, lt);
+  auto fetch = [&](int k0) {
+    const bool tail = k0 + kBK > kv_len;
+    const int kb = k0 + 16 * lw;
+    if (stage_k) fetch_k<D, FP8, UPAGE>(raw[0], a.k, pt, hk, kb, kv_len, page_mask, lane, tail);
+    if (stage_v) fetch_v<D, FP8, UPAGE>(raw[NRAW - 1], a.v, pt, hk, kb, kv_len, page_mask, lane, tail);
   };
-  auto fetch_rows = [&](int k0) {
-    if (stage_k) k_fetch<D, FP8>(raw[0], ids[0], a.k, hk, k0, kv_len, page_mask, lt);
-    if (stage_v) v_fetch<D, FP8>(raw[NRAW - 1], ids[NRAW - 1], a.v, hk, k0, kv_len, page_mask, lt);
-  };
-  auto store_rows = [&](int buf) {
-    if (stage_k) k_store<D, FP8>(raw[0], klds[buf], lt);
-    if (stage_v) v_store<D, FP8>(raw[NRAW - 1], vlds[buf], lt);
+  auto store = [&](int buf) {
+    if (stage_k) store_k<D, FP8>(raw[0], klds[buf], lw, lane);
+    if (stage_v) store_v<D, FP8>(raw[NRAW - 1], vlds[buf], lw, lane);
   };
 
   if (tile_lo <= tile_hi) {
-    fetch_ids(ids, tile_lo * kBK);
-    fetch_rows(tile_lo * kBK);
-    if (tile_lo + 1 <= tile_hi) fetch_ids(ids_next, (tile_lo + 1) * kBK);
-    store_rows(0);
+    fetch(tile_lo * kBK);
+    store(0);
   }
   __syncthreads();
 
   const int krow_lane = swap_bits23(col);
+  const int vrow_base = col * T::VS + ((half ^ (col >> 4)) & 1) * 8;
 
   for (int tile = tile_lo; tile <= tile_hi; ++tile) {
     const int buf = (tile - tile_lo) & 1;
     const int k0 = tile * kBK;
     const bool more = tile + 1 <= tile_hi;
-    if (more) {
-      for (int r = 0; r < NRAW; ++r)
-        for (int i = 0; i < T::IDS; ++i) ids[r][i] = ids_next[r][i];
-      fetch_rows(k0 + kBK);
-      if (tile + 2 <= tile_hi) fetch_ids(ids_next, k0 + 2 * kBK);
-    }
+    if (more) fetch(k0 + kBK);
 
     const bool wave_tile = wave_active && k0 <= wkey_hi && k0 + kBK - 1 >= wkey_lo;
     if (wave_tile) {
-      // S^T = K Q^T over head_dim
+      // S^T = K Q^T over head_dim: all K fragments of the tile first
+      const __bf16* kbuf = klds[buf];
+      bf16x8 kf[2][KSTEPS];
+      for (int s = 0; s < KSTEPS; ++s)
+        for (int mt = 0; mt < 2; ++mt)
+          kf[mt][s] = *reinterpret_cast<const bf16x8*>(kbuf + (mt * 32 + krow_lane) * T::KS + s * 16 + half * 8);
       f32x16 sacc[2][NT];
       for (int mt = 0; mt < 2; ++mt)
         for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = f32x16{};
-      const __bf16* kb = klds[buf];
-      for (int s = 0; s < KSTEPS; ++s) {
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(kb + (mt * 32 + krow_lane) * T::KS + s * 16 + half * 8);
-          for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = mfma32(kf, qf[nt][s], sacc[mt][nt]);
-        }
-      }
+      for (int s = 0; s < KSTEPS; ++s)
+        for (int mt = 0; mt < 2; ++mt)
+          for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = mfma32(kf[mt][s], qf[nt][s], sacc[mt][nt]);
 
-      // masking: only tiles cut by the causal / window / length bounds
+      // mask only tiles cut by the causal / window / length bounds
       const bool need_mask = (k0 + kBK - 1 > wpos_first) || (W >= 0 && k0 < wpos_last - W) ||
                              (k0 + kBK > kv_len);
       float mx[NT];
       for (int nt = 0; nt < NT; ++nt) {
         float m = kNegInf;
         if (need_mask) {
-          const int hi = pos[nt] < kv_len - 1 ? pos[nt] : kv_len - 1;
-          const int lo = W >= 0 ? pos[nt] - W : -1;
+          const int base = k0 + 8 * half;
+          const int hi = (pos[nt] < kv_len - 1 ? pos[nt] : kv_len - 1) - base;
+          const int lo = (W >= 0 ? pos[nt] - W : -0x40000000) - base;
           for (int mt = 0; mt < 2; ++mt)
             for (int v = 0; v < 16; ++v) {
-              const int key = k0 + mt * 32 + 16 * (v >> 3) + 8 * half + (v & 7);
-              const bool ok = key <= hi && key >= lo;
+              const int off = mt * 32 + 16 * (v >> 3) + (v & 7);
+              const bool ok = off <= hi && off >= lo;
               sacc[mt][nt][v] = ok ? sacc[mt][nt][v] : kNegInf;
-              m = fmaxf(m, sacc[mt][nt][v]);
             }
-        } else {
-          for (int mt = 0; mt < 2; ++mt)
-            for (int v = 0; v < 16; ++v) m = fmaxf(m, sacc[mt][nt][v]);
         }
+        for (int mt = 0; mt < 2; ++mt)
+          for (int v = 0; v < 16; ++v) m = fmaxf(m, sacc[mt][nt][v]);
         mx[nt] = fmaxf(m, __shfl_xor(m, 32));
       }
 
@@ -433,7 +464,7 @@ __global__ __launch_bounds__(64 * NW) void paged_prefill_kernel(AttnArgs a) {
       float mtile[NT];
       bool any = false;
       for (int nt = 0; nt < NT; ++nt) {
-        mtile[nt] = mx[nt] == kNegInf ? kNegInf : mx[nt] * c;
+        mtile[nt] = mx[nt] * c;   // -inf stays -inf (c > 0)
         need[nt] = mtile[nt] > m_run[nt] + kRescaleThreshold;
         any = any || need[nt];
       }
@@ -447,7 +478,8 @@ __global__ __launch_bounds__(64 * NW) void paged_prefill_kernel(AttnArgs a) {
         }
       }
 
-      // P = exp2(c s - m), row partial sums, bf16 B operands of O^T += V^T P^T
+      // P = exp2(c s - m) (masked logits give exp2(-inf) = 0), row partial
+      // sums, bf16 B operands of O^T += V^T P^T
       bf16x8 pb[NT][4];
       for (int nt = 0; nt < NT; ++nt) {
         const float mb = m_run[nt] == kNegInf ? 0.f : m_run[nt];
@@ -456,7 +488,6 @@ __global__ __launch_bounds__(64 * NW) void paged_prefill_kernel(AttnArgs a) {
           float p[16];
           for (int v = 0; v < 16; ++v) {
             p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][nt][v], c, -mb));
-            if (need_mask) p[v] = sacc[mt][nt][v] == kNegInf ? 0.f : p[v];
             sum += p[v];
           }
           for (int sh = 0; sh < 2; ++sh) {
@@ -468,17 +499,20 @@ __global__ __launch_bounds__(64 * NW) void paged_prefill_kernel(AttnArgs a) {
         l_part[nt] += sum;
       }
 
-      const __bf16* vb = vlds[buf];
-      for (int ks = 0; ks < 4; ++ks) {
-        for (int md = 0; md < MD; ++md) {
-          const bf16x8 vf =
-              *reinterpret_cast<const bf16x8*>(vb + (md * 32 + col) * T::VS + ks * 16 + half * 8);
-          for (int nt = 0; nt < NT; ++nt) oacc[nt][md] = mfma32(vf, pb[nt][ks], oacc[nt][md]);
-        }
-      }
+      // O^T += V^T P^T: all V fragments of the tile first
+      // lane (col, half) reads dims md*32 + col, keys 16 ks + 8 half .. + 7; in
+      // the swizzled layout that key chunk is 2 (ks ^ md) + (half ^ (col >> 4))
+      const __bf16* vbuf = vlds[buf] + vrow_base;
+      bf16x8 vf[MD][4];
+      for (int ks = 0; ks < 4; ++ks)
+        for (int md = 0; md < MD; ++md)
+          vf[md][ks] = *reinterpret_cast<const bf16x8*>(vbuf + md * 32 * T::VS + ((ks ^ md) & 3) * 16);
+      for (int ks = 0; ks < 4; ++ks)
+        for (int md = 0; md < MD; ++md)
+          for (int nt = 0; nt < NT; ++nt) oacc[nt][md] = mfma32(vf[md][ks], pb[nt][ks], oacc[nt][md]);
     }
 
-    if (more) store_rows(buf ^ 1);
+    if (more) store(buf ^ 1);
     __syncthreads();
   }
 
@@ -557,15 +591,21 @@ int log2_exact(int x) {
 }
 
 // Kernel shape: 8 waves x 32 rows (two waves per SIMD) unless PPA_WAVES=4
-// asks for 4 waves x 64 rows (one wave per SIMD).
-template <int D, bool FP8>
-hipError_t launch(const AttnArgs& a, int grid, hipStream_t stream, int waves) {
+// asks for 4 waves x 64 rows (one wave per SIMD).  UPAGE: page_size >= 16.
+template <int D, bool FP8, bool UPAGE>
+hipError_t launch_shape(const AttnArgs& a, int grid, hipStream_t stream, int waves) {
   if (waves == 4) {
-    hipLaunchKernelGGL((paged_prefill_kernel<D, FP8, 2, 4>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((paged_prefill_kernel<D, FP8, 2, 4, UPAGE>), dim3(grid), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((paged_prefill_kernel<D, FP8, 1, 8>), dim3(grid), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((paged_prefill_kernel<D, FP8, 1, 8, UPAGE>), dim3(grid), dim3(512), 0, stream, a);
   }
   return hipGetLastError();
+}
+
+template <int D, bool FP8>
+hipError_t launch(const AttnArgs& a, int grid, hipStream_t stream, int waves, bool upage) {
+  return upage ? launch_shape<D, FP8, true>(a, grid, stream, waves)
+               : launch_shape<D, FP8, false>(a, grid, stream, waves);
 }
 
 int waves_setting() {
@@ -627,10 +667,19 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
   const bool fp8 = p->kv_dtype == PPA_DTYPE_FP8_E4M3FN;
   const int w = waves_setting();
   const int g = static_cast<int>(grid);
+  // uniform-page staging needs pages of >= 16 tokens whose byte extent fits
+  // the 32-bit in-page offsets
+  const int eb = fp8 ? 1 : 2;
+  auto extent = [&](const PagedPlane& pl) {
+    return (static_cast<int64_t>(p->page_size) * pl.tok_stride +
+            static_cast<int64_t>(p->num_kv_heads) * pl.head_stride + p->head_dim) * eb;
+  };
+  const bool upage = p->page_size >= 16 && extent(a.k) < (int64_t{1} << 31) &&
+                     extent(a.v) < (int64_t{1} << 31);
   if (p->head_dim == 128)
-    e = fp8 ? launch<128, true>(a, g, s, w) : launch<128, false>(a, g, s, w);
+    e = fp8 ? launch<128, true>(a, g, s, w, upage) : launch<128, false>(a, g, s, w, upage);
   else
-    e = fp8 ? launch<64, true>(a, g, s, w) : launch<64, false>(a, g, s, w);
+    e = fp8 ? launch<64, true>(a, g, s, w, upage) : launch<64, false>(a, g, s, w, upage);
   return e == hipSuccess ? PPA_OK : PPA_ERR_HIP;
 }
 

@@ -9,12 +9,12 @@
 // per-head sink adds e^{sink} to the softmax denominator only.
 //
 // Work decomposition
-//   One workgroup = 4 waves = 256 "rows"; a row is one (token, q head) pair of
+//   One workgroup = 8 waves = 256 "rows"; a row is one (token, q head) pair of
 //   one request and one kv head.  The GW = min(G, 16) query heads of a GQA
 //   group that share the kv head are interleaved (row = token * GW + head), so
 //   a K/V tile staged once in LDS serves every head of the group and the
-//   causal boundary of a 32-row MFMA tile spans only 32 / GW tokens.
-//   Each wave owns 64 rows = two 32-column MFMA tiles.
+//   causal boundary of a 32-row MFMA tile spans only 32 / GW tokens.  Each
+//   wave owns 32 rows (one MFMA column tile); two waves share a SIMD.
 //   The grid is 1-D and ordered heaviest-first: blockIdx / R picks the query
 //   tile from the last (longest causal span) to the first, blockIdx % R picks
 //   (request, kv head, head group).  With R a multiple of 8, every tile of one
@@ -22,9 +22,12 @@
 //   8 XCDs), so its K/V stays in one L2.
 //
 // Per 64-key tile
-//   1. page ids -> K rows (natural layout) and V rows (transposed in
-//      registers) into double-buffered LDS; fp8 codes are widened to bf16 on
-//      the way (exact: every e4m3fn value is a bf16 value);
+//   1. staging: each wave copies 8 consecutive keys of K and of V from their
+//      pages into double-buffered LDS, K in natural layout and V transposed
+//      in registers to [dim][key] (fp8 codes are widened to bf16 on the way:
+//      every e4m3fn value is a bf16 value).  With pages of >= 8 tokens a
+//      wave's keys share one page, whose id is read by a scalar load one tile
+//      ahead;
 //   2. S^T = K Q^T on v_mfma_f32_32x32x16_bf16: keys along M, rows along N,
 //      so a lane holds 32 keys of one row and its partner lane (lane ^ 32) the
 //      other 32: row max / sum need one cross-lane step;
@@ -56,7 +59,7 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr int kBK = 64;            // keys per tile
-constexpr int kLoadWaves = 4;      // waves of threads that stage one operand (K or V) of a tile
+constexpr int kWaves = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 constexpr float kNegInf = -__builtin_inff();
@@ -95,8 +98,7 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  f32x2 v = {lo, hi};
-  bf16x2 r = __builtin_convertvector(v, bf16x2);   // v_cvt_pk_bf16_f32, round to nearest even
+  bf16x2 r = __builtin_convertvector(f32x2{lo, hi}, bf16x2);   // v_cvt_pk_bf16_f32, round to nearest even
   return __builtin_bit_cast(uint32_t, r);
 }
 
@@ -116,157 +118,156 @@ __device__ __forceinline__ int swap_bits23(int i) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Tile geometry.  K and V of a 64-key tile are each staged by 4 loader waves;
-// loader wave lw owns the 16 consecutive keys [16 lw, 16 lw + 16) of the tile,
-// so with pages of >= 16 tokens its keys lie in one page and the page id and
-// base address are wave-uniform.  K goes to LDS in natural [key][dim] layout
-// with 16-byte loads; V goes as 4 consecutive keys x V_DPT dims per lane,
-// transposed in registers to [dim][key].  Both need RAW dwords per lane.
+// Tile geometry.  Every wave stages 8 consecutive keys of both K and V of a
+// 64-key tile, so the staging work is the same for all waves and, with pages
+// of >= 8 tokens, a wave's keys lie in one page whose id is wave-uniform.
+// K goes to LDS in natural [key][dim] layout (row stride padded by 16 bytes,
+// so the S operand reads, 16 different rows per 16 lanes, hit distinct
+// banks).  V goes as 4 consecutive keys x V_DPT dims per lane, transposed in
+// registers to [dim][key], with the 16-byte key chunks of each dim row XOR
+// swizzled by (dim >> 4) & 7 and rows padded by 16 bytes, which keeps both the
+// transposed writes and the MFMA operand reads free of bank conflicts.
 template <int D, bool FP8>
 struct Tile {
   static constexpr int EB = FP8 ? 1 : 2;        // bytes per cache element
-  static constexpr int K_CHUNK = 16 / EB;       // elements per 16-byte load
+  static constexpr int K_LANE_BYTES = D * EB / 8;              // 8 rows per wave
+  static constexpr int K_LOAD = K_LANE_BYTES < 16 ? K_LANE_BYTES : 16;
+  static constexpr int K_PASSES = K_LANE_BYTES / K_LOAD;
+  static constexpr int K_CHUNK = K_LOAD / EB;   // elements per load
   static constexpr int K_TPR = D / K_CHUNK;     // lanes per key row
   static constexpr int K_RPI = 64 / K_TPR;      // key rows per wave instruction
-  static constexpr int K_PASSES = 16 / K_RPI;   // instructions per loader wave
-  static constexpr int V_DPT = D / 16;          // head-dim values per lane
-  static constexpr int V_DW = V_DPT * EB / 4;   // raw dwords per key
-  static constexpr int RAW = D * EB / 16;       // raw dwords per lane and operand
-  // LDS row strides in bf16 elements.  K rows are padded by 16 bytes; V rows
-  // by 16 bytes plus an XOR swizzle of their 16-byte key chunks by
-  // (dim >> 4) & 7, which together keep the MFMA operand reads and the
-  // transposed V writes free of bank conflicts.
+  static constexpr int V_DPT = D / 32;          // dims per lane (32 dim groups)
+  static constexpr int V_KEY_BYTES = V_DPT * EB;   // raw bytes per key per lane
+  static constexpr int K_DW = K_LANE_BYTES / 4;
+  static constexpr int V_DW = (4 * V_KEY_BYTES + 3) / 4;
   static constexpr int KS = D + 8;
   static constexpr int VS = kBK + 8;
   static constexpr int K_ELEMS = kBK * KS;
   static constexpr int V_ELEMS = D * VS;
-  static_assert(K_PASSES * K_RPI == 16, "K tile mapping");
-  static_assert(K_PASSES * 4 == RAW && 4 * V_DW == RAW, "K and V prefetch sizes");
-  static_assert(V_DW >= 1, "V load");
+  static_assert(K_PASSES * K_RPI == 8, "K staging map");
 };
 
 __device__ __forceinline__ int vt_offset(int d, int key, int vs) {
   // element offset of V^T[d][key] in the swizzled layout
-  const int chunk = (key >> 3) ^ ((d >> 4) & 7);
-  return d * vs + chunk * 8 + (key & 7);
+  return d * vs + (((key >> 3) ^ ((d >> 4) & 7)) << 3) + (key & 7);
 }
 
-// ---- staging: global -> registers ---------------------------------------------
-// UPAGE: the loader wave's 16 keys share one page (page_size >= 16 and the tile
-// is not the last one of the request).  Otherwise every lane resolves its own
-// keys, clamped to the sequence, and zero-fills keys past kv_len.
-template <int D, bool FP8, bool UPAGE>
-__device__ __forceinline__ void fetch_k(uint32_t* raw, const PagedPlane& pl, const PageTable& pt,
-                                        int hk, int kb, int kv_len, int page_mask, int lane,
-                                        bool tail) {
+template <int BYTES>
+__device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src, bool ok) {
+  if constexpr (BYTES == 16) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+    for (int i = 0; i < 4; ++i) dst[i] = ok ? x[i] : 0u;
+  } else if constexpr (BYTES == 8) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(src);
+    dst[0] = ok ? x[0] : 0u;
+    dst[1] = ok ? x[1] : 0u;
+  } else if constexpr (BYTES == 4) {
+    const uint32_t x = *reinterpret_cast<const uint32_t*>(src);
+    dst[0] = ok ? x : 0u;
+  }
+}
+
+// ---- staging: pages -> registers --------------------------------------------
+// The wave's keys are [kb, kb + 8).  Fast path (`id` is their page, the tile is
+// not the last one of the request): rows are addressed by 32-bit offsets from
+// the wave-uniform page base.  General path: every lane resolves its own keys
+// through the page table, clamped to the sequence, and zero-fills keys past
+// kv_len.
+template <int D, bool FP8, bool FAST>
+__device__ __forceinline__ void fetch_kv(uint32_t* kraw, uint32_t* vraw, const AttnArgs& a, const PageTable& pt,
+                                         int id, int hk, int kb, int kv_len, int page_mask, int lane) {
   using T = Tile<D, FP8>;
-  const int kchunk = lane % T::K_TPR;
   const int r0 = lane / T::K_TPR;
-  if (UPAGE && !tail) {
-    const int id = uniform(page_id(pt, kb));
-    const uint8_t* base = pl.base + (static_cast<int64_t>(id) * pl.page_stride +
-                                     static_cast<int64_t>(hk) * pl.head_stride) * T::EB;
+  const int chunk = lane % T::K_TPR;
+  const int kgl = lane >> 5;   // V: keys kb + 4 kgl .. + 3
+  const int dg = lane & 31;    // V: dims dg * V_DPT .. + V_DPT - 1
+  if (FAST) {
+    const int64_t page_off = static_cast<int64_t>(id) * a.k.page_stride + static_cast<int64_t>(hk) * a.k.head_stride;
+    const int64_t vpage_off = static_cast<int64_t>(id) * a.v.page_stride + static_cast<int64_t>(hk) * a.v.head_stride;
+    const uint8_t* kbase = a.k.base + page_off * T::EB;
+    const uint8_t* vbase = a.v.base + vpage_off * T::EB;
     const int slot0 = kb & page_mask;
     for (int p = 0; p < T::K_PASSES; ++p) {
       const uint32_t off = static_cast<uint32_t>(
-          ((slot0 + p * T::K_RPI + r0) * static_cast<int>(pl.tok_stride) + kchunk * T::K_CHUNK) * T::EB);
-      const u32x4 x = *reinterpret_cast<const u32x4*>(base + off);
-      for (int i = 0; i < 4; ++i) raw[4 * p + i] = x[i];
+          ((slot0 + p * T::K_RPI + r0) * static_cast<int>(a.k.tok_stride) + chunk * T::K_CHUNK) * T::EB);
+      load_bytes<T::K_LOAD>(kraw + p * (T::K_LOAD / 4), kbase + off, true);
+    }
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t off = static_cast<uint32_t>(
+          ((slot0 + 4 * kgl + r) * static_cast<int>(a.v.tok_stride) + dg * T::V_DPT) * T::EB);
+      if constexpr (T::V_KEY_BYTES >= 4) {
+        load_bytes<T::V_KEY_BYTES>(vraw + r * (T::V_KEY_BYTES / 4), vbase + off, true);
+      } else {   // 2 bytes per key: pack two keys per dword
+        const uint32_t x = *reinterpret_cast<const uint16_t*>(vbase + off);
+        vraw[r >> 1] = (r & 1) ? (vraw[r >> 1] | (x << 16)) : x;
+      }
     }
   } else {
     for (int p = 0; p < T::K_PASSES; ++p) {
       const int key = kb + p * T::K_RPI + r0;
       const bool ok = key < kv_len;
       const int kc = ok ? key : kv_len - 1;
-      const int id = page_id(pt, kc);
-      u32x4 x = *reinterpret_cast<const u32x4*>(token_row<T::EB>(pl, id, page_mask, kc, hk, kchunk * T::K_CHUNK));
-      for (int i = 0; i < 4; ++i) raw[4 * p + i] = ok ? x[i] : 0u;
+      const int kid = page_id(pt, kc);
+      load_bytes<T::K_LOAD>(kraw + p * (T::K_LOAD / 4),
+                            token_row<T::EB>(a.k, kid, page_mask, kc, hk, chunk * T::K_CHUNK), ok);
     }
-  }
-}
-
-template <int D, bool FP8, bool UPAGE>
-__device__ __forceinline__ void fetch_v(uint32_t* raw, const PagedPlane& pl, const PageTable& pt,
-                                        int hk, int kb, int kv_len, int page_mask, int lane,
-                                        bool tail) {
-  using T = Tile<D, FP8>;
-  const int kgl = lane >> 4;   // 4 keys: kb + 4 kgl .. + 3
-  const int dg = lane & 15;
-  auto load = [&](const uint8_t* src, uint32_t* dst, bool ok) {
-    if constexpr (T::V_DW == 4) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(src);
-      for (int i = 0; i < 4; ++i) dst[i] = ok ? x[i] : 0u;
-    } else if constexpr (T::V_DW == 2) {
-      const u32x2 x = *reinterpret_cast<const u32x2*>(src);
-      dst[0] = ok ? x[0] : 0u;
-      dst[1] = ok ? x[1] : 0u;
-    } else {
-      const uint32_t x = *reinterpret_cast<const uint32_t*>(src);
-      dst[0] = ok ? x : 0u;
-    }
-  };
-  if (UPAGE && !tail) {
-    const int id = uniform(page_id(pt, kb));
-    const uint8_t* base = pl.base + (static_cast<int64_t>(id) * pl.page_stride +
-                                     static_cast<int64_t>(hk) * pl.head_stride) * T::EB;
-    const int slot0 = (kb & page_mask) + 4 * kgl;
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t off = static_cast<uint32_t>(
-          ((slot0 + r) * static_cast<int>(pl.tok_stride) + dg * T::V_DPT) * T::EB);
-      load(base + off, raw + T::V_DW * r, true);
-    }
-  } else {
     for (int r = 0; r < 4; ++r) {
       const int key = kb + 4 * kgl + r;
       const bool ok = key < kv_len;
       const int kc = ok ? key : kv_len - 1;
-      const int id = page_id(pt, kc);
-      load(token_row<T::EB>(pl, id, page_mask, kc, hk, dg * T::V_DPT), raw + T::V_DW * r, ok);
+      const int vid = page_id(pt, kc);
+      const uint8_t* src = token_row<T::EB>(a.v, vid, page_mask, kc, hk, dg * T::V_DPT);
+      if constexpr (T::V_KEY_BYTES >= 4) {
+        load_bytes<T::V_KEY_BYTES>(vraw + r * (T::V_KEY_BYTES / 4), src, ok);
+      } else {
+        const uint32_t x = ok ? static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(src)) : 0u;
+        vraw[r >> 1] = (r & 1) ? (vraw[r >> 1] | (x << 16)) : x;
+      }
     }
   }
 }
 
-// ---- staging: registers -> LDS ---------------------------------------------------
+// ---- staging: registers -> LDS ------------------------------------------------
 template <int D, bool FP8>
-__device__ __forceinline__ void store_k(const uint32_t* raw, __bf16* klds, int lw, int lane) {
+__device__ __forceinline__ void store_kv(const uint32_t* kraw, const uint32_t* vraw, __bf16* klds, __bf16* vlds,
+                                         int wave, int lane) {
   using T = Tile<D, FP8>;
-  const int kchunk = lane % T::K_TPR;
+  // K rows
   const int r0 = lane / T::K_TPR;
+  const int chunk = lane % T::K_TPR;
   for (int p = 0; p < T::K_PASSES; ++p) {
-    __bf16* dst = klds + (16 * lw + p * T::K_RPI + r0) * T::KS + kchunk * T::K_CHUNK;
+    __bf16* dst = klds + (8 * wave + p * T::K_RPI + r0) * T::KS + chunk * T::K_CHUNK;
+    const uint32_t* x = kraw + p * (T::K_LOAD / 4);
     if constexpr (!FP8) {
-      *reinterpret_cast<u32x4*>(dst) = u32x4{raw[4 * p], raw[4 * p + 1], raw[4 * p + 2], raw[4 * p + 3]};
+      if constexpr (T::K_LOAD == 16) *reinterpret_cast<u32x4*>(dst) = u32x4{x[0], x[1], x[2], x[3]};
+      else *reinterpret_cast<u32x2*>(dst) = u32x2{x[0], x[1]};
     } else {
-      const u32x2 a0 = fp8x4_to_bf16x4(raw[4 * p]);
-      const u32x2 a1 = fp8x4_to_bf16x4(raw[4 * p + 1]);
-      const u32x2 a2 = fp8x4_to_bf16x4(raw[4 * p + 2]);
-      const u32x2 a3 = fp8x4_to_bf16x4(raw[4 * p + 3]);
-      reinterpret_cast<u32x4*>(dst)[0] = u32x4{a0[0], a0[1], a1[0], a1[1]};
-      reinterpret_cast<u32x4*>(dst)[1] = u32x4{a2[0], a2[1], a3[0], a3[1]};
+      for (int i = 0; i < T::K_LOAD / 4; ++i) {
+        const u32x2 w = fp8x4_to_bf16x4(x[i]);
+        *reinterpret_cast<u32x2*>(dst + 4 * i) = w;
+      }
     }
   }
-}
-
-template <int D, bool FP8>
-__device__ __forceinline__ void store_v(const uint32_t* raw, __bf16* vlds, int lw, int lane) {
-  using T = Tile<D, FP8>;
+  // V: 4 keys x V_DPT dims -> V_DPT dim rows of 4 keys
   constexpr int PAIRS = T::V_DPT / 2;   // bf16 pairs per key
   uint32_t w[4][PAIRS];
   for (int r = 0; r < 4; ++r) {
     if constexpr (!FP8) {
-      for (int i = 0; i < PAIRS; ++i) w[r][i] = raw[T::V_DW * r + i];
-    } else {
-      for (int i = 0; i < T::V_DW; ++i) {
-        const u32x2 x = fp8x4_to_bf16x4(raw[T::V_DW * r + i]);
-        w[r][2 * i] = x[0];
-        w[r][2 * i + 1] = x[1];
-      }
+      for (int i = 0; i < PAIRS; ++i) w[r][i] = vraw[PAIRS * r + i];
+    } else if constexpr (T::V_KEY_BYTES == 4) {   // 4 fp8 per key
+      const u32x2 x = fp8x4_to_bf16x4(vraw[r]);
+      w[r][0] = x[0];
+      w[r][1] = x[1];
+    } else {                                       // 2 fp8 per key, two keys per dword
+      const uint32_t codes = (vraw[r >> 1] >> (16 * (r & 1))) & 0xffffu;
+      const u32x2 x = fp8x4_to_bf16x4(codes);
+      w[r][0] = x[0];
     }
   }
-  const int key0 = 16 * lw + 4 * (lane >> 4);
-  const int dg = lane & 15;
+  const int key0 = 8 * wave + 4 * (lane >> 5);
+  const int dg = lane & 31;
   for (int i = 0; i < PAIRS; ++i) {
-    // head-dim 2i: low halves of the 4 keys; head-dim 2i+1: high halves
+    // dim 2i of the lane: low halves of the 4 keys; dim 2i+1: high halves
     const uint32_t lo01 = (w[0][i] & 0xffffu) | (w[1][i] << 16);
     const uint32_t lo23 = (w[2][i] & 0xffffu) | (w[3][i] << 16);
     const uint32_t hi01 = (w[0][i] >> 16) | (w[1][i] & 0xffff0000u);
@@ -277,18 +278,14 @@ __device__ __forceinline__ void store_v(const uint32_t* raw, __bf16* vlds, int l
   }
 }
 
-// NT: 32-row MFMA column tiles per wave; NW: waves per workgroup.  Every
-// configuration has 256 rows per workgroup.  With NW = 8 (two waves per
-// SIMD), waves 0-3 stage K and waves 4-7 stage V; with NW = 4 every wave
-// stages both.
-template <int D, bool FP8, int NT, int NW, bool UPAGE>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+// Per tile: stage tile j+1 into registers, run S, softmax and PV for tile j
+// from LDS, store tile j+1 into the other LDS buffer, barrier.
+template <int D, bool FP8, bool UPAGE>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void paged_prefill_kernel(AttnArgs a) {
   using T = Tile<D, FP8>;
   constexpr int KSTEPS = D / 16;   // MFMA K-steps over head_dim
   constexpr int MD = D / 32;       // 32-wide head_dim tiles of O^T
-  constexpr bool SPLIT_STAGING = NW == 8;
-  static_assert(NT * NW * 32 == 256, "256 rows per workgroup");
   __shared__ __attribute__((aligned(16))) __bf16 klds[2][T::K_ELEMS];
   __shared__ __attribute__((aligned(16))) __bf16 vlds[2][T::V_ELEMS];
 
@@ -332,19 +329,14 @@ void paged_prefill_kernel(AttnArgs a) {
   c = negate_q ? -c : c;
   c = c > kMinScale ? c : kMinScale;
 
-  // ---- the wave's rows ----------------------------------------------------
-  constexpr int WROWS = 32 * NT;
-  int tok[NT], hd[NT], pos[NT];
-  bool rvalid[NT];
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = wave * WROWS + nt * 32 + col;
-    tok[nt] = r / a.gw;
-    hd[nt] = r % a.gw;
-    rvalid[nt] = tok[nt] < ntok && hd[nt] < nheads;
-    pos[nt] = prefix + t0 + tok[nt];
-  }
-  const int wtok_first = (wave * WROWS) / a.gw;
-  int wtok_last = (wave * WROWS + WROWS - 1) / a.gw;
+  // ---- the wave's 32 rows -----------------------------------------------------
+  const int r = wave * 32 + col;
+  const int tok = r / a.gw;
+  const int hd = r % a.gw;
+  const bool rvalid = tok < ntok && hd < nheads;
+  const int pos = prefix + t0 + tok;
+  const int wtok_first = (wave * 32) / a.gw;
+  int wtok_last = (wave * 32 + 31) / a.gw;
   wtok_last = wtok_last < ntok - 1 ? wtok_last : ntok - 1;
   const bool wave_active = wtok_first < ntok;
   const int wpos_first = prefix + t0 + wtok_first;
@@ -352,27 +344,23 @@ void paged_prefill_kernel(AttnArgs a) {
   const int wkey_hi = wpos_last < kv_len - 1 ? wpos_last : kv_len - 1;
   const int wkey_lo = W >= 0 ? (wpos_first - W > 0 ? wpos_first - W : 0) : 0;
 
-  // ---- Q into registers (B operand of S^T = K Q^T) ------------------------
-  bf16x8 qf[NT][KSTEPS];
-  for (int nt = 0; nt < NT; ++nt) {
-    const uint16_t* qrow = a.q + static_cast<int64_t>(q0 + t0 + tok[nt]) * a.q_tok +
-                           static_cast<int64_t>(h0 + hd[nt]) * a.q_head;
+  bf16x8 qf[KSTEPS];   // B operand of S^T = K Q^T
+  {
+    const uint16_t* qrow = a.q + static_cast<int64_t>(q0 + t0 + tok) * a.q_tok +
+                           static_cast<int64_t>(h0 + hd) * a.q_head;
     for (int s = 0; s < KSTEPS; ++s) {
       u32x4 x = u32x4{0, 0, 0, 0};
-      if (rvalid[nt]) x = *reinterpret_cast<const u32x4*>(qrow + s * 16 + half * 8);
+      if (rvalid) x = *reinterpret_cast<const u32x4*>(qrow + s * 16 + half * 8);
       if (negate_q) x ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-      qf[nt][s] = __builtin_bit_cast(bf16x8, x);
+      qf[s] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
-  f32x16 oacc[NT][MD];
-  for (int nt = 0; nt < NT; ++nt)
-    for (int md = 0; md < MD; ++md) oacc[nt][md] = f32x16{};
-  float m_run[NT], l_part[NT];
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = kNegInf;
-    l_part[nt] = 0.f;
-  }
+  f32x16 oacc[MD];
+  for (int md = 0; md < MD; ++md) oacc[md] = f32x16{};
+  float m_run = kNegInf, l_part = 0.f;
+  f32x16 sacc[2];
+  bf16x8 pb[4];
 
   // ---- K/V tile range of the workgroup -------------------------------------
   const int pos_first = prefix + t0;
@@ -388,152 +376,135 @@ void paged_prefill_kernel(AttnArgs a) {
   pt.num_pages = a.num_pages;
   pt.page_shift = a.page_shift;
   const int page_mask = (1 << a.page_shift) - 1;
+  uint32_t kraw[T::K_DW], vraw[T::V_DW];
+  int id_next = 0;   // page id of the wave's keys in the next tile to fetch
 
-  // staging roles
-  const int lw = wave & (kLoadWaves - 1);
-  const bool stage_k = !SPLIT_STAGING || wave < kLoadWaves;
-  const bool stage_v = !SPLIT_STAGING || wave >= kLoadWaves;
-  constexpr int NRAW = SPLIT_STAGING ? 1 : 2;
-  uint32_t raw[NRAW][T::RAW];
+  const int krow_lane = swap_bits23(col);
+  // V^T operand reads: lane (col, half) reads dims md*32 + col, keys
+  // 16 ks + 8 half .. + 7; in the swizzled layout that key chunk is
+  // 2 (ks ^ md) + (half ^ (col >> 4))
+  const int vrow_base = col * T::VS + ((half ^ (col >> 4)) & 1) * 8;
 
-  auto fetch = [&](int k0) {
-    const bool tail = k0 + kBK > kv_len;
-    const int kb = k0 + 16 * lw;
-    if (stage_k) fetch_k<D, FP8, UPAGE>(raw[0], a.k, pt, hk, kb, kv_len, page_mask, lane, tail);
-    if (stage_v) fetch_v<D, FP8, UPAGE>(raw[NRAW - 1], a.v, pt, hk, kb, kv_len, page_mask, lane, tail);
+  auto wave_tile = [&](int j) {
+    return wave_active && j * kBK <= wkey_hi && j * kBK + kBK - 1 >= wkey_lo;
   };
-  auto store = [&](int buf) {
-    if (stage_k) store_k<D, FP8>(raw[0], klds[buf], lw, lane);
-    if (stage_v) store_v<D, FP8>(raw[NRAW - 1], vlds[buf], lw, lane);
+  auto page_of = [&](int j) { return UPAGE ? page_id_uniform(pt, uniform(j * kBK + 8 * wave)) : 0; };
+  // copy the wave's 8 keys of tile j into registers; `id` is their page id
+  auto stage_fetch = [&](int j, int id) {
+    const int kb = j * kBK + 8 * wave;
+    if (UPAGE && j * kBK + kBK <= kv_len) fetch_kv<D, FP8, true>(kraw, vraw, a, pt, id, hk, kb, kv_len, page_mask, lane);
+    else fetch_kv<D, FP8, false>(kraw, vraw, a, pt, id, hk, kb, kv_len, page_mask, lane);
+  };
+  auto stage_store = [&](int j) {
+    const int buf = (j - tile_lo) & 1;
+    store_kv<D, FP8>(kraw, vraw, klds[buf], vlds[buf], wave, lane);
+  };
+  auto gemm_s = [&](int j) {
+    const __bf16* kbuf = klds[(j - tile_lo) & 1] + krow_lane * T::KS + half * 8;
+    bf16x8 kf[2][KSTEPS];
+    for (int s = 0; s < KSTEPS; ++s)
+      for (int mt = 0; mt < 2; ++mt)
+        kf[mt][s] = *reinterpret_cast<const bf16x8*>(kbuf + mt * 32 * T::KS + s * 16);
+    __builtin_amdgcn_sched_barrier(0);
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+    for (int s = 0; s < KSTEPS; ++s)
+      for (int mt = 0; mt < 2; ++mt) sacc[mt] = mfma32(kf[mt][s], qf[s], sacc[mt]);
+  };
+  auto gemm_pv = [&](int j) {
+    const __bf16* vbuf = vlds[(j - tile_lo) & 1] + vrow_base;
+    bf16x8 vf[MD][4];
+    for (int ks = 0; ks < 4; ++ks)
+      for (int md = 0; md < MD; ++md)
+        vf[md][ks] = *reinterpret_cast<const bf16x8*>(vbuf + md * 32 * T::VS + ((ks ^ md) & 3) * 16);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int ks = 0; ks < 4; ++ks)
+      for (int md = 0; md < MD; ++md) oacc[md] = mfma32(vf[md][ks], pb[ks], oacc[md]);
+  };
+  auto softmax = [&](int j) {
+    const int k0 = j * kBK;
+    const bool need_mask = (k0 + kBK - 1 > wpos_first) || (W >= 0 && k0 < wpos_last - W) ||
+                           (k0 + kBK > kv_len);
+    if (need_mask) {
+      const int base = k0 + 8 * half;
+      const int hi = (pos < kv_len - 1 ? pos : kv_len - 1) - base;
+      const int lo = (W >= 0 ? pos - W : -0x40000000) - base;
+      for (int mt = 0; mt < 2; ++mt)
+        for (int v = 0; v < 16; ++v) {
+          const int off = mt * 32 + 16 * (v >> 3) + (v & 7);
+          sacc[mt][v] = (off <= hi && off >= lo) ? sacc[mt][v] : kNegInf;
+        }
+    }
+    float m = kNegInf;
+    for (int mt = 0; mt < 2; ++mt)
+      for (int v = 0; v < 16; ++v) m = fmaxf(m, sacc[mt][v]);
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const float mtile = m * c;   // -inf stays -inf (c > 0)
+    const bool need = mtile > m_run + kRescaleThreshold;
+    if (__ballot(need) != 0ull) {
+      const float m_new = need ? mtile : m_run;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      m_run = m_new;
+      l_part *= alpha;
+      for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
+    }
+    const float mb = m_run == kNegInf ? 0.f : m_run;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float sum = l_part;
+    for (int mt = 0; mt < 2; ++mt)
+      for (int sh = 0; sh < 2; ++sh) {
+        bf16x2 w[4];
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][8 * sh + 2 * e], c, -mb));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][8 * sh + 2 * e + 1], c, -mb));
+          w[e] = __builtin_convertvector(f32x2{p0, p1}, bf16x2);   // round to nearest even
+          // row sums of the bf16 weights the PV product uses.  (The packed
+          // value is fed to v_dot2 directly; reading it back out of a 4-dword
+          // vector first was miscompiled - every dot2 got the same operand.)
+          sum = __builtin_amdgcn_fdot2_f32_bf16(w[e], ones, sum, false);
+        }
+        pb[2 * mt + sh] = bf16x8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
+      }
+    l_part = sum;
   };
 
   if (tile_lo <= tile_hi) {
-    fetch(tile_lo * kBK);
-    store(0);
-  }
-  __syncthreads();
-
-  const int krow_lane = swap_bits23(col);
-  const int vrow_base = col * T::VS + ((half ^ (col >> 4)) & 1) * 8;
-
-  for (int tile = tile_lo; tile <= tile_hi; ++tile) {
-    const int buf = (tile - tile_lo) & 1;
-    const int k0 = tile * kBK;
-    const bool more = tile + 1 <= tile_hi;
-    if (more) fetch(k0 + kBK);
-
-    const bool wave_tile = wave_active && k0 <= wkey_hi && k0 + kBK - 1 >= wkey_lo;
-    if (wave_tile) {
-      // S^T = K Q^T over head_dim: all K fragments of the tile first
-      const __bf16* kbuf = klds[buf];
-      bf16x8 kf[2][KSTEPS];
-      for (int s = 0; s < KSTEPS; ++s)
-        for (int mt = 0; mt < 2; ++mt)
-          kf[mt][s] = *reinterpret_cast<const bf16x8*>(kbuf + (mt * 32 + krow_lane) * T::KS + s * 16 + half * 8);
-      f32x16 sacc[2][NT];
-      for (int mt = 0; mt < 2; ++mt)
-        for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = f32x16{};
-      for (int s = 0; s < KSTEPS; ++s)
-        for (int mt = 0; mt < 2; ++mt)
-          for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = mfma32(kf[mt][s], qf[nt][s], sacc[mt][nt]);
-
-      // mask only tiles cut by the causal / window / length bounds
-      const bool need_mask = (k0 + kBK - 1 > wpos_first) || (W >= 0 && k0 < wpos_last - W) ||
-                             (k0 + kBK > kv_len);
-      float mx[NT];
-      for (int nt = 0; nt < NT; ++nt) {
-        float m = kNegInf;
-        if (need_mask) {
-          const int base = k0 + 8 * half;
-          const int hi = (pos[nt] < kv_len - 1 ? pos[nt] : kv_len - 1) - base;
-          const int lo = (W >= 0 ? pos[nt] - W : -0x40000000) - base;
-          for (int mt = 0; mt < 2; ++mt)
-            for (int v = 0; v < 16; ++v) {
-              const int off = mt * 32 + 16 * (v >> 3) + (v & 7);
-              const bool ok = off <= hi && off >= lo;
-              sacc[mt][nt][v] = ok ? sacc[mt][nt][v] : kNegInf;
-            }
-        }
-        for (int mt = 0; mt < 2; ++mt)
-          for (int v = 0; v < 16; ++v) m = fmaxf(m, sacc[mt][nt][v]);
-        mx[nt] = fmaxf(m, __shfl_xor(m, 32));
-      }
-
-      // lazy rescale of the running maximum (log2 domain)
-      bool need[NT];
-      float mtile[NT];
-      bool any = false;
-      for (int nt = 0; nt < NT; ++nt) {
-        mtile[nt] = mx[nt] * c;   // -inf stays -inf (c > 0)
-        need[nt] = mtile[nt] > m_run[nt] + kRescaleThreshold;
-        any = any || need[nt];
-      }
-      if (__ballot(any) != 0ull) {
-        for (int nt = 0; nt < NT; ++nt) {
-          const float m_new = need[nt] ? mtile[nt] : m_run[nt];
-          const float alpha = need[nt] ? __builtin_amdgcn_exp2f(m_run[nt] - m_new) : 1.f;
-          m_run[nt] = m_new;
-          l_part[nt] *= alpha;
-          for (int md = 0; md < MD; ++md) oacc[nt][md] *= alpha;
-        }
-      }
-
-      // P = exp2(c s - m) (masked logits give exp2(-inf) = 0), row partial
-      // sums, bf16 B operands of O^T += V^T P^T
-      bf16x8 pb[NT][4];
-      for (int nt = 0; nt < NT; ++nt) {
-        const float mb = m_run[nt] == kNegInf ? 0.f : m_run[nt];
-        float sum = 0.f;
-        for (int mt = 0; mt < 2; ++mt) {
-          float p[16];
-          for (int v = 0; v < 16; ++v) {
-            p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][nt][v], c, -mb));
-            sum += p[v];
-          }
-          for (int sh = 0; sh < 2; ++sh) {
-            u32x4 w;
-            for (int e = 0; e < 4; ++e) w[e] = pack_bf16(p[8 * sh + 2 * e], p[8 * sh + 2 * e + 1]);
-            pb[nt][2 * mt + sh] = __builtin_bit_cast(bf16x8, w);
-          }
-        }
-        l_part[nt] += sum;
-      }
-
-      // O^T += V^T P^T: all V fragments of the tile first
-      // lane (col, half) reads dims md*32 + col, keys 16 ks + 8 half .. + 7; in
-      // the swizzled layout that key chunk is 2 (ks ^ md) + (half ^ (col >> 4))
-      const __bf16* vbuf = vlds[buf] + vrow_base;
-      bf16x8 vf[MD][4];
-      for (int ks = 0; ks < 4; ++ks)
-        for (int md = 0; md < MD; ++md)
-          vf[md][ks] = *reinterpret_cast<const bf16x8*>(vbuf + md * 32 * T::VS + ((ks ^ md) & 3) * 16);
-      for (int ks = 0; ks < 4; ++ks)
-        for (int md = 0; md < MD; ++md)
-          for (int nt = 0; nt < NT; ++nt) oacc[nt][md] = mfma32(vf[md][ks], pb[nt][ks], oacc[nt][md]);
-    }
-
-    if (more) store(buf ^ 1);
+    const int lo = tile_lo, hi = tile_hi;
+    stage_fetch(lo, page_of(lo));
+    if (lo + 1 <= hi) id_next = page_of(lo + 1);
+    stage_store(lo);
     __syncthreads();
+    for (int j = lo; j <= hi; ++j) {
+      const bool more = j + 1 <= hi;
+      if (more) {
+        stage_fetch(j + 1, id_next);
+        if (j + 2 <= hi) id_next = page_of(j + 2);
+      }
+      if (wave_tile(j)) {
+        gemm_s(j);
+        softmax(j);
+        gemm_pv(j);
+      }
+      if (more) stage_store(j + 1);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue -------------------------------------------------------------
   if (!wave_active) return;
-  for (int nt = 0; nt < NT; ++nt) {
-    float l = l_part[nt] + __shfl_xor(l_part[nt], 32);
-    if (!rvalid[nt]) continue;
-    const int h = h0 + hd[nt];
-    const float mb = m_run[nt] == kNegInf ? 0.f : m_run[nt];
-    if (a.sinks) l += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - mb);
-    const float inv = bmm2 / l;
-    uint16_t* orow = a.out + static_cast<int64_t>(q0 + t0 + tok[nt]) * a.o_tok +
-                     static_cast<int64_t>(h) * a.o_head;
-    for (int md = 0; md < MD; ++md) {
-      for (int g = 0; g < 4; ++g) {
-        const int d = md * 32 + 8 * g + 4 * half;
-        const u32x2 w = u32x2{pack_bf16(oacc[nt][md][4 * g] * inv, oacc[nt][md][4 * g + 1] * inv),
-                              pack_bf16(oacc[nt][md][4 * g + 2] * inv, oacc[nt][md][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d) = w;
-      }
+  float l = l_part + __shfl_xor(l_part, 32);
+  if (!rvalid) return;
+  const int h = h0 + hd;
+  const float mb = m_run == kNegInf ? 0.f : m_run;
+  if (a.sinks) l += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - mb);
+  const float inv = bmm2 / l;
+  uint16_t* orow = a.out + static_cast<int64_t>(q0 + t0 + tok) * a.o_tok + static_cast<int64_t>(h) * a.o_head;
+  for (int md = 0; md < MD; ++md) {
+    for (int g = 0; g < 4; ++g) {
+      const int d = md * 32 + 8 * g + 4 * half;
+      const u32x2 w = u32x2{pack_bf16(oacc[md][4 * g] * inv, oacc[md][4 * g + 1] * inv),
+                            pack_bf16(oacc[md][4 * g + 2] * inv, oacc[md][4 * g + 3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + d) = w;
     }
   }
 }
@@ -590,30 +561,13 @@ int log2_exact(int x) {
   return s;
 }
 
-// Kernel shape: 8 waves x 32 rows (two waves per SIMD) unless PPA_WAVES=4
-// asks for 4 waves x 64 rows (one wave per SIMD).  UPAGE: page_size >= 16.
-template <int D, bool FP8, bool UPAGE>
-hipError_t launch_shape(const AttnArgs& a, int grid, hipStream_t stream, int waves) {
-  if (waves == 4) {
-    hipLaunchKernelGGL((paged_prefill_kernel<D, FP8, 2, 4, UPAGE>), dim3(grid), dim3(256), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((paged_prefill_kernel<D, FP8, 1, 8, UPAGE>), dim3(grid), dim3(512), 0, stream, a);
-  }
-  return hipGetLastError();
-}
-
 template <int D, bool FP8>
-hipError_t launch(const AttnArgs& a, int grid, hipStream_t stream, int waves, bool upage) {
-  return upage ? launch_shape<D, FP8, true>(a, grid, stream, waves)
-               : launch_shape<D, FP8, false>(a, grid, stream, waves);
-}
-
-int waves_setting() {
-  static int w = [] {
-    const char* s = getenv("PPA_WAVES");
-    return (s != nullptr && atoi(s) == 4) ? 4 : 8;
-  }();
-  return w;
+hipError_t launch(const AttnArgs& a, int grid, hipStream_t stream, bool upage) {
+  if (upage)
+    hipLaunchKernelGGL((paged_prefill_kernel<D, FP8, true>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL((paged_prefill_kernel<D, FP8, false>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -665,21 +619,20 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   const bool fp8 = p->kv_dtype == PPA_DTYPE_FP8_E4M3FN;
-  const int w = waves_setting();
   const int g = static_cast<int>(grid);
-  // uniform-page staging needs pages of >= 16 tokens whose byte extent fits
+  // uniform-page staging needs pages of >= 8 tokens whose byte extent fits
   // the 32-bit in-page offsets
   const int eb = fp8 ? 1 : 2;
   auto extent = [&](const PagedPlane& pl) {
     return (static_cast<int64_t>(p->page_size) * pl.tok_stride +
             static_cast<int64_t>(p->num_kv_heads) * pl.head_stride + p->head_dim) * eb;
   };
-  const bool upage = p->page_size >= 16 && extent(a.k) < (int64_t{1} << 31) &&
+  const bool upage = p->page_size >= 8 && extent(a.k) < (int64_t{1} << 31) &&
                      extent(a.v) < (int64_t{1} << 31);
   if (p->head_dim == 128)
-    e = fp8 ? launch<128, true>(a, g, s, w, upage) : launch<128, false>(a, g, s, w, upage);
+    e = fp8 ? launch<128, true>(a, g, s, upage) : launch<128, false>(a, g, s, upage);
   else
-    e = fp8 ? launch<64, true>(a, g, s, w, upage) : launch<64, false>(a, g, s, w, upage);
+    e = fp8 ? launch<64, true>(a, g, s, upage) : launch<64, false>(a, g, s, upage);
   return e == hipSuccess ? PPA_OK : PPA_ERR_HIP;
 }
 

@@ -44,6 +44,20 @@ __device__ __forceinline__ int page_id(const PageTable& pt, int token) {
   return id;
 }
 
+// The same lookup for a key that is uniform across the wave: the table is
+// read through the constant address space, so the load is a scalar one whose
+// result does not wait behind the wave's outstanding vector loads.
+__device__ __forceinline__ int page_id_uniform(const PageTable& pt, int token) {
+  int col = token >> pt.page_shift;
+  col = col < pt.cols - 1 ? col : pt.cols - 1;
+  const __attribute__((address_space(4))) int32_t* row =
+      (const __attribute__((address_space(4))) int32_t*)(pt.row);
+  int id = row[col];
+  id = id < 0 ? 0 : id;
+  id = id < pt.num_pages ? id : pt.num_pages - 1;
+  return id;
+}
+
 // Byte address of element `elem` of token `token` (page `id`) for kv head hk.
 template <int ELEM_BYTES>
 __device__ __forceinline__ const uint8_t* token_row(const PagedPlane& pl, int id, int page_mask,

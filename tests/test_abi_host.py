@@ -1,0 +1,287 @@
+"""Host-side checks of the C-ABI library (no GPU, no compute calls).
+
+* the shared library loads and exports every function that include/ppa.h
+  declares, with the ABI version and struct size the binding expects;
+* every rejection of the shape validator and of the host metadata validator
+  is forced from the host, each with its own status code (the API page's
+  argument list fixes what each array means; lengths, tables and window
+  bounds follow from the definition of the causal paged prefill).
+
+The validators read no device memory, so CPU tensors stand in for device
+buffers here: only their shapes, strides and base pointers are used.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ppa.h")
+
+ppa = pytest.importorskip("paged_kv_prefill_varlen_amd")
+from paged_kv_prefill_varlen_amd import binding as B  # noqa: E402
+
+OK = 0
+
+
+def _header_text() -> str:
+    with open(HEADER) as f:
+        return f.read()
+
+
+def _status_codes() -> dict:
+    codes = {}
+    for name, val in re.findall(r"\b(PPA_(?:OK|ERR_[A-Z_]+))\s*=\s*(-?\d+)", _header_text()):
+        codes[name] = int(val)
+    return codes
+
+
+ERR = _status_codes()  # the ppa_status enum, read back from the header
+
+
+def _declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(ppa_[a-z0-9_]+)\s*\(", text)))
+
+
+# --------------------------------------------------------------------------
+# the library and its exports
+# --------------------------------------------------------------------------
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for need in ("ppa_paged_prefill_attention", "ppa_validate_shapes", "ppa_validate_metadata_host",
+                 "ppa_workspace_bytes", "ppa_strerror", "ppa_gather_paged_kv"):
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.library_path())
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_abi_version_and_struct_size():
+    assert B.ppa_abi_version() == B.PPA_ABI_VERSION
+    assert B.ppa_params_size() == ctypes.sizeof(B.PpaParams)
+    m = re.search(r"#define\s+PPA_ABI_VERSION\s+(\d+)", _header_text())
+    assert m and int(m.group(1)) == B.PPA_ABI_VERSION
+
+
+def test_strerror_covers_every_status():
+    seen = set()
+    for name, code in ERR.items():
+        s = B.ppa_strerror(code)
+        assert s and s not in seen, (name, s)
+        seen.add(s)
+    assert "unknown" in B.ppa_strerror(-999).lower()
+
+
+# --------------------------------------------------------------------------
+# a valid host-side description, then one defect at a time
+# --------------------------------------------------------------------------
+
+def _case(D=64, Hq=4, Hkv=2, P=16, pages=8, layout="HND", combined=False, kv_dtype=torch.bfloat16,
+          q_lens=(5, 0, 9), prefix=(3, 4, 0)):
+    kv_lens = [q + p for q, p in zip(q_lens, prefix)]
+    T = sum(q_lens)
+    cols = max(1, max((k + P - 1) // P for k in kv_lens))
+    q = torch.zeros(T, Hq, D, dtype=torch.bfloat16)
+    shape = (pages, Hkv, P, D) if layout == "HND" else (pages, P, Hkv, D)
+    if combined:
+        kv = torch.zeros(pages, 2, *shape[1:], dtype=kv_dtype)
+    else:
+        kv = (torch.zeros(shape, dtype=kv_dtype), torch.zeros(shape, dtype=kv_dtype))
+    bt = torch.zeros(len(q_lens), cols, dtype=torch.int32)
+    for b, k in enumerate(kv_lens):
+        for j in range((k + P - 1) // P):
+            bt[b, j] = (b * 3 + j) % pages
+    sl = torch.tensor(kv_lens, dtype=torch.int32)
+    cuq = torch.tensor([0] + list(torch.tensor(q_lens).cumsum(0).tolist()), dtype=torch.int32)
+    cukv = torch.tensor([0] + list(torch.tensor(kv_lens).cumsum(0).tolist()), dtype=torch.int32)
+    out = torch.empty_like(q)
+    c = dict(q=q, kv=kv, bt=bt, sl=sl, cuq=cuq, cukv=cukv, out=out, layout=layout,
+             max_q=max(q_lens), max_kv=max(kv_lens), B=len(q_lens), sinks=None, W=-1)
+    return c
+
+
+def _params(c, **over):
+    p = B.make_params(c["q"], c["kv"], None, c["bt"], c["sl"], c["max_q"], c["max_kv"], 0.125, 1.0, c["B"],
+                      c["cuq"], c["cukv"], c["W"], c["out"], c["layout"], c["sinks"])
+    for k, v in over.items():
+        if isinstance(getattr(p, k), ctypes.Array):
+            getattr(p, k)[:] = v
+        else:
+            setattr(p, k, v)
+    return p
+
+
+def _shapes(p):
+    return B.ppa_validate_shapes(p)
+
+
+def _meta(p, c, **arrays):
+    a = dict(cuq=c["cuq"], cukv=c["cukv"], sl=c["sl"], bt=c["bt"])
+    a.update(arrays)
+    return B.ppa_validate_metadata_host(p, a["cuq"], a["cukv"], a["sl"], a["bt"])
+
+
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+@pytest.mark.parametrize("combined", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_valid_descriptions_pass(layout, combined, D):
+    c = _case(D=D, layout=layout, combined=combined)
+    p = _params(c)
+    assert _shapes(p) == (OK, "")
+    assert _meta(p, c)[0] == OK
+    assert B.ppa_workspace_bytes(p) == 0
+
+
+def test_fp8_kv_and_sinks_pass():
+    c = _case(kv_dtype=torch.float8_e4m3fn)
+    c["sinks"] = torch.zeros(4, dtype=torch.float32)
+    c["W"] = 0
+    p = _params(c)
+    assert _shapes(p)[0] == OK
+
+
+SHAPE_DEFECTS = [
+    # (name, overrides of ppa_params, expected status)
+    ("abi version", dict(abi_version=99), "PPA_ERR_ABI"),
+    ("struct size", dict(struct_size=8), "PPA_ERR_ABI"),
+    ("query fp32", dict(query_dtype=B.PPA_DTYPE_FP32), "PPA_ERR_DTYPE"),
+    ("out fp8", dict(out_dtype=B.PPA_DTYPE_FP8_E4M3FN), "PPA_ERR_DTYPE"),
+    ("kv fp32", dict(kv_dtype=B.PPA_DTYPE_FP32), "PPA_ERR_DTYPE"),
+    ("kv dtype 0", dict(kv_dtype=0), "PPA_ERR_DTYPE"),
+    ("layout 2", dict(kv_layout=2), "PPA_ERR_LAYOUT"),
+    ("form 5", dict(kv_form=5), "PPA_ERR_LAYOUT"),
+    ("negative tokens", dict(num_tokens=-1), "PPA_ERR_SHAPE"),
+    ("negative batch", dict(batch_size=-2), "PPA_ERR_SHAPE"),
+    ("heads not multiple", dict(num_qo_heads=3), "PPA_ERR_HEADS"),
+    ("zero kv heads", dict(num_kv_heads=0), "PPA_ERR_HEADS"),
+    ("head_dim 96", dict(head_dim=96), "PPA_ERR_HEAD_DIM"),
+    ("page 24", dict(page_size=24), "PPA_ERR_PAGE_SIZE"),
+    ("page 0", dict(page_size=0), "PPA_ERR_PAGE_SIZE"),
+    ("window -2", dict(window_left=-2), "PPA_ERR_WINDOW"),
+    ("max_q > max_kv", dict(max_q_len=100), "PPA_ERR_LENGTHS"),
+    ("table too narrow", dict(block_tables_cols=0), "PPA_ERR_TABLE"),
+    ("table row stride", dict(block_tables_row_stride=0), "PPA_ERR_STRIDE"),
+    ("null query", dict(query=None), "PPA_ERR_NULL_POINTER"),
+    ("null out", dict(out=None), "PPA_ERR_NULL_POINTER"),
+    ("null k", dict(k_cache=None), "PPA_ERR_NULL_POINTER"),
+    ("null seq_lens", dict(seq_lens=None), "PPA_ERR_NULL_POINTER"),
+    ("null cu_q", dict(cum_seq_lens_q=None), "PPA_ERR_NULL_POINTER"),
+    ("null table", dict(block_tables=None), "PPA_ERR_NULL_POINTER"),
+    ("query inner stride", dict(query_strides=[256, 64, 2]), "PPA_ERR_STRIDE"),
+    ("out inner stride", dict(out_strides=[256, 64, 2]), "PPA_ERR_STRIDE"),
+    ("query row not 16B", dict(query_strides=[257, 64, 1]), "PPA_ERR_STRIDE"),
+    ("k inner stride", dict(k_cache_strides=[2048, 1024, 64, 2]), "PPA_ERR_STRIDE"),
+    ("v token stride not 16B", dict(v_cache_strides=[2048, 1024, 63, 1]), "PPA_ERR_STRIDE"),
+]
+
+
+@pytest.mark.parametrize("name,over,expect", SHAPE_DEFECTS, ids=[d[0] for d in SHAPE_DEFECTS])
+def test_shape_validator_rejects(name, over, expect):
+    c = _case()
+    p = _params(c, **over)
+    st, msg = _shapes(p)
+    assert st == ERR[expect], (st, msg)
+    assert msg, "a rejection carries a message"
+
+
+def test_shape_validator_rejects_null_params():
+    buf = ctypes.create_string_buffer(128)
+    lib = ctypes.CDLL(B.library_path())
+    lib.ppa_validate_shapes.restype = ctypes.c_int32
+    assert lib.ppa_validate_shapes(None, buf, len(buf)) == ERR["PPA_ERR_NULL_POINTER"]
+
+
+def test_combined_cache_defects():
+    c = _case(combined=True)
+    assert _shapes(_params(c, kv_planes=3))[0] == ERR["PPA_ERR_LAYOUT"]
+    assert _shapes(_params(c, kv_planes=0))[0] == ERR["PPA_ERR_LAYOUT"]
+    assert _shapes(_params(c, kv_cache=None))[0] == ERR["PPA_ERR_NULL_POINTER"]
+    # a plane stride that is not a 16-byte multiple
+    s = list(c["kv"].stride())
+    s[1] = 7
+    assert _shapes(_params(c, kv_cache_strides=s))[0] == ERR["PPA_ERR_STRIDE"]
+
+
+def test_misaligned_pointers():
+    c = _case()
+    p = _params(c)
+    assert _shapes(_params(c, query=p.query + 2))[0] in (ERR["PPA_ERR_ALIGNMENT"],)
+    assert _shapes(_params(c, k_cache=p.k_cache + 8))[0] == ERR["PPA_ERR_ALIGNMENT"]
+    # sinks are fp32: 4-byte alignment is enough, 2 is not
+    c["sinks"] = torch.zeros(5, dtype=torch.float32)[1:]
+    p = _params(c)
+    assert _shapes(p)[0] == OK
+    assert _shapes(_params(c, sinks=p.sinks + 2))[0] == ERR["PPA_ERR_ALIGNMENT"]
+
+
+def test_zero_pages_with_nonzero_kv():
+    c = _case()
+    assert _shapes(_params(c, num_pages=0))[0] == ERR["PPA_ERR_SHAPE"]
+
+
+def test_empty_batch_is_valid():
+    c = _case()
+    p = _params(c, batch_size=0, max_q_len=0, max_kv_len=0)
+    assert _shapes(p)[0] == OK
+    assert _meta(p, c, cuq=torch.zeros(1, dtype=torch.int32), cukv=torch.zeros(1, dtype=torch.int32))[0] == OK
+
+
+def _i(xs):
+    return torch.tensor(xs, dtype=torch.int32)
+
+
+def test_metadata_validator_rejects():
+    c = _case()  # q_lens (5, 0, 9), kv_lens (8, 4, 9), P 16, 8 pages
+    p = _params(c)
+    E = ERR
+    # cum_seq_lens_q must start at 0, never decrease, and end within num_tokens
+    assert _meta(p, c, cuq=_i([1, 6, 6, 15]))[0] == E["PPA_ERR_METADATA"]
+    assert _meta(p, c, cuq=_i([0, 6, 5, 14]))[0] == E["PPA_ERR_METADATA"]
+    assert _meta(_params(c, num_tokens=13), c)[0] == E["PPA_ERR_METADATA"]
+    # cum_seq_lens_kv must be the running sum of seq_lens
+    assert _meta(p, c, cukv=_i([0, 8, 13, 21]))[0] == E["PPA_ERR_METADATA"]
+    assert _meta(p, c, cukv=_i([2, 10, 14, 23]))[0] == E["PPA_ERR_METADATA"]
+    # q_len > kv_len leaves an empty causal span: rejected
+    assert _meta(p, c, sl=_i([4, 4, 9]), cukv=_i([0, 4, 8, 17]))[0] == E["PPA_ERR_LENGTHS"]
+    # negative kv length
+    assert _meta(p, c, sl=_i([8, -1, 9]), cukv=_i([0, 8, 7, 16]))[0] == E["PPA_ERR_LENGTHS"]
+    # q_len above max_q_len, kv_len above max_kv_len
+    assert _meta(_params(c, max_q_len=8), c)[0] == E["PPA_ERR_LENGTHS"]
+    assert _meta(_params(c, max_kv_len=8), c)[0] == E["PPA_ERR_LENGTHS"]
+    # a page id out of range, negative, or a table narrower than a request needs
+    bt = c["bt"].clone()
+    bt[2, 0] = 8
+    assert _meta(p, c, bt=bt)[0] == E["PPA_ERR_TABLE"]
+    bt[2, 0] = -1
+    assert _meta(p, c, bt=bt)[0] == E["PPA_ERR_TABLE"]
+    c2 = _case(q_lens=(5, 0, 20), prefix=(3, 4, 0))  # request 2 needs 2 pages of 16
+    p2 = _params(c2, block_tables_cols=1, block_tables_row_stride=1)
+    assert _meta(p2, c2, bt=c2["bt"][:, :1].contiguous())[0] == E["PPA_ERR_TABLE"]
+    # missing host arrays
+    assert _meta(p, c, cuq=None)[0] == E["PPA_ERR_NULL_POINTER"]
+
+
+def test_metadata_ignores_columns_past_a_request():
+    # columns past ceil(kv_len / P) are never read: garbage there is accepted
+    c = _case(q_lens=(5, 0, 20), prefix=(3, 4, 0))
+    bt = c["bt"].clone()
+    bt[0, 1] = -7
+    bt[1, 1] = 10 ** 6
+    assert _meta(_params(c), c, bt=bt)[0] == OK
+
+
+def test_cum_seq_lens_kv_optional():
+    c = _case()
+    c["cukv"] = None
+    p = _params(c)
+    assert _shapes(p)[0] == OK
+    assert _meta(p, c, cukv=None)[0] == OK

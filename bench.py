@@ -176,7 +176,9 @@ def main():
     cukv = case["cum_seq_lens_kv"].to(dev)
     sinks = None if case["sinks"] is None else case["sinks"].to(dev)
     out = torch.empty_like(q)
-    p = ppa.make_params(q, kv, None, bt, sl, case["max_q_len"], case["max_kv_len"], case["bmm1_scale"],
+    # zeroed scheduler workspace: persistent workgroups pull balanced work
+    workspace = torch.zeros(ppa.WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    p = ppa.make_params(q, kv, workspace, bt, sl, case["max_q_len"], case["max_kv_len"], case["bmm1_scale"],
                         case["bmm2_scale"], case["batch_size"], cuq, cukv, case["window_left"], out,
                         case["kv_layout"], sinks)
     st, msg = ppa.ppa_validate_metadata_host(p, case["cum_seq_lens_q"], case["cum_seq_lens_kv"],

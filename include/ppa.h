@@ -125,9 +125,14 @@ typedef struct ppa_params {
   int64_t k_cache_strides[4];
   int64_t v_cache_strides[4];
 
-  /* Scratch owned by the caller; must hold ppa_workspace_bytes() bytes and be
-     zero on first use (API page, parameter workspace_buffer).  The library
-     leaves it as it found it. */
+  /* Scratch owned by the caller (API page, parameter workspace_buffer).
+     Optional.  When not NULL it must hold at least ppa_workspace_bytes()
+     bytes, be 16-byte aligned and be ZERO before its first use; every call
+     leaves it zero again.  It holds the work counters of the balanced
+     schedule: persistent workgroups pull work items from it, so no compute
+     unit idles while work remains.  Calls that share one workspace must not
+     run at the same time (enqueue them on one stream).  When NULL, a plain
+     one-workgroup-per-item grid is launched instead. */
   void* workspace;
   size_t workspace_bytes;
 
@@ -185,7 +190,7 @@ const char* ppa_strerror(int32_t status);
  * device memory: pointers, dtypes, enums, head counts, head_dim, page size,
  * window, strides and alignment, block-table width >= ceil(max_kv_len /
  * page_size) (the table-width rule of the article's TrtllmAttentionMetadata
- * section), workspace size.  Cheap; ppa_paged_prefill_attention runs it on
+ * section), workspace size and alignment.  Cheap; ppa_paged_prefill_attention runs it on
  * every call.
  */
 int32_t ppa_validate_shapes(const ppa_params* p, char* msg, size_t msg_len);
@@ -204,7 +209,8 @@ int32_t ppa_validate_metadata_host(const ppa_params* p, const int32_t* cum_seq_l
                                    const int32_t* cum_seq_lens_kv, const int32_t* seq_lens,
                                    const int32_t* block_tables, char* msg, size_t msg_len);
 
-/* Bytes of workspace a call with these arguments needs (0 at present). */
+/* Bytes of workspace the balanced schedule uses (a small constant; p may be
+   NULL). */
 size_t ppa_workspace_bytes(const ppa_params* p);
 
 /*

@@ -166,8 +166,12 @@ def ppa_validate_metadata_host(params: PpaParams, cum_seq_lens_q, cum_seq_lens_k
     return int(st), buf.value.decode()
 
 
-def ppa_workspace_bytes(params: PpaParams) -> int:
-    return int(_lib.ppa_workspace_bytes(ctypes.byref(params)))
+def ppa_workspace_bytes(params: Optional[PpaParams] = None) -> int:
+    return int(_lib.ppa_workspace_bytes(None if params is None else ctypes.byref(params)))
+
+
+# bytes of the optional scheduler workspace (the same for every call)
+WORKSPACE_BYTES = ppa_workspace_bytes()
 
 
 def _stream_handle(device: torch.device, stream) -> int:

@@ -65,6 +65,11 @@ constexpr float kRescaleThreshold = 8.0f;   // log2 units
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kMinScale = 1.17549435e-38f;  // FLT_MIN
 
+// Scheduler counters in the workspace: kSchedQueues queue heads, then the
+// number of workgroups that have finished.
+constexpr int kSchedQueues = 8;
+constexpr int kSchedDone = kSchedQueues;
+
 struct AttnArgs {
   const uint16_t* q;
   int64_t q_tok, q_head;
@@ -91,6 +96,9 @@ struct AttnArgs {
   const float* bmm1_ptr;
   const float* bmm2_ptr;
   const float* sinks;
+  uint32_t* sched;     // persistent schedule: counters in the workspace
+  int32_t n_items;     // n_qt * batch * num_kv_heads * n_hg
+  int32_t n_queues;    // 1 or kSchedQueues
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -278,11 +286,12 @@ __device__ __forceinline__ void store_kv(const uint32_t* kraw, const uint32_t* v
   }
 }
 
-// Per tile: stage tile j+1 into registers, run S, softmax and PV for tile j
-// from LDS, store tile j+1 into the other LDS buffer, barrier.
+// One work item: `item` = (query tile, request, kv head, head group), counted
+// heaviest query tile first.  Per K/V tile: stage tile j+1 into registers, run
+// S, softmax and PV for tile j from LDS, store tile j+1 into the other LDS
+// buffer, barrier.  Every wave of the workgroup calls this with the same item.
 template <int D, bool FP8, bool UPAGE>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void paged_prefill_kernel(AttnArgs a) {
+__device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   using T = Tile<D, FP8>;
   constexpr int KSTEPS = D / 16;   // MFMA K-steps over head_dim
   constexpr int MD = D / 32;       // 32-wide head_dim tiles of O^T
@@ -291,9 +300,8 @@ void paged_prefill_kernel(AttnArgs a) {
 
   // ---- which work item --------------------------------------------------
   const int R = a.batch * a.num_kv_heads * a.n_hg;
-  const int L = blockIdx.x;
-  const int qt = a.n_qt - 1 - L / R;
-  const int rest = L % R;
+  const int qt = a.n_qt - 1 - item / R;
+  const int rest = item % R;
   const int b = rest / (a.num_kv_heads * a.n_hg);
   const int hk = (rest / a.n_hg) % a.num_kv_heads;
   const int hg = rest % a.n_hg;
@@ -509,6 +517,42 @@ void paged_prefill_kernel(AttnArgs a) {
   }
 }
 
+// One workgroup per work item, in heaviest-first order.
+template <int D, bool FP8, bool UPAGE>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void paged_prefill_kernel(AttnArgs a) {
+  attend_item<D, FP8, UPAGE>(a, blockIdx.x);
+}
+
+// Persistent workgroups (as many as fit on the device at once) pull work
+// items from counters in the caller's workspace, so a workgroup that finishes
+// early takes the next heaviest item instead of idling behind the hardware's
+// fixed block-to-engine dealing.  With n_queues = 8, queue x holds the items
+// whose index is x mod 8 (all tiles of a fixed set of (request, kv head)
+// pairs) and is served by the workgroups with blockIdx % 8 == x, which the
+// dispatcher places on one XCD, so that K/V stays in one L2.  The last
+// workgroup to finish returns every counter to zero for the next call.
+template <int D, bool FP8, bool UPAGE>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void paged_prefill_persistent(AttnArgs a) {
+  __shared__ uint32_t next_item[2];
+  const uint32_t nq = static_cast<uint32_t>(a.n_queues);
+  const uint32_t queue = blockIdx.x % nq;
+  uint32_t* sched = a.sched;
+  for (uint32_t round = 0;; ++round) {
+    // two slots: a slow wave may still read the previous round's value
+    if (threadIdx.x == 0) next_item[round & 1] = atomicAdd(sched + queue, 1u);
+    __syncthreads();
+    const uint64_t item = static_cast<uint64_t>(next_item[round & 1]) * nq + queue;
+    if (item >= static_cast<uint64_t>(a.n_items)) break;
+    attend_item<D, FP8, UPAGE>(a, static_cast<int>(item));
+  }
+  if (threadIdx.x == 0 && atomicAdd(sched + kSchedDone, 1u) == gridDim.x - 1) {
+    // every workgroup has made its last fetch: no counter is read again
+    for (int i = 0; i <= kSchedDone; ++i) atomicExch(sched + i, 0u);
+  }
+}
+
 // ---- address-unit check: paged K or V -> contiguous [tokens, H_kv, D] ------
 struct GatherArgs {
   PagedPlane plane;
@@ -561,13 +605,45 @@ int log2_exact(int x) {
   return s;
 }
 
-template <int D, bool FP8>
-hipError_t launch(const AttnArgs& a, int grid, hipStream_t stream, bool upage) {
-  if (upage)
-    hipLaunchKernelGGL((paged_prefill_kernel<D, FP8, true>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
-  else
-    hipLaunchKernelGGL((paged_prefill_kernel<D, FP8, false>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
+// Workgroups of a persistent kernel that the device holds at once (cached per
+// device and kernel).
+template <int D, bool FP8, bool UPAGE>
+int resident_workgroups() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] > 0) return cache[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, paged_prefill_persistent<D, FP8, UPAGE>,
+                                                   64 * kWaves, 0) != hipSuccess)
+    return 0;
+  cache[dev] = cus * (per_cu > 0 ? per_cu : 1);
+  return cache[dev];
+}
+
+template <int D, bool FP8, bool UPAGE>
+hipError_t launch_variant(AttnArgs a, int items, hipStream_t stream) {
+  const int resident = a.sched ? resident_workgroups<D, FP8, UPAGE>() : 0;
+  if (resident <= 0) {
+    hipLaunchKernelGGL((paged_prefill_kernel<D, FP8, UPAGE>), dim3(items), dim3(64 * kWaves), 0, stream, a);
+    return hipGetLastError();
+  }
+  const int R = a.batch * a.num_kv_heads * a.n_hg;
+  int grid = resident < items ? resident : items;
+  a.n_queues = 1;
+  if (R % kSchedQueues == 0 && grid >= kSchedQueues) {
+    grid -= grid % kSchedQueues;
+    a.n_queues = kSchedQueues;
+  }
+  a.n_items = items;
+  hipLaunchKernelGGL((paged_prefill_persistent<D, FP8, UPAGE>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D, bool FP8>
+hipError_t launch(const AttnArgs& a, int items, hipStream_t stream, bool upage) {
+  return upage ? launch_variant<D, FP8, true>(a, items, stream) : launch_variant<D, FP8, false>(a, items, stream);
 }
 
 }  // namespace
@@ -613,6 +689,7 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
   a.bmm1_ptr = p->bmm1_scale_ptr;
   a.bmm2_ptr = p->bmm2_scale_ptr;
   a.sinks = p->sinks;
+  a.sched = static_cast<uint32_t*>(p->workspace);
 
   const int64_t grid = static_cast<int64_t>(a.n_qt) * a.batch * a.num_kv_heads * a.n_hg;
   if (grid > 0x7fffffff) return PPA_ERR_SHAPE;

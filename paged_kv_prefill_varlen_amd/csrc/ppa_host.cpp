@@ -124,7 +124,7 @@ const char* ppa_strerror(int32_t status) {
 
 size_t ppa_workspace_bytes(const ppa_params* p) {
   (void)p;
-  return 0;
+  return 256;   // scheduler counters (9 x uint32), rounded up
 }
 
 int32_t ppa_validate_shapes(const ppa_params* p, char* msg, size_t msg_len) {
@@ -220,10 +220,10 @@ int32_t ppa_validate_shapes(const ppa_params* p, char* msg, size_t msg_len) {
   if ((reinterpret_cast<uintptr_t>(p->sinks) & 3u) != 0)
     return fail(PPA_ERR_ALIGNMENT, msg, msg_len, "sinks");
 
-  if (p->workspace_bytes < ppa_workspace_bytes(p) ||
-      (ppa_workspace_bytes(p) > 0 && p->workspace == nullptr))
+  if (p->workspace != nullptr && p->workspace_bytes < ppa_workspace_bytes(p))
     return fail(PPA_ERR_WORKSPACE, msg, msg_len, "workspace of %zu bytes, need %zu",
                 p->workspace_bytes, ppa_workspace_bytes(p));
+  if (!aligned16(p->workspace)) return fail(PPA_ERR_ALIGNMENT, msg, msg_len, "workspace");
   return PPA_OK;
 }
 

@@ -24,13 +24,31 @@ def to_device(case: dict, device="cuda") -> dict:
     return d
 
 
+_WORKSPACES = {}
+
+
+def workspace(device="cuda") -> torch.Tensor:
+    """One zeroed scheduler workspace per device, shared by every call (each
+    call leaves it zero again; calls run one after another on one stream)."""
+    import paged_kv_prefill_varlen_amd as ppa
+    dev = torch.device(device)
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    if key not in _WORKSPACES:
+        _WORKSPACES[key] = torch.zeros(ppa.WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    return _WORKSPACES[key]
+
+
 def run_gpu(dcase: dict, out: torch.Tensor = None, bmm1=None, bmm2=None, stream=None,
-            validate=True) -> torch.Tensor:
+            validate=True, schedule="persistent") -> torch.Tensor:
+    """schedule: "persistent" (workspace given: balanced persistent workgroups)
+    or "grid" (no workspace: one workgroup per work item)."""
     import paged_kv_prefill_varlen_amd as ppa
     if out is None:
         out = torch.empty_like(dcase["query"]).view(torch.int16).fill_(GUARD).view(torch.bfloat16)
+    ws = workspace(dcase["query"].device) if schedule == "persistent" else None
+    assert schedule in ("persistent", "grid")
     ppa.batch_context_with_kv_cache(
-        dcase["query"], dcase["kv_cache"], None, dcase["block_tables"], dcase["seq_lens"],
+        dcase["query"], dcase["kv_cache"], ws, dcase["block_tables"], dcase["seq_lens"],
         dcase["max_q_len"], dcase["max_kv_len"],
         dcase["bmm1_scale"] if bmm1 is None else bmm1,
         dcase["bmm2_scale"] if bmm2 is None else bmm2,

@@ -138,7 +138,7 @@ def test_valid_descriptions_pass(layout, combined, D):
     p = _params(c)
     assert _shapes(p) == (OK, "")
     assert _meta(p, c)[0] == OK
-    assert B.ppa_workspace_bytes(p) == 0
+    assert B.ppa_workspace_bytes(p) == B.WORKSPACE_BYTES > 0
 
 
 def test_fp8_kv_and_sinks_pass():
@@ -285,3 +285,16 @@ def test_cum_seq_lens_kv_optional():
     p = _params(c)
     assert _shapes(p)[0] == OK
     assert _meta(p, c, cukv=None)[0] == OK
+
+
+def test_workspace_is_optional_but_checked_when_given():
+    c = _case()
+    ws = torch.zeros(B.WORKSPACE_BYTES + 64, dtype=torch.uint8)
+    p = _params(c)
+    assert _shapes(p)[0] == OK                       # no workspace: plain grid schedule
+    p = _params(c, workspace=ws.data_ptr(), workspace_bytes=B.WORKSPACE_BYTES)
+    assert _shapes(p)[0] == OK
+    p = _params(c, workspace=ws.data_ptr(), workspace_bytes=B.WORKSPACE_BYTES - 4)
+    assert _shapes(p)[0] == ERR["PPA_ERR_WORKSPACE"]
+    p = _params(c, workspace=ws.data_ptr() + 4, workspace_bytes=B.WORKSPACE_BYTES)
+    assert _shapes(p)[0] == ERR["PPA_ERR_ALIGNMENT"]

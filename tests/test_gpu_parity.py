@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (assert_close, errors, guard_rows_untouched, run_gpu, to_device)
+from gpu_helpers import (assert_close, errors, guard_rows_untouched, run_gpu, to_device, workspace)
 from oracle.case_io import decode_tensor, oracle_inputs, run_oracle, run_oracle_rows
 from workloads import make_case, make_custom_case
 from workloads.cases import relayout
@@ -122,11 +122,16 @@ def test_edge_case_parity(name):
                             **EDGE[name])
     _say("edge", name, case["q_lens"], case["kv_lens"])
     want, written = run_oracle(case)
-    out = run_gpu(to_device(case))
+    d = to_device(case)
+    out = run_gpu(d)
+    grid_out = run_gpu(d, schedule="grid")
     torch.cuda.synchronize()
     assert guard_rows_untouched(out, written), "rows outside the requests were written"
     mx, mean = assert_close(out, want, written, fp8=case["kv_dtype"] != "bf16", what=name)
     _say(f"  max {mx:.2e} mean {mean:.2e}")
+    # both schedules run the same per-item arithmetic: identical bits
+    assert torch.equal(out.view(torch.int16), grid_out.view(torch.int16)), "persistent != grid schedule"
+    assert not workspace().any(), "scheduler workspace not returned to zero"
 
 
 def test_tiny_config_full():
@@ -142,11 +147,14 @@ def test_chunked_config_full():
     case = make_case("chunked")
     _say("chunked", case["q_lens"], case["kv_lens"])
     want, written = run_oracle(case)
-    out = run_gpu(to_device(case))
+    d = to_device(case)
+    out = run_gpu(d)
+    grid_out = run_gpu(d, schedule="grid")
     torch.cuda.synchronize()
     assert guard_rows_untouched(out, written)
     mx, mean = assert_close(out, want, written, what="chunked")
     _say(f"  max {mx:.2e} mean {mean:.2e}")
+    assert torch.equal(out.view(torch.int16), grid_out.view(torch.int16))
 
 
 def _sample_rows(case, n_random=96, seed=0):
@@ -172,7 +180,9 @@ def test_full_size_config_sampled(name):
     _say("full", name, "tokens", sum(case["q_lens"]))
     d = to_device(case)
     out = run_gpu(d)
+    grid_out = run_gpu(d, schedule="grid")
     torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), grid_out.view(torch.int16)), "persistent != grid schedule"
     written = np.zeros(case["num_tokens"], dtype=bool)
     written[:int(case["cum_seq_lens_q"][-1])] = True
     assert guard_rows_untouched(out, written)
@@ -253,3 +263,46 @@ def test_rejects_bad_metadata_without_launch():
     bad[1] = 3  # q_len 7 > kv_len 3
     with pytest.raises(ppa.PpaError):
         run_gpu(dict(d, seq_lens=bad), validate=True)
+
+
+# --------------------------------------------------------------------------
+# the persistent schedule's workspace
+# --------------------------------------------------------------------------
+
+def test_schedule_back_to_back_and_workspace_reset():
+    """Calls of different sizes, back to back on one stream, sharing one
+    workspace: every call sees zeroed counters (the previous call's last
+    workgroup reset them), so every call covers all of its work items."""
+    cases = [make_custom_case(name="bb%d" % i, batch=b, num_qo_heads=hq, num_kv_heads=hk, head_dim=d,
+                              page_size=ps, q_lens=ql, prefix_lens=pl, seed=500 + i)
+             for i, (b, hq, hk, d, ps, ql, pl) in enumerate([
+                 (3, 32, 8, 128, 32, (700, 64, 300), (100, 0, 900)),    # 8 queues
+                 (1, 6, 2, 64, 16, (90,), (10,)),                        # 1 queue, few items
+                 (5, 16, 4, 128, 64, (1, 2, 3, 4, 900), (0, 5, 60, 0, 7)),
+                 (2, 64, 8, 64, 16, (2000, 17), (0, 3000)),
+             ])]
+    ws = workspace()
+    assert not ws.any()
+    wants = [run_oracle(c) for c in cases]
+    devs = [to_device(c) for c in cases]
+    for rep in range(2):
+        outs = [run_gpu(d, validate=False) for d in devs]   # no sync between calls
+        torch.cuda.synchronize()
+        for c, (want, written), out in zip(cases, wants, outs):
+            assert guard_rows_untouched(out, written)
+            assert_close(out, want, written, what=c["name"] if "name" in c else "bb")
+        assert not ws.any(), "workspace not zero after the calls"
+
+
+def test_rejects_small_or_misaligned_workspace():
+    import paged_kv_prefill_varlen_amd as ppa
+    case = make_case("tiny")
+    d = to_device(case)
+    out = torch.empty_like(d["query"])
+    for ws in (torch.zeros(8, dtype=torch.uint8, device="cuda"),
+               torch.zeros(ppa.WORKSPACE_BYTES + 16, dtype=torch.uint8, device="cuda")[4:]):
+        p = ppa.make_params(d["query"], d["kv_cache"], ws, d["block_tables"], d["seq_lens"], d["max_q_len"],
+                            d["max_kv_len"], d["bmm1_scale"], d["bmm2_scale"], d["batch_size"],
+                            d["cum_seq_lens_q"], d["cum_seq_lens_kv"], -1, out, d["kv_layout"], None)
+        with pytest.raises(ppa.PpaError):
+            ppa.ppa_paged_prefill_attention(p)

@@ -126,6 +126,25 @@ __device__ __forceinline__ int swap_bits23(int i) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Combine the values of the lane pair (l, l ^ 32) without an LDS round trip:
+// v_permlane32_swap with both operands holding x leaves x[l % 32] in the
+// first and x[32 + l % 32] in the second.  Written as inline asm because
+// hipcc (ROCm 7.2) folds the two results of __builtin_amdgcn_permlane32_swap
+// into one value (max(r0, r1) becomes r0, r0 + r1 becomes 2 r0).  The nops
+// cover the VALU-write -> permlane and permlane -> VALU-read hazards.
+__device__ __forceinline__ float pair_max(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1"
+               : "+v"(a), "+v"(b));
+  return a;
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_add_f32 %0, %0, %1"
+               : "+v"(a), "+v"(b));
+  return a;
+}
+
 // Tile geometry.  Every wave stages 8 consecutive keys of both K and V of a
 // 64-key tile, so the staging work is the same for all waves and, with pages
 // of >= 8 tokens, a wave's keys lie in one page whose id is wave-uniform.
@@ -446,7 +465,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     float m = kNegInf;
     for (int mt = 0; mt < 2; ++mt)
       for (int v = 0; v < 16; ++v) m = fmaxf(m, sacc[mt][v]);
-    m = fmaxf(m, __shfl_xor(m, 32));
+    m = pair_max(m);
     const float mtile = m * c;   // -inf stays -inf (c > 0)
     const bool need = mtile > m_run + kRescaleThreshold;
     if (__ballot(need) != 0ull) {
@@ -500,7 +519,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
 
   // ---- epilogue -------------------------------------------------------------
   if (!wave_active) return;
-  float l = l_part + __shfl_xor(l_part, 32);
+  float l = pair_sum(l_part);
   if (!rvalid) return;
   const int h = h0 + hd;
   const float mb = m_run == kNegInf ? 0.f : m_run;

@@ -240,7 +240,7 @@ def main():
             "traffic": stored_traffic(args.config),
             "algorithmic_bytes": algorithmic_bytes(case),
             "kernel_ms": round(launch_ms, 5),
-            "kernel": "paged_prefill_kernel<%d,%s>" % (case["head_dim"], "fp8" if fp8 else "bf16"),
+            "kernel": "paged_prefill_persistent<%d,%s>" % (case["head_dim"], "fp8" if fp8 else "bf16"),
         },
         "cpu_baseline": None,
     }

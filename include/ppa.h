@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PPA_ABI_VERSION 1
+#define PPA_ABI_VERSION 2
 
 typedef enum ppa_status {
   PPA_OK = 0,
@@ -77,6 +77,11 @@ typedef enum ppa_kv_layout {
   PPA_KV_LAYOUT_HND = 0,       /* page = [num_kv_heads, page_size, head_dim]        */
   PPA_KV_LAYOUT_NHD = 1        /* page = [page_size, num_kv_heads, head_dim]        */
 } ppa_kv_layout;
+
+typedef enum ppa_page_table_form {
+  PPA_PAGE_TABLE_PADDED = 0,   /* block_tables [batch_size, cols] (API page)      */
+  PPA_PAGE_TABLE_CSR = 1       /* kv_indptr / kv_indices (flat, per request)     */
+} ppa_page_table_form;
 
 typedef enum ppa_kv_form {
   PPA_KV_SPLIT = 0,            /* two tensors: K pool and V pool                    */
@@ -175,6 +180,28 @@ typedef struct ppa_params {
   void* out;
   int32_t out_dtype;
   int64_t out_strides[3];
+
+  /* Page-table form.  PPA_PAGE_TABLE_PADDED: block_tables above.
+     PPA_PAGE_TABLE_CSR: the flat form of the TensorRT-LLM attention-backend
+     article (section on why FlashInfer uses a flat index array plus an
+     indptr instead of a 2-D table); block_tables is then unused (may be
+     NULL):
+       kv_indptr        [batch_size + 1] int32 device array, non-decreasing;
+                        request b's pages are kv_indices[kv_indptr[b] ..
+                        kv_indptr[b + 1])
+       kv_indices       [kv_indices_len] int32 device array of page ids in
+                        [0, num_pages)
+       kv_last_page_len [batch_size] int32 device array or NULL; only the host
+                        checker reads it: seq_lens[b] must then equal
+                        (pages_b - 1) * page_size + kv_last_page_len[b] with
+                        1 <= kv_last_page_len[b] <= page_size (0 pages: 0)
+     Only the first ceil(seq_lens[b] / page_size) pages of a request are read;
+     indptr values are clamped to [0, kv_indices_len] on the device. */
+  int32_t page_table_form;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  int64_t kv_indices_len;
+  const int32_t* kv_last_page_len;
 } ppa_params;
 
 /* ABI guards for bindings: the version this library was built with and
@@ -203,11 +230,24 @@ int32_t ppa_validate_shapes(const ppa_params* p, char* msg, size_t msg_len);
  * span has no defined output); q_len <= max_q_len, kv_len <= max_kv_len;
  * cum_seq_lens_kv (if not NULL) is the running sum of seq_lens; every table
  * entry a request reaches lies in [0, num_pages).  block_tables uses the
- * row stride of p->block_tables_row_stride.  Pure function of its inputs.
+ * row stride of p->block_tables_row_stride; with the CSR page-table form it
+ * is not read (may be NULL).  Pure function of its inputs.
  */
 int32_t ppa_validate_metadata_host(const ppa_params* p, const int32_t* cum_seq_lens_q,
                                    const int32_t* cum_seq_lens_kv, const int32_t* seq_lens,
                                    const int32_t* block_tables, char* msg, size_t msg_len);
+
+/*
+ * The page-table part of the deep check for the CSR form, on HOST copies:
+ * kv_indptr[0] >= 0, non-decreasing, kv_indptr[batch_size] <= kv_indices_len;
+ * every request has at least ceil(seq_lens[b] / page_size) pages, each a page
+ * id in [0, num_pages); with kv_last_page_len, the page count and last-page
+ * length reproduce seq_lens exactly.  (ppa_validate_metadata_host checks the
+ * lengths and skips the table for this form.)  Pure function of its inputs.
+ */
+int32_t ppa_validate_page_table_csr_host(const ppa_params* p, const int32_t* seq_lens,
+                                         const int32_t* kv_indptr, const int32_t* kv_indices,
+                                         const int32_t* kv_last_page_len, char* msg, size_t msg_len);
 
 /* Bytes of workspace the balanced schedule uses (a small constant; p may be
    NULL). */

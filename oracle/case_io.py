@@ -49,7 +49,9 @@ def oracle_inputs(case: dict) -> dict:
         query=decode_tensor(case["query"]),
         kv_cache=kv_np,
         kv_layout=case["kv_layout"],
-        block_tables=case["block_tables"].cpu().numpy(),
+        block_tables=None if case.get("kv_indptr") is not None else case["block_tables"].cpu().numpy(),
+        kv_indptr=None if case.get("kv_indptr") is None else case["kv_indptr"].cpu().numpy(),
+        kv_indices=None if case.get("kv_indices") is None else case["kv_indices"].cpu().numpy(),
         seq_lens=case["seq_lens"].cpu().numpy(),
         cum_seq_lens_q=case["cum_seq_lens_q"].cpu().numpy(),
         page_size=case["page_size"],

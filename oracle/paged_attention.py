@@ -14,7 +14,10 @@ at a time, in the order the pages define the operation:
    step of the TensorRT-LLM attention-backend article (section "path 1:
    VanillaAttention"), with a page id from ``block_tables[b, t // P]`` and the
    slot ``t % P`` (FlashInfer API page, parameters ``kv_cache`` and
-   ``block_tables``; article section "physical meaning of handle -> offset");
+   ``block_tables``; article section "physical meaning of handle -> offset"),
+   or, for the flat page table, from ``kv_indices[kv_indptr[b] + t // P]``
+   (article section on why FlashInfer uses a flat index array with an
+   indptr rather than a 2-D table);
 3. for each query head, logits ``bmm1_scale * q . k`` (API page, parameter
    ``bmm1_scale``);
 4. the causal mask with the new queries at the end of the KV sequence
@@ -188,21 +191,31 @@ def attention_one_request(q: np.ndarray, k: np.ndarray, v: np.ndarray, bmm1_scal
     return out
 
 
+def request_pages(b: int, block_tables: Optional[np.ndarray], kv_indptr: Optional[np.ndarray] = None,
+                  kv_indices: Optional[np.ndarray] = None) -> np.ndarray:
+    """Page ids of request b: row b of the padded table, or the slice
+    ``kv_indices[kv_indptr[b]:kv_indptr[b + 1]]`` of the flat one."""
+    if kv_indptr is not None:
+        return np.asarray(kv_indices)[int(kv_indptr[b]):int(kv_indptr[b + 1])]
+    return np.asarray(block_tables[b])
+
+
 def paged_prefill_attention(query: np.ndarray, kv_cache, kv_layout: str,
-                            block_tables: np.ndarray, seq_lens: np.ndarray,
+                            block_tables: Optional[np.ndarray], seq_lens: np.ndarray,
                             cum_seq_lens_q: np.ndarray, page_size: int,
                             bmm1_scale: float, bmm2_scale: float,
                             window_left: int = -1,
                             sinks: Optional[np.ndarray] = None,
                             requests: Optional[Sequence[int]] = None,
-                            chunk: int = 256) -> Tuple[np.ndarray, np.ndarray]:
+                            chunk: int = 256, kv_indptr: Optional[np.ndarray] = None,
+                            kv_indices: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """The whole batched call on decoded float64 inputs.
 
     ``query`` ``[num_tokens, H_q, D]``; ``kv_cache`` a (K, V) tuple of page
     pools or one array with the K/V planes in dim 1, laid out per
-    ``kv_layout``; ``block_tables`` ``[batch, W]``; ``seq_lens`` the KV length
-    of each request (cached prefix included); ``cum_seq_lens_q``
-    ``[batch + 1]``.  Returns ``(out, written)``: ``out`` ``[num_tokens, H_q,
+    ``kv_layout``; ``block_tables`` ``[batch, W]`` (or None with the flat
+    ``kv_indptr`` / ``kv_indices``); ``seq_lens`` the KV length of each
+    request (cached prefix included); ``cum_seq_lens_q`` ``[batch + 1]``.  Returns ``(out, written)``: ``out`` ``[num_tokens, H_q,
     D]`` float64 with NaN in rows no request owns, and ``written`` the bool
     row mask.  ``requests`` restricts the work to some requests (the other
     rows stay NaN / unwritten)."""
@@ -219,18 +232,21 @@ def paged_prefill_attention(query: np.ndarray, kv_cache, kv_layout: str,
             continue
         if q_len > kv_len:
             raise ValueError(f"request {b}: q_len {q_len} > kv_len {kv_len}")
-        k = gather_paged_kv(kv_cache, block_tables[b], 0, kv_len, page_size, kv_layout)
-        v = gather_paged_kv(kv_cache, block_tables[b], 1, kv_len, page_size, kv_layout)
+        pages = request_pages(b, block_tables, kv_indptr, kv_indices)
+        k = gather_paged_kv(kv_cache, pages, 0, kv_len, page_size, kv_layout)
+        v = gather_paged_kv(kv_cache, pages, 1, kv_len, page_size, kv_layout)
         out[q0:q1] = attention_one_request(query[q0:q1], k, v, bmm1_scale, bmm2_scale,
                                            window_left, sinks, chunk)
         written[q0:q1] = True
     return out, written
 
 
-def attention_rows(query: np.ndarray, kv_cache, kv_layout: str, block_tables: np.ndarray,
+def attention_rows(query: np.ndarray, kv_cache, kv_layout: str, block_tables: Optional[np.ndarray],
                    seq_lens: np.ndarray, cum_seq_lens_q: np.ndarray, page_size: int,
                    bmm1_scale: float, bmm2_scale: float, window_left: int,
-                   sinks: Optional[np.ndarray], rows: Sequence[Tuple[int, int]]) -> np.ndarray:
+                   sinks: Optional[np.ndarray], rows: Sequence[Tuple[int, int]],
+                   kv_indptr: Optional[np.ndarray] = None,
+                   kv_indices: Optional[np.ndarray] = None) -> np.ndarray:
     """Selected output rows, one (token, q head) pair at a time: ``[len(rows),
     D]``.  Used to check full-size runs on a sample of outputs."""
     num_tokens, num_qo_heads, head_dim = query.shape
@@ -245,8 +261,9 @@ def attention_rows(query: np.ndarray, kv_cache, kv_layout: str, block_tables: np
         q_len = int(cu[b + 1]) - q0
         i = t - q0
         if b not in cache:
-            cache[b] = (gather_paged_kv(kv_cache, block_tables[b], 0, kv_len, page_size, kv_layout),
-                        gather_paged_kv(kv_cache, block_tables[b], 1, kv_len, page_size, kv_layout))
+            pages = request_pages(b, block_tables, kv_indptr, kv_indices)
+            cache[b] = (gather_paged_kv(kv_cache, pages, 0, kv_len, page_size, kv_layout),
+                        gather_paged_kv(kv_cache, pages, 1, kv_len, page_size, kv_layout))
         k, v = cache[b]
         hk = _kv_head(h, num_qo_heads, num_kv_heads)
         valid = _valid_mask(q_len, kv_len, window_left)[i:i + 1]

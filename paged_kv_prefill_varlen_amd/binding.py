@@ -14,7 +14,7 @@ from typing import Optional, Sequence, Tuple, Union
 import numpy as np
 import torch
 
-PPA_ABI_VERSION = 1
+PPA_ABI_VERSION = 2
 
 # enums of ppa.h
 PPA_DTYPE_BF16 = 1
@@ -24,6 +24,8 @@ PPA_KV_LAYOUT_HND = 0
 PPA_KV_LAYOUT_NHD = 1
 PPA_KV_SPLIT = 0
 PPA_KV_COMBINED = 1
+PPA_PAGE_TABLE_PADDED = 0
+PPA_PAGE_TABLE_CSR = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.environ.get("PPA_LIBRARY", os.path.join(_HERE, "_lib", "libppa.so"))
@@ -72,6 +74,11 @@ class PpaParams(ctypes.Structure):
         ("out", c_void_p),
         ("out_dtype", c_int32),
         ("out_strides", c_int64 * 3),
+        ("page_table_form", c_int32),
+        ("kv_indptr", c_void_p),
+        ("kv_indices", c_void_p),
+        ("kv_indices_len", c_int64),
+        ("kv_last_page_len", c_void_p),
     ]
 
 
@@ -93,6 +100,8 @@ def _load():
         "ppa_strerror": (c_char_p, [c_int32]),
         "ppa_validate_shapes": (c_int32, [P, c_char_p, c_size_t]),
         "ppa_validate_metadata_host": (c_int32, [P, c_void_p, c_void_p, c_void_p, c_void_p, c_char_p, c_size_t]),
+        "ppa_validate_page_table_csr_host": (c_int32, [P, c_void_p, c_void_p, c_void_p, c_void_p, c_char_p,
+                                                       c_size_t]),
         "ppa_workspace_bytes": (c_size_t, [P]),
         "ppa_paged_prefill_attention": (c_int32, [P, c_void_p]),
         "ppa_gather_paged_kv": (c_int32, [P, c_int32, c_void_p, c_int64, c_void_p]),
@@ -166,6 +175,20 @@ def ppa_validate_metadata_host(params: PpaParams, cum_seq_lens_q, cum_seq_lens_k
     return int(st), buf.value.decode()
 
 
+def ppa_validate_page_table_csr_host(params: PpaParams, seq_lens, kv_indptr, kv_indices,
+                                     kv_last_page_len=None) -> Tuple[int, str]:
+    """Page-table check of the flat (CSR) form on host copies."""
+    sl = _host_i32(seq_lens)
+    ip = _host_i32(kv_indptr)
+    ix = _host_i32(kv_indices)
+    lp = _host_i32(kv_last_page_len)
+    ptr = lambda a: None if a is None else a.ctypes.data_as(c_void_p)  # noqa: E731
+    buf = ctypes.create_string_buffer(512)
+    st = _lib.ppa_validate_page_table_csr_host(ctypes.byref(params), ptr(sl), ptr(ip), ptr(ix), ptr(lp), buf,
+                                               len(buf))
+    return int(st), buf.value.decode()
+
+
 def ppa_workspace_bytes(params: Optional[PpaParams] = None) -> int:
     return int(_lib.ppa_workspace_bytes(None if params is None else ctypes.byref(params)))
 
@@ -227,12 +250,16 @@ def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
 
 
 def make_params(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.Tensor],
-                block_tables: torch.Tensor, seq_lens: torch.Tensor, max_q_len: int, max_kv_len: int,
+                block_tables: Optional[torch.Tensor], seq_lens: torch.Tensor, max_q_len: int, max_kv_len: int,
                 bmm1_scale, bmm2_scale, batch_size: int, cum_seq_lens_q: torch.Tensor,
                 cum_seq_lens_kv: Optional[torch.Tensor], window_left: int, out: torch.Tensor,
-                kv_layout: str = "HND", sinks=None) -> PpaParams:
+                kv_layout: str = "HND", sinks=None, kv_indptr: Optional[torch.Tensor] = None,
+                kv_indices: Optional[torch.Tensor] = None,
+                kv_last_page_len: Optional[torch.Tensor] = None) -> PpaParams:
     """Fill a PpaParams from torch tensors (the FlashInfer API page's argument
-    list).  Keeps no reference to the tensors: the caller keeps them alive."""
+    list).  With kv_indptr / kv_indices the flat (CSR) page table is used and
+    block_tables may be None.  Keeps no reference to the tensors: the caller
+    keeps them alive."""
     p = PpaParams()
     p.abi_version = PPA_ABI_VERSION
     p.struct_size = ctypes.sizeof(PpaParams)
@@ -278,12 +305,28 @@ def make_params(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.
         p.workspace = _ptr(workspace_buffer)
         p.workspace_bytes = workspace_buffer.numel() * workspace_buffer.element_size()
 
-    bt = _i32(block_tables, "block_tables")
-    if bt.dim() != 2 or bt.stride(1) != 1:
-        raise ValueError("block_tables must be [batch_size, cols] with unit column stride")
-    p.block_tables = _ptr(bt)
-    p.block_tables_cols = int(bt.shape[1])
-    p.block_tables_row_stride = int(bt.stride(0))
+    if kv_indptr is not None or kv_indices is not None:
+        if kv_indptr is None or kv_indices is None:
+            raise ValueError("the flat page table needs both kv_indptr and kv_indices")
+        ip = _i32(kv_indptr, "kv_indptr")
+        ix = _i32(kv_indices, "kv_indices")
+        if ip.dim() != 1 or ix.dim() != 1:
+            raise ValueError("kv_indptr and kv_indices must be 1-D")
+        p.page_table_form = PPA_PAGE_TABLE_CSR
+        p.kv_indptr = _ptr(ip)
+        p.kv_indices = _ptr(ix)
+        p.kv_indices_len = int(ix.numel())
+        if kv_last_page_len is not None:
+            p.kv_last_page_len = _ptr(_i32(kv_last_page_len, "kv_last_page_len"))
+    if block_tables is not None:
+        bt = _i32(block_tables, "block_tables")
+        if bt.dim() != 2 or bt.stride(1) != 1:
+            raise ValueError("block_tables must be [batch_size, cols] with unit column stride")
+        p.block_tables = _ptr(bt)
+        p.block_tables_cols = int(bt.shape[1])
+        p.block_tables_row_stride = int(bt.stride(0))
+    elif p.page_table_form != PPA_PAGE_TABLE_CSR:
+        raise ValueError("block_tables is required unless kv_indptr / kv_indices are given")
     p.seq_lens = _ptr(_i32(seq_lens, "seq_lens"))
     p.cum_seq_lens_q = _ptr(_i32(cum_seq_lens_q, "cum_seq_lens_q"))
     p.cum_seq_lens_kv = None if cum_seq_lens_kv is None else _ptr(_i32(cum_seq_lens_kv, "cum_seq_lens_kv"))
@@ -319,23 +362,28 @@ def make_params(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.
 
 
 def batch_context_with_kv_cache(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.Tensor],
-                                block_tables: torch.Tensor, seq_lens: torch.Tensor, max_q_len: int,
+                                block_tables: Optional[torch.Tensor], seq_lens: torch.Tensor, max_q_len: int,
                                 max_kv_len: int, bmm1_scale, bmm2_scale, batch_size: int,
                                 cum_seq_lens_q: torch.Tensor, cum_seq_lens_kv: Optional[torch.Tensor],
                                 window_left: int = -1, out: Optional[torch.Tensor] = None,
                                 out_dtype=None, kv_layout: str = "HND", sinks=None,
-                                validate: bool = False, stream=None) -> torch.Tensor:
+                                validate: bool = False, stream=None, kv_indptr=None, kv_indices=None,
+                                kv_last_page_len=None) -> torch.Tensor:
     """Batched paged prefill attention; argument list of the API page
-    (without the nvfp4 output and PDL options).  ``validate=True`` also runs
-    the deep metadata check on host copies (a device-to-host sync)."""
+    (without the nvfp4 output and PDL options), plus the optional flat page
+    table (kv_indptr / kv_indices / kv_last_page_len) in place of
+    block_tables.  ``validate=True`` also runs the deep metadata check on host
+    copies (a device-to-host sync)."""
     if out is None:
         dt = query.dtype if out_dtype is None else out_dtype
         out = torch.empty(query.shape, dtype=dt, device=query.device)
     p = make_params(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_q_len, max_kv_len,
                     bmm1_scale, bmm2_scale, batch_size, cum_seq_lens_q, cum_seq_lens_kv, window_left,
-                    out, kv_layout, sinks)
+                    out, kv_layout, sinks, kv_indptr, kv_indices, kv_last_page_len)
     if validate:
         st, msg = ppa_validate_metadata_host(p, cum_seq_lens_q, cum_seq_lens_kv, seq_lens, block_tables)
+        if st == 0 and p.page_table_form == PPA_PAGE_TABLE_CSR:
+            st, msg = ppa_validate_page_table_csr_host(p, seq_lens, kv_indptr, kv_indices, kv_last_page_len)
         if st != 0:
             raise PpaError(st, msg)
     ppa_paged_prefill_attention(p, stream, query.device)

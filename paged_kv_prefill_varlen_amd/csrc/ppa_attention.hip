@@ -81,6 +81,9 @@ struct AttnArgs {
   int32_t bt_cols;
   int32_t num_pages;
   int32_t page_shift;
+  const int32_t* kv_indptr;    // flat page table, or NULL
+  const int32_t* kv_indices;
+  int64_t kv_indices_len;
   const int32_t* seq_lens;
   const int32_t* cu_q;
   int32_t num_tokens;
@@ -398,8 +401,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   const int tile_hi = key_hi >= 0 ? key_hi / kBK : -1;
 
   PageTable pt;
-  pt.row = a.block_tables + static_cast<int64_t>(b) * a.bt_row_stride;
-  pt.cols = a.bt_cols;
+  request_table(pt, b, a.block_tables, a.bt_row_stride, a.bt_cols, a.kv_indptr, a.kv_indices, a.kv_indices_len);
   pt.num_pages = a.num_pages;
   pt.page_shift = a.page_shift;
   const int page_mask = (1 << a.page_shift) - 1;
@@ -575,6 +577,9 @@ void paged_prefill_persistent(AttnArgs a) {
 // ---- address-unit check: paged K or V -> contiguous [tokens, H_kv, D] ------
 struct GatherArgs {
   PagedPlane plane;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  int64_t kv_indices_len;
   const int32_t* block_tables;
   int64_t bt_row_stride;
   int32_t bt_cols, num_pages, page_shift;
@@ -593,8 +598,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs g) {
   const int t0 = blockIdx.x * kGatherTokens;
   if (t0 >= kv_len) return;
   PageTable pt;
-  pt.row = g.block_tables + static_cast<int64_t>(b) * g.bt_row_stride;
-  pt.cols = g.bt_cols;
+  request_table(pt, b, g.block_tables, g.bt_row_stride, g.bt_cols, g.kv_indptr, g.kv_indices, g.kv_indices_len);
   pt.num_pages = g.num_pages;
   pt.page_shift = g.page_shift;
   const int page_mask = (1 << g.page_shift) - 1;
@@ -690,6 +694,11 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
   a.block_tables = p->block_tables;
   a.bt_row_stride = p->batch_size > 1 ? p->block_tables_row_stride : 0;
   a.bt_cols = p->block_tables_cols;
+  if (p->page_table_form == PPA_PAGE_TABLE_CSR) {
+    a.kv_indptr = p->kv_indptr;
+    a.kv_indices = p->kv_indices;
+    a.kv_indices_len = p->kv_indices_len;
+  }
   a.num_pages = p->num_pages;
   a.page_shift = log2_exact(p->page_size);
   a.seq_lens = p->seq_lens;
@@ -753,6 +762,11 @@ extern "C" int32_t ppa_gather_paged_kv(const ppa_params* p, int32_t kv_idx, void
   g.block_tables = p->block_tables;
   g.bt_row_stride = p->batch_size > 1 ? p->block_tables_row_stride : 0;
   g.bt_cols = p->block_tables_cols;
+  if (p->page_table_form == PPA_PAGE_TABLE_CSR) {
+    g.kv_indptr = p->kv_indptr;
+    g.kv_indices = p->kv_indices;
+    g.kv_indices_len = p->kv_indices_len;
+  }
   g.num_pages = p->num_pages;
   g.page_shift = log2_exact(p->page_size);
   g.seq_lens = p->seq_lens;

@@ -149,10 +149,13 @@ int32_t ppa_validate_shapes(const ppa_params* p, char* msg, size_t msg_len) {
     return fail(PPA_ERR_LAYOUT, msg, msg_len, "kv_form %d", p->kv_form);
   if (p->kv_form == PPA_KV_COMBINED && p->kv_planes != 1 && p->kv_planes != 2)
     return fail(PPA_ERR_LAYOUT, msg, msg_len, "kv_cache dim 1 is %d, must be 1 or 2", p->kv_planes);
+  if (p->page_table_form != PPA_PAGE_TABLE_PADDED && p->page_table_form != PPA_PAGE_TABLE_CSR)
+    return fail(PPA_ERR_LAYOUT, msg, msg_len, "page_table_form %d", p->page_table_form);
+  const bool csr = p->page_table_form == PPA_PAGE_TABLE_CSR;
 
   // sizes
   if (p->num_tokens < 0 || p->batch_size < 0 || p->max_q_len < 0 || p->max_kv_len < 0 ||
-      p->num_pages < 0 || p->block_tables_cols < 0)
+      p->num_pages < 0 || (!csr && p->block_tables_cols < 0) || (csr && p->kv_indices_len < 0))
     return fail(PPA_ERR_SHAPE, msg, msg_len, "negative size");
   if (p->num_kv_heads <= 0 || p->num_qo_heads <= 0 || p->num_qo_heads % p->num_kv_heads != 0)
     return fail(PPA_ERR_HEADS, msg, msg_len, "num_qo_heads %d, num_kv_heads %d", p->num_qo_heads,
@@ -167,7 +170,13 @@ int32_t ppa_validate_shapes(const ppa_params* p, char* msg, size_t msg_len) {
                 p->max_kv_len);
 
   const bool work = p->batch_size > 0 && p->max_q_len > 0 && p->num_tokens > 0;
-  if (p->batch_size > 0) {
+  if (p->batch_size > 0 && csr) {
+    if (p->seq_lens == nullptr || p->cum_seq_lens_q == nullptr || p->kv_indptr == nullptr ||
+        p->kv_indices == nullptr)
+      return fail(PPA_ERR_NULL_POINTER, msg, msg_len, "seq_lens / cum_seq_lens_q / kv_indptr / kv_indices");
+    if (p->max_kv_len > 0 && p->num_pages < 1)
+      return fail(PPA_ERR_SHAPE, msg, msg_len, "num_pages is 0 but max_kv_len is %d", p->max_kv_len);
+  } else if (p->batch_size > 0) {
     if (p->seq_lens == nullptr || p->cum_seq_lens_q == nullptr || p->block_tables == nullptr)
       return fail(PPA_ERR_NULL_POINTER, msg, msg_len, "seq_lens / cum_seq_lens_q / block_tables");
     const int64_t need = (static_cast<int64_t>(p->max_kv_len) + p->page_size - 1) / p->page_size;
@@ -235,7 +244,8 @@ int32_t ppa_validate_metadata_host(const ppa_params* p, const int32_t* cu_q, con
   const int B = p->batch_size;
   if (B < 0) return fail(PPA_ERR_SHAPE, msg, msg_len, "batch_size %d", B);
   if (B == 0) return PPA_OK;
-  if (cu_q == nullptr || seq_lens == nullptr || block_tables == nullptr)
+  const bool csr = p->page_table_form == PPA_PAGE_TABLE_CSR;
+  if (cu_q == nullptr || seq_lens == nullptr || (!csr && block_tables == nullptr))
     return fail(PPA_ERR_NULL_POINTER, msg, msg_len, "host metadata");
   if (p->page_size < 1) return fail(PPA_ERR_PAGE_SIZE, msg, msg_len, "page_size %d", p->page_size);
   if (cu_q[0] != 0) return fail(PPA_ERR_METADATA, msg, msg_len, "cum_seq_lens_q[0] = %d, must be 0", cu_q[0]);
@@ -264,6 +274,7 @@ int32_t ppa_validate_metadata_host(const ppa_params* p, const int32_t* cu_q, con
       return fail(PPA_ERR_METADATA, msg, msg_len,
                   "cum_seq_lens_kv[%d] = %d, the running sum of seq_lens is %lld", b + 1, cu_kv[b + 1],
                   (long long)kv_run);
+    if (csr) continue;   // the table is checked by ppa_validate_page_table_csr_host
     const int64_t pages = (kv_len + p->page_size - 1) / p->page_size;
     if (pages > p->block_tables_cols)
       return fail(PPA_ERR_TABLE, msg, msg_len, "request %d needs %lld pages, table has %d columns", b,
@@ -278,6 +289,50 @@ int32_t ppa_validate_metadata_host(const ppa_params* p, const int32_t* cu_q, con
   if (cu_q[B] > p->num_tokens)
     return fail(PPA_ERR_METADATA, msg, msg_len, "cum_seq_lens_q[%d] = %d > num_tokens %d", B, cu_q[B],
                 p->num_tokens);
+  return PPA_OK;
+}
+
+int32_t ppa_validate_page_table_csr_host(const ppa_params* p, const int32_t* seq_lens,
+                                         const int32_t* kv_indptr, const int32_t* kv_indices,
+                                         const int32_t* kv_last_page_len, char* msg, size_t msg_len) {
+  if (msg != nullptr && msg_len > 0) msg[0] = '\0';
+  if (p == nullptr) return fail(PPA_ERR_NULL_POINTER, msg, msg_len, "params is NULL");
+  const int B = p->batch_size;
+  if (B < 0) return fail(PPA_ERR_SHAPE, msg, msg_len, "batch_size %d", B);
+  if (B == 0) return PPA_OK;
+  if (seq_lens == nullptr || kv_indptr == nullptr || (kv_indices == nullptr && p->kv_indices_len > 0))
+    return fail(PPA_ERR_NULL_POINTER, msg, msg_len, "host page table");
+  if (p->page_size < 1) return fail(PPA_ERR_PAGE_SIZE, msg, msg_len, "page_size %d", p->page_size);
+  if (kv_indptr[0] < 0) return fail(PPA_ERR_TABLE, msg, msg_len, "kv_indptr[0] = %d", kv_indptr[0]);
+  for (int b = 0; b < B; ++b)
+    if (kv_indptr[b + 1] < kv_indptr[b])
+      return fail(PPA_ERR_TABLE, msg, msg_len, "kv_indptr decreases at request %d", b);
+  if (kv_indptr[B] > p->kv_indices_len)
+    return fail(PPA_ERR_TABLE, msg, msg_len, "kv_indptr[%d] = %d > kv_indices_len %lld", B, kv_indptr[B],
+                static_cast<long long>(p->kv_indices_len));
+  for (int b = 0; b < B; ++b) {
+    const int64_t kv_len = seq_lens[b];
+    const int64_t have = static_cast<int64_t>(kv_indptr[b + 1]) - kv_indptr[b];
+    const int64_t need = kv_len > 0 ? (kv_len + p->page_size - 1) / p->page_size : 0;
+    if (have < need)
+      return fail(PPA_ERR_TABLE, msg, msg_len, "request %d needs %lld pages, kv_indptr gives %lld", b,
+                  static_cast<long long>(need), static_cast<long long>(have));
+    for (int64_t j = 0; j < need; ++j) {
+      const int32_t id = kv_indices[kv_indptr[b] + j];
+      if (id < 0 || id >= p->num_pages)
+        return fail(PPA_ERR_TABLE, msg, msg_len, "kv_indices[%lld] (request %d) = %d outside [0, %d)",
+                    static_cast<long long>(kv_indptr[b] + j), b, id, p->num_pages);
+    }
+    if (kv_last_page_len != nullptr) {
+      const int64_t last = kv_last_page_len[b];
+      const bool ok = have == 0 ? (kv_len == 0 && last == 0)
+                                : (last >= 1 && last <= p->page_size && (have - 1) * p->page_size + last == kv_len);
+      if (!ok)
+        return fail(PPA_ERR_TABLE, msg, msg_len,
+                    "request %d: %lld pages with last_page_len %lld do not give seq_len %lld", b,
+                    static_cast<long long>(have), static_cast<long long>(last), static_cast<long long>(kv_len));
+    }
+  }
   return PPA_OK;
 }
 

@@ -1,7 +1,8 @@
 // Page-table address unit (device side).
 //
 // A request's logical KV token t lives in page block_tables[b][t >> log2(P)]
-// at slot t & (P - 1); the page's first element is the pool base plus
+// (or kv_indices[kv_indptr[b] + (t >> log2(P))] for the flat form) at slot
+// t & (P - 1); the page's first element is the pool base plus
 // page id x page stride (FlashInfer API page, parameters kv_cache and
 // block_tables; TensorRT-LLM attention-backend article, section "physical
 // meaning of handle -> offset": tables hold ids, the kernel multiplies by the
@@ -12,8 +13,8 @@
 //
 // Ids are int32; the products are int64 so pools above 4 GiB work.  The
 // column index is clamped to the table width and the id to [0, num_pages),
-// so metadata that the host checker would reject can never send a read
-// outside the pool.
+// and a table without columns is not read, so metadata that the host
+// checker would reject can never send a read outside the pool.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,13 +30,14 @@ struct PagedPlane {
 };
 
 struct PageTable {
-  const int32_t* row;    // block_tables + b * row_stride
-  int32_t cols;          // table width
+  const int32_t* row;    // block_tables + b * row_stride, or kv_indices + kv_indptr[b]
+  int32_t cols;          // table width (pages of the request for the flat form)
   int32_t num_pages;
   int32_t page_shift;    // log2(page_size)
 };
 
 __device__ __forceinline__ int page_id(const PageTable& pt, int token) {
+  if (pt.cols <= 0) return 0;   // no pages: never read the table
   int col = token >> pt.page_shift;
   col = col < pt.cols - 1 ? col : pt.cols - 1;
   int id = pt.row[col];
@@ -48,6 +50,7 @@ __device__ __forceinline__ int page_id(const PageTable& pt, int token) {
 // read through the constant address space, so the load is a scalar one whose
 // result does not wait behind the wave's outstanding vector loads.
 __device__ __forceinline__ int page_id_uniform(const PageTable& pt, int token) {
+  if (pt.cols <= 0) return 0;
   int col = token >> pt.page_shift;
   col = col < pt.cols - 1 ? col : pt.cols - 1;
   const __attribute__((address_space(4))) int32_t* row =
@@ -56,6 +59,24 @@ __device__ __forceinline__ int page_id_uniform(const PageTable& pt, int token) {
   id = id < 0 ? 0 : id;
   id = id < pt.num_pages ? id : pt.num_pages - 1;
   return id;
+}
+
+// Row of request b: block_tables (padded form) or kv_indices from kv_indptr[b]
+// (flat form, indptr clamped to [0, indices_len]).
+__device__ __forceinline__ void request_table(PageTable& pt, int b, const int32_t* block_tables,
+                                              int64_t bt_row_stride, int32_t bt_cols, const int32_t* kv_indptr,
+                                              const int32_t* kv_indices, int64_t indices_len) {
+  if (kv_indptr != nullptr) {
+    int64_t s0 = kv_indptr[b], s1 = kv_indptr[b + 1];
+    s0 = s0 < 0 ? 0 : (s0 > indices_len ? indices_len : s0);
+    s1 = s1 < s0 ? s0 : (s1 > indices_len ? indices_len : s1);
+    pt.row = kv_indices + s0;
+    const int64_t n = s1 - s0;
+    pt.cols = static_cast<int32_t>(n < 0x7fffffff ? n : 0x7fffffff);
+  } else {
+    pt.row = block_tables + static_cast<int64_t>(b) * bt_row_stride;
+    pt.cols = bt_cols;
+  }
 }
 
 // Byte address of element `elem` of token `token` (page `id`) for kv head hk.

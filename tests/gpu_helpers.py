@@ -16,8 +16,10 @@ GUARD = 0x7FC1  # a NaN payload no kernel produces: marks rows that must stay un
 
 def to_device(case: dict, device="cuda") -> dict:
     d = dict(case)
-    for k in ("query", "block_tables", "seq_lens", "cum_seq_lens_q", "cum_seq_lens_kv"):
-        d[k] = case[k].to(device)
+    for k in ("query", "block_tables", "seq_lens", "cum_seq_lens_q", "cum_seq_lens_kv",
+              "kv_indptr", "kv_indices", "kv_last_page_len"):
+        if case.get(k) is not None:
+            d[k] = case[k].to(device)
     kv = case["kv_cache"]
     d["kv_cache"] = tuple(t.to(device) for t in kv) if isinstance(kv, tuple) else kv.to(device)
     d["sinks"] = None if case["sinks"] is None else case["sinks"].to(device)
@@ -47,14 +49,16 @@ def run_gpu(dcase: dict, out: torch.Tensor = None, bmm1=None, bmm2=None, stream=
         out = torch.empty_like(dcase["query"]).view(torch.int16).fill_(GUARD).view(torch.bfloat16)
     ws = workspace(dcase["query"].device) if schedule == "persistent" else None
     assert schedule in ("persistent", "grid")
+    flat = dcase.get("kv_indptr") is not None
     ppa.batch_context_with_kv_cache(
-        dcase["query"], dcase["kv_cache"], ws, dcase["block_tables"], dcase["seq_lens"],
+        dcase["query"], dcase["kv_cache"], ws, None if flat else dcase["block_tables"], dcase["seq_lens"],
         dcase["max_q_len"], dcase["max_kv_len"],
         dcase["bmm1_scale"] if bmm1 is None else bmm1,
         dcase["bmm2_scale"] if bmm2 is None else bmm2,
         dcase["batch_size"], dcase["cum_seq_lens_q"], dcase["cum_seq_lens_kv"],
         window_left=dcase["window_left"], out=out, kv_layout=dcase["kv_layout"],
-        sinks=dcase["sinks"], validate=validate, stream=stream)
+        sinks=dcase["sinks"], validate=validate, stream=stream, kv_indptr=dcase.get("kv_indptr"),
+        kv_indices=dcase.get("kv_indices"), kv_last_page_len=dcase.get("kv_last_page_len"))
     return out
 
 

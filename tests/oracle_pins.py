@@ -22,7 +22,7 @@ import torch
 import oracle.paged_attention as OA
 from oracle.case_io import decode_tensor, oracle_inputs
 from workloads import make_custom_case
-from workloads.cases import relayout
+from workloads.cases import relayout, to_flat_page_table
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -411,6 +411,26 @@ def pin_gqa_equals_repeated_mha():
     assert np.array_equal(base, got, equal_nan=True)
 
 
+def pin_flat_page_table():
+    """The flat page table (kv_indptr / kv_indices) names the same pages as
+    the padded one: pages gathered through it reproduce the generator's
+    logical K/V, and the output equals the padded-table output bit for bit,
+    with junk entries before request 0 and after each request's pages."""
+    case = _tiny(611, sinks=True, window_left=3, q_lens=(5, 0, 7), prefix_lens=(3, 2, 6))
+    base, _ = _run(case)
+    flat = to_flat_page_table(case, slack=2, lead=3, seed=5)
+    a = oracle_inputs(flat)
+    assert a["block_tables"] is None
+    for b, kv in enumerate(case["kv_lens"]):
+        pages = OA.request_pages(b, None, a["kv_indptr"], a["kv_indices"])
+        for kv_idx, logical in ((0, case["logical_k"]), (1, case["logical_v"])):
+            got = OA.gather_paged_kv(a["kv_cache"], pages, kv_idx, kv, case["page_size"], case["kv_layout"])
+            want = decode_tensor(logical[b]) if kv else np.zeros((0,) + got.shape[1:])
+            assert np.array_equal(got, want), (b, kv_idx)
+    got, _ = OA.paged_prefill_attention(**a)
+    assert np.array_equal(base, got, equal_nan=True)
+
+
 ALL_PINS = [
     pin_bf16_decode_all_codes,
     pin_e4m3fn_decode_all_codes,
@@ -430,4 +450,5 @@ ALL_PINS = [
     pin_request_permutation,
     pin_bmm2_linear,
     pin_gqa_equals_repeated_mha,
+    pin_flat_page_table,
 ]

@@ -298,3 +298,82 @@ def test_workspace_is_optional_but_checked_when_given():
     assert _shapes(p)[0] == ERR["PPA_ERR_WORKSPACE"]
     p = _params(c, workspace=ws.data_ptr() + 4, workspace_bytes=B.WORKSPACE_BYTES)
     assert _shapes(p)[0] == ERR["PPA_ERR_ALIGNMENT"]
+
+
+# --------------------------------------------------------------------------
+# the flat (CSR) page table
+# --------------------------------------------------------------------------
+
+def _csr(c, slack=0, lead=0):
+    ptr = [lead]   # page size 16 (the _case default)
+    idx = [0] * lead
+    last = []
+    for b in range(c["B"]):
+        kv = int(c["sl"][b])
+        n = (kv + 15) // 16
+        idx += [int(x) for x in c["bt"][b, :n]] + [1] * slack
+        ptr.append(len(idx))
+        last.append(0 if n == 0 else kv - (n - 1) * 16)
+    return (torch.tensor(ptr, dtype=torch.int32), torch.tensor(idx or [0], dtype=torch.int32),
+            torch.tensor(last, dtype=torch.int32))
+
+
+def _csr_params(c, ptr, idx, last=None, **over):
+    p = B.make_params(c["q"], c["kv"], None, None, c["sl"], c["max_q"], c["max_kv"], 0.125, 1.0, c["B"],
+                      c["cuq"], c["cukv"], c["W"], c["out"], c["layout"], c["sinks"], ptr, idx, last)
+    for k, v in over.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_csr_valid_description_passes():
+    c = _case()   # P 16, kv_lens (8, 4, 9)
+    ptr, idx, last = _csr(c)
+    p = _csr_params(c, ptr, idx, last)
+    assert p.page_table_form == B.PPA_PAGE_TABLE_CSR and p.block_tables is None
+    assert _shapes(p) == (OK, "")
+    assert B.ppa_validate_metadata_host(p, c["cuq"], c["cukv"], c["sl"], None)[0] == OK
+    assert B.ppa_validate_page_table_csr_host(p, c["sl"], ptr, idx, last)[0] == OK
+    # slack after each request and junk before request 0 are fine without last_page_len
+    ptr2, idx2, _ = _csr(c, slack=2, lead=3)
+    p2 = _csr_params(c, ptr2, idx2)
+    assert B.ppa_validate_page_table_csr_host(p2, c["sl"], ptr2, idx2, None)[0] == OK
+
+
+def test_csr_rejections():
+    c = _case()
+    ptr, idx, last = _csr(c)
+    E = ERR
+    chk = lambda p, ip, ix, lp=None: B.ppa_validate_page_table_csr_host(p, c["sl"], ip, ix, lp)[0]  # noqa: E731
+    p = _csr_params(c, ptr, idx, last)
+    # null device pointers / bad form
+    assert _shapes(_csr_params(c, ptr, idx, kv_indptr=None))[0] == E["PPA_ERR_NULL_POINTER"]
+    assert _shapes(_csr_params(c, ptr, idx, kv_indices=None))[0] == E["PPA_ERR_NULL_POINTER"]
+    assert _shapes(_csr_params(c, ptr, idx, page_table_form=7))[0] == E["PPA_ERR_LAYOUT"]
+    assert _shapes(_csr_params(c, ptr, idx, kv_indices_len=-1))[0] == E["PPA_ERR_SHAPE"]
+    # indptr decreasing, negative start, past the index array
+    bad = ptr.clone(); bad[1], bad[2] = bad[2], bad[1]
+    assert chk(p, bad, idx) == E["PPA_ERR_TABLE"]
+    bad = ptr.clone(); bad[0] = -1
+    assert chk(p, bad, idx) == E["PPA_ERR_TABLE"]
+    bad = ptr.clone(); bad[-1] = bad[-1] + 1
+    assert chk(p, bad, idx) == E["PPA_ERR_TABLE"]
+    # too few pages for a request, page id out of range
+    bad = ptr.clone(); bad[1] = 0
+    assert chk(p, bad, idx) == E["PPA_ERR_TABLE"]
+    badi = idx.clone(); badi[0] = 8
+    assert chk(p, ptr, badi) == E["PPA_ERR_TABLE"]
+    badi[0] = -1
+    assert chk(p, ptr, badi) == E["PPA_ERR_TABLE"]
+    # last_page_len inconsistent with seq_lens, or a slack page with last_page_len
+    badl = last.clone(); badl[0] += 1
+    assert chk(p, ptr, idx, badl) == E["PPA_ERR_TABLE"]
+    badl = last.clone(); badl[2] = 0
+    assert chk(p, ptr, idx, badl) == E["PPA_ERR_TABLE"]
+    ptr2, idx2, _ = _csr(c, slack=1)
+    p2 = _csr_params(c, ptr2, idx2)
+    assert chk(p2, ptr2, idx2, last) == E["PPA_ERR_TABLE"]
+    # the padded form still requires block_tables
+    with pytest.raises(ValueError):
+        B.make_params(c["q"], c["kv"], None, None, c["sl"], c["max_q"], c["max_kv"], 0.125, 1.0, c["B"],
+                      c["cuq"], c["cukv"], c["W"], c["out"], c["layout"], None)

@@ -19,7 +19,7 @@ import torch
 from gpu_helpers import (assert_close, errors, guard_rows_untouched, run_gpu, to_device, workspace)
 from oracle.case_io import decode_tensor, oracle_inputs, run_oracle, run_oracle_rows
 from workloads import make_case, make_custom_case
-from workloads.cases import relayout
+from workloads.cases import relayout, to_flat_page_table
 
 pytestmark = pytest.mark.gpu
 
@@ -306,3 +306,58 @@ def test_rejects_small_or_misaligned_workspace():
                             d["cum_seq_lens_q"], d["cum_seq_lens_kv"], -1, out, d["kv_layout"], None)
         with pytest.raises(ppa.PpaError):
             ppa.ppa_paged_prefill_attention(p)
+
+
+# --------------------------------------------------------------------------
+# the flat (CSR) page table: the same pages as the padded table
+# --------------------------------------------------------------------------
+
+FLAT_CASES = {
+    "hnd_p16_d128": dict(num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                         q_lens=(100, 0, 260), prefix_lens=(30, 9, 0)),
+    "nhd_p4_d64_window_sinks": dict(num_qo_heads=16, num_kv_heads=2, head_dim=64, page_size=4,
+                                    kv_layout="NHD", window_left=40, sinks=True,
+                                    q_lens=(70, 33), prefix_lens=(10, 90)),
+    "combined_p64_fp8": dict(num_qo_heads=16, num_kv_heads=2, head_dim=128, page_size=64,
+                             kv_form="combined", kv_dtype="fp8_e4m3fn", q_lens=(150,), prefix_lens=(300,)),
+    "empty_and_ragged": dict(num_qo_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
+                             q_lens=(0, 50, 0, 3), prefix_lens=(0, 0, 7, 0), extra_tokens=3),
+}
+
+
+@pytest.mark.parametrize("name", list(FLAT_CASES))
+@pytest.mark.parametrize("slack,lead", [(0, 0), (3, 5)])
+def test_flat_page_table_bitwise(name, slack, lead):
+    case = make_custom_case(name=name, batch=len(FLAT_CASES[name]["q_lens"]),
+                            seed=zlib.crc32(name.encode()) % 10000, **FLAT_CASES[name])
+    flat = to_flat_page_table(case, slack=slack, lead=lead, seed=9)
+    _say("flat", name, slack, lead)
+    want, written = run_oracle(flat)
+    padded = run_gpu(to_device(case))
+    d = to_device(flat)
+    got = run_gpu(d)
+    got_grid = run_gpu(d, schedule="grid")
+    torch.cuda.synchronize()
+    assert guard_rows_untouched(got, written)
+    assert torch.equal(got.view(torch.int16), padded.view(torch.int16)), "flat != padded table"
+    assert torch.equal(got_grid.view(torch.int16), padded.view(torch.int16))
+    assert_close(got, want, written, fp8=case["kv_dtype"] != "bf16", what=name)
+
+
+def test_flat_page_table_gather():
+    import paged_kv_prefill_varlen_amd as ppa
+    case = make_custom_case(batch=3, num_qo_heads=4, num_kv_heads=2, q_lens=(40, 0, 130),
+                            prefix_lens=(100, 7, 3), seed=12, page_size=8, head_dim=64, kv_layout="NHD")
+    flat = to_flat_page_table(case, slack=2, lead=4, seed=3)
+    d = to_device(flat)
+    out = torch.empty_like(d["query"])
+    p = ppa.make_params(d["query"], d["kv_cache"], None, None, d["seq_lens"], d["max_q_len"], d["max_kv_len"],
+                        1.0, 1.0, d["batch_size"], d["cum_seq_lens_q"], d["cum_seq_lens_kv"], -1, out,
+                        d["kv_layout"], None, d["kv_indptr"], d["kv_indices"], None)
+    rows = sum(case["kv_lens"])
+    for kv_idx, logical in ((0, case["logical_k"]), (1, case["logical_v"])):
+        dst = torch.zeros((rows, case["num_kv_heads"], case["head_dim"]), dtype=case["cache_dtype"], device="cuda")
+        ppa.ppa_gather_paged_kv(p, kv_idx, dst)
+        torch.cuda.synchronize()
+        want = torch.cat(logical, dim=0)
+        assert torch.equal(dst.cpu().view(torch.uint8), want.contiguous().view(torch.uint8))

@@ -115,6 +115,17 @@ MUTANTS["slot_shift"] = ("_page_rows", _slot_shift)
 MUTANTS["hnd_reshaped_not_transposed"] = ("_page_rows", _hnd_reshaped)
 MUTANTS["e4m3_bias_8"] = ("E4M3FN_TABLE", _bad_table())
 MUTANTS["bf16_shift_15"] = ("decode_bf16", _bf16_shift_15)
+_orig_pages = OA.request_pages
+
+
+def _flat_off_by_one(b, block_tables, kv_indptr=None, kv_indices=None):
+    # the flat table read one entry late (indptr taken as exclusive start)
+    if kv_indptr is not None:
+        return np.asarray(kv_indices)[int(kv_indptr[b]) + 1:int(kv_indptr[b + 1]) + 1]
+    return _orig_pages(b, block_tables)
+
+
+MUTANTS["flat_table_off_by_one"] = ("request_pages", _flat_off_by_one)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

@@ -343,6 +343,33 @@ def relayout(case: dict, kv_layout: Optional[str] = None, kv_form: Optional[str]
     return out
 
 
+def to_flat_page_table(case: dict, slack: int = 0, lead: int = 0, seed: int = 0) -> dict:
+    """The same case with the flat page table (kv_indptr / kv_indices /
+    kv_last_page_len, the indptr form of the TensorRT-LLM attention-backend
+    article) in place of block_tables.  Each request lists exactly the pages
+    it uses; with ``slack`` > 0 every request gets that many extra (random,
+    never read) page ids after its own, and ``lead`` junk entries come before
+    request 0 (kv_indptr[0] = lead).  kv_last_page_len is given only when
+    there is no slack (the page count then fixes seq_lens)."""
+    rng = np.random.default_rng(seed)
+    P = case["page_size"]
+    bt = case["block_tables"].numpy()
+    indptr = [lead]
+    indices = list(rng.integers(-5, case["num_pages"] + 5, size=lead))
+    last = []
+    for b, kv in enumerate(case["kv_lens"]):
+        n = (kv + P - 1) // P
+        indices += [int(x) for x in bt[b, :n]]
+        indices += [int(x) for x in rng.integers(-5, case["num_pages"] + 5, size=slack)]
+        indptr.append(len(indices))
+        last.append(0 if n == 0 else kv - (n - 1) * P)
+    out = dict(case)
+    out.update(kv_indptr=torch.tensor(indptr, dtype=torch.int32),
+               kv_indices=torch.tensor(indices if indices else [0], dtype=torch.int32),
+               kv_last_page_len=None if slack else torch.tensor(last, dtype=torch.int32))
+    return out
+
+
 def as_codes(t: torch.Tensor) -> np.ndarray:
     """Raw storage codes of a bf16 / fp8 tensor as unsigned numpy integers
     (uint16 / uint8).  This is how values cross to the oracle, which decodes

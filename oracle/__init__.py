@@ -6,4 +6,5 @@ its HIP extension is missing rather than fall back to anything here.
 """
 from .paged_attention import (E4M3FN_TABLE, attention_one_request, attention_rows,  # noqa: F401
                               decode_bf16, decode_e4m3fn, e4m3fn_value, gather_paged_kv,
-                              paged_prefill_attention)
+                              log_sum_exp_rows, merge_states, paged_prefill_attention,
+                              paged_prefill_lse, partial_state)

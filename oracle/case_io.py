@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 from .paged_attention import (attention_rows, decode_bf16, decode_e4m3fn,
-                              paged_prefill_attention)
+                              paged_prefill_attention, paged_prefill_lse)
 
 
 def _codes(t: torch.Tensor) -> np.ndarray:
@@ -67,6 +67,12 @@ def run_oracle(case: dict, requests: Optional[Sequence[int]] = None,
     """``(out float64 [num_tokens, H_q, D], written bool [num_tokens])``."""
     a = inputs if inputs is not None else oracle_inputs(case)
     return paged_prefill_attention(requests=requests, **a)
+
+
+def run_oracle_lse(case: dict, inputs: Optional[dict] = None) -> np.ndarray:
+    """``lse float64 [num_tokens, H_q]`` (natural log, sink included)."""
+    a = dict(inputs if inputs is not None else oracle_inputs(case))
+    return paged_prefill_lse(**a)
 
 
 def run_oracle_rows(case: dict, rows: Sequence[Tuple[int, int]],

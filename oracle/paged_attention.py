@@ -200,6 +200,109 @@ def request_pages(b: int, block_tables: Optional[np.ndarray], kv_indptr: Optiona
     return np.asarray(block_tables[b])
 
 
+# ---------------------------------------------------------------------------
+# 4. Log-sum-exp, partial states and their merge
+# ---------------------------------------------------------------------------
+#
+# The softmax denominator of a row, kept as its natural logarithm, is what
+# lets attention over a split key set be recombined: a partial state is the
+# normalized output and log-denominator over a subset of the keys; merging
+# weights each part by exp(lse_part - lse_total).  Read from the sibling
+# decode call of the TokenSpeed backend source (the decode path of the
+# TRT-LLM MHA backend) and the split-KV row of the survey; the sink, a term
+# of the denominator only (API page, parameter sinks), is added once, at
+# the merge.
+
+
+def log_sum_exp_rows(s: np.ndarray, valid: np.ndarray, sink: Optional[float]) -> np.ndarray:
+    """``log(sum_valid exp(s_ij) [+ exp(sink)])`` per row; -inf for a row
+    with no valid key and no sink."""
+    s = np.where(valid, s, -np.inf)
+    m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
+    if sink is not None:
+        m = np.maximum(m, sink)
+    finite = np.isfinite(m)
+    mm = np.where(finite, m, 0.0)
+    tot = np.where(valid, np.exp(s - mm[:, None]), 0.0).sum(axis=1)
+    if sink is not None:
+        tot = tot + np.exp(sink - mm)
+    with np.errstate(divide="ignore"):
+        return np.where(finite, mm + np.log(tot), -np.inf)
+
+
+def partial_state(q: np.ndarray, k: np.ndarray, v: np.ndarray, bmm1_scale: float, bmm2_scale: float,
+                  window_left: int, key_begin: int, key_end: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of one request restricted to the keys in ``[key_begin,
+    key_end)`` (and the causal / window mask), without sinks: ``(o, lse)``
+    with ``o`` ``[q_len, H_q, D]`` normalized over that key subset (times
+    bmm2) and ``lse`` ``[q_len, H_q]``.  A row with no valid key in the
+    subset gets ``o = 0`` and ``lse = -inf``."""
+    q_len, num_qo_heads, _ = q.shape
+    kv_len, num_kv_heads, _ = k.shape
+    mask = _valid_mask(q_len, kv_len, window_left)
+    sub = np.zeros(kv_len, dtype=bool)
+    sub[max(0, key_begin):max(0, min(kv_len, key_end))] = True
+    mask = mask & sub[None, :]
+    o = np.zeros((q_len, num_qo_heads, v.shape[2]), dtype=np.float64)
+    lse = np.full((q_len, num_qo_heads), -np.inf, dtype=np.float64)
+    rows = mask.any(axis=1)
+    for h in range(num_qo_heads):
+        hk = _kv_head(h, num_qo_heads, num_kv_heads)
+        s = bmm1_scale * (q[:, h, :] @ k[:, hk, :].T)
+        lse[:, h] = log_sum_exp_rows(s, mask, None)
+        if rows.any():
+            o[rows, h, :] = bmm2_scale * _softmax_weighted_sum(s[rows], mask[rows], v[:, hk, :], None)
+    return o, lse
+
+
+def merge_states(o_parts: np.ndarray, lse_parts: np.ndarray,
+                 sink: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Merge S partial states: ``o_parts`` ``[S, ..., D]``, ``lse_parts``
+    ``[S, ...]``; ``sink`` (broadcast against ``lse_parts[0]``) is one more
+    term of the total denominator.  ``lse = log(sum_s exp(lse_s) [+
+    exp(sink)])`` and ``o = sum_s exp(lse_s - lse) o_s``."""
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    terms = lse_parts if sink is None else np.concatenate(
+        [lse_parts, np.broadcast_to(np.asarray(sink, dtype=np.float64), lse_parts.shape[1:])[None]], axis=0)
+    m = terms.max(axis=0)
+    finite = np.isfinite(m)
+    mm = np.where(finite, m, 0.0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(finite, mm + np.log(np.exp(terms - mm).sum(axis=0)), -np.inf)
+    w = np.where(finite[None], np.exp(lse_parts - np.where(finite, lse, 0.0)[None]), 0.0)
+    o = (w[..., None] * np.asarray(o_parts, dtype=np.float64)).sum(axis=0)
+    return o, lse
+
+
+def paged_prefill_lse(query: np.ndarray, kv_cache, kv_layout: str, block_tables: Optional[np.ndarray],
+                      seq_lens: np.ndarray, cum_seq_lens_q: np.ndarray, page_size: int, bmm1_scale: float,
+                      bmm2_scale: float, window_left: int = -1, sinks: Optional[np.ndarray] = None,
+                      kv_indptr: Optional[np.ndarray] = None, kv_indices: Optional[np.ndarray] = None,
+                      requests: Optional[Sequence[int]] = None, chunk: int = 256) -> np.ndarray:
+    """``[num_tokens, H_q]`` natural-log softmax denominators of the batched
+    call (sink included); NaN in rows no request owns."""
+    num_tokens, num_qo_heads, _ = query.shape
+    lse = np.full((num_tokens, num_qo_heads), np.nan, dtype=np.float64)
+    todo = range(len(seq_lens)) if requests is None else requests
+    for b in todo:
+        q0, q1 = int(cum_seq_lens_q[b]), int(cum_seq_lens_q[b + 1])
+        q_len, kv_len = q1 - q0, int(seq_lens[b])
+        if q_len == 0:
+            continue
+        pages = request_pages(b, block_tables, kv_indptr, kv_indices)
+        k = gather_paged_kv(kv_cache, pages, 0, kv_len, page_size, kv_layout)
+        mask = _valid_mask(q_len, kv_len, window_left)
+        num_kv_heads = k.shape[1]
+        for h in range(num_qo_heads):
+            hk = _kv_head(h, num_qo_heads, num_kv_heads)
+            sink = None if sinks is None else float(sinks[h])
+            for r0 in range(0, q_len, chunk):
+                r1 = min(q_len, r0 + chunk)
+                s = bmm1_scale * (query[q0 + r0:q0 + r1, h, :] @ k[:, hk, :].T)
+                lse[q0 + r0:q0 + r1, h] = log_sum_exp_rows(s, mask[r0:r1], sink)
+    return lse
+
+
 def paged_prefill_attention(query: np.ndarray, kv_cache, kv_layout: str,
                             block_tables: Optional[np.ndarray], seq_lens: np.ndarray,
                             cum_seq_lens_q: np.ndarray, page_size: int,

@@ -431,6 +431,100 @@ def pin_flat_page_table():
     assert np.array_equal(base, got, equal_nan=True)
 
 
+def pin_lse_closed_forms():
+    """bmm1 = 0 makes every valid logit 0: lse = log(n_valid) (log(n_valid +
+    e^sink) with a sink); window 0 leaves the diagonal key alone:
+    lse = bmm1 q_i . k_(prefix+i)."""
+    case = _tiny(701, bmm1_scale=0.0, window_left=2)
+    lse = OA.paged_prefill_lse(**oracle_inputs(case))
+    cu = case["cum_seq_lens_q"].numpy()
+    for b, (q_len, kv_len) in enumerate(zip(case["q_lens"], case["kv_lens"])):
+        pre = kv_len - q_len
+        for i in range(q_len):
+            n = min(pre + i, 2) + 1
+            assert np.allclose(lse[cu[b] + i], math.log(n), rtol=0, atol=1e-13)
+    sinks = torch.tensor([0.5, -1.0, 2.0, -3.0])
+    case = _tiny(702, bmm1_scale=0.0, sinks=True)
+    case["sinks"] = sinks
+    lse = OA.paged_prefill_lse(**oracle_inputs(case))
+    for b, (q_len, kv_len) in enumerate(zip(case["q_lens"], case["kv_lens"])):
+        pre = kv_len - q_len
+        for i in range(q_len):
+            for h in range(4):
+                want = math.log(pre + i + 1 + math.exp(float(sinks[h])))
+                assert abs(lse[cu[b] + i, h] - want) < 1e-12
+    case = _tiny(703, window_left=0)
+    a = oracle_inputs(case)
+    lse = OA.paged_prefill_lse(**a)
+    q = a["query"]
+    for b, (q_len, kv_len) in enumerate(zip(case["q_lens"], case["kv_lens"])):
+        pre = kv_len - q_len
+        k = decode_tensor(case["logical_k"][b])
+        for i in range(q_len):
+            for h in range(4):
+                s_ii = a["bmm1_scale"] * float(q[cu[b] + i, h] @ k[pre + i, h // 2])
+                assert abs(lse[cu[b] + i, h] - s_ii) < 1e-12
+
+
+def pin_lse_brute_force():
+    """Against scipy's logsumexp over logits formed key by key from the
+    pages, with the sink as one more term."""
+    from scipy.special import logsumexp
+    case = _tiny(704, sinks=True, window_left=4)
+    a = oracle_inputs(case)
+    lse = OA.paged_prefill_lse(**a)
+    q, bt, P = a["query"], a["block_tables"], case["page_size"]
+    kplane = a["kv_cache"][0]
+    cu = case["cum_seq_lens_q"].numpy()
+    for b, (q_len, kv_len) in enumerate(zip(case["q_lens"], case["kv_lens"])):
+        pre = kv_len - q_len
+        for i in range(q_len):
+            pos = pre + i
+            for h in range(4):
+                terms = [float(a["sinks"][h])]
+                for j in range(max(0, pos - 4), pos + 1):
+                    krow = kplane[bt[b][j // P], h // 2, j % P]   # HND: [page, head, slot, dim]
+                    terms.append(a["bmm1_scale"] * float(q[cu[b] + i, h] @ krow))
+                assert abs(lse[cu[b] + i, h] - logsumexp(terms)) < 1e-12
+
+
+def pin_merge_of_key_splits_is_full():
+    """Partial states over a partition of the keys (one part empty, one past
+    the causal band), merged with the sink, give the full output and lse."""
+    case = _tiny(705, sinks=True, window_left=5, q_lens=(6, 9), prefix_lens=(4, 2), batch=2)
+    a = oracle_inputs(case)
+    full, _ = OA.paged_prefill_attention(**a)
+    full_lse = OA.paged_prefill_lse(**a)
+    cu = case["cum_seq_lens_q"].numpy()
+    for b, kv_len in enumerate(case["kv_lens"]):
+        q = a["query"][cu[b]:cu[b + 1]]
+        k = OA.gather_paged_kv(a["kv_cache"], a["block_tables"][b], 0, kv_len, case["page_size"], "HND")
+        v = OA.gather_paged_kv(a["kv_cache"], a["block_tables"][b], 1, kv_len, case["page_size"], "HND")
+        cuts = [0, 3, 3, 7, kv_len, kv_len + 4]
+        parts = [OA.partial_state(q, k, v, a["bmm1_scale"], a["bmm2_scale"], 5, c0, c1)
+                 for c0, c1 in zip(cuts, cuts[1:])]
+        o, lse = OA.merge_states(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]),
+                                 a["sinks"][None, :])
+        assert np.allclose(o, full[cu[b]:cu[b + 1]], rtol=1e-12, atol=1e-12)
+        assert np.allclose(lse, full_lse[cu[b]:cu[b + 1]], rtol=1e-12, atol=1e-12)
+
+
+def pin_merge_identities():
+    """One part merges to itself; an empty part (o 0, lse -inf) changes
+    nothing; the order of parts does not matter."""
+    rng = np.random.default_rng(706)
+    o = rng.standard_normal((3, 5, 2, 8))
+    lse = rng.standard_normal((3, 5, 2)) * 4
+    o1, l1 = OA.merge_states(o[:1], lse[:1])
+    assert np.allclose(o1, o[0], rtol=1e-14, atol=1e-14) and np.allclose(l1, lse[0], rtol=1e-14, atol=1e-14)
+    base_o, base_l = OA.merge_states(o, lse)
+    eo, el = OA.merge_states(np.concatenate([o, np.zeros((1, 5, 2, 8))]),
+                             np.concatenate([lse, np.full((1, 5, 2), -np.inf)]))
+    assert np.allclose(eo, base_o, rtol=1e-14, atol=1e-14) and np.allclose(el, base_l, rtol=1e-14, atol=1e-14)
+    po, pl = OA.merge_states(o[::-1], lse[::-1])
+    assert np.allclose(po, base_o, rtol=1e-13, atol=1e-13) and np.allclose(pl, base_l, rtol=1e-13, atol=1e-13)
+
+
 ALL_PINS = [
     pin_bf16_decode_all_codes,
     pin_e4m3fn_decode_all_codes,
@@ -451,4 +545,8 @@ ALL_PINS = [
     pin_bmm2_linear,
     pin_gqa_equals_repeated_mha,
     pin_flat_page_table,
+    pin_lse_closed_forms,
+    pin_lse_brute_force,
+    pin_merge_of_key_splits_is_full,
+    pin_merge_identities,
 ]

@@ -126,6 +126,17 @@ def _flat_off_by_one(b, block_tables, kv_indptr=None, kv_indices=None):
 
 
 MUTANTS["flat_table_off_by_one"] = ("request_pages", _flat_off_by_one)
+_orig_lse = OA.log_sum_exp_rows
+_orig_merge = OA.merge_states
+_orig_partial = OA.partial_state
+MUTANTS["lse_in_log2_units"] = ("log_sum_exp_rows", lambda s, valid, sink: _orig_lse(s, valid, sink) / np.log(2.0))
+MUTANTS["lse_sink_ignored"] = ("log_sum_exp_rows", lambda s, valid, sink: _orig_lse(s, valid, None))
+MUTANTS["merge_sink_ignored"] = ("merge_states", lambda o, lse, sink=None: _orig_merge(o, lse, None))
+MUTANTS["merge_plain_mean"] = ("merge_states",
+                               lambda o, lse, sink=None: (np.mean(o, axis=0), _orig_merge(o, lse, sink)[1]))
+MUTANTS["partial_ignores_key_range"] = ("partial_state",
+                                        lambda q, k, v, b1, b2, w, k0, k1: _orig_partial(q, k, v, b1, b2, w, 0,
+                                                                                         k.shape[0]))
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PPA_ABI_VERSION 2
+#define PPA_ABI_VERSION 3
 
 typedef enum ppa_status {
   PPA_OK = 0,
@@ -202,7 +202,49 @@ typedef struct ppa_params {
   const int32_t* kv_indices;
   int64_t kv_indices_len;
   const int32_t* kv_last_page_len;
+
+  /* Log-sum-exp output, optional: fp32 [num_tokens, num_qo_heads] with
+     strides lse_strides (elements), the natural log of each row's softmax
+     denominator, log(sum_valid e^{s_ij} + [sinks] e^{sinks[h]}) with
+     s_ij = bmm1_scale * q_i . k_j.  Written for the same rows as out; NULL:
+     not written.  With it, partial results over disjoint key sets can be
+     combined by ppa_merge_attention_states. */
+  float* lse;
+  int64_t lse_strides[2];
+
+  /* Split-KV: the key tiles of every work item are divided into kv_splits
+     chunks (0 or 1: no split; at most 256) processed by separate
+     workgroups.  Each chunk's partial output and log-sum-exp go to the
+     workspace, which is then required and must hold ppa_workspace_bytes(p)
+     bytes; a merge pass in the same call combines them and adds the sink
+     once.  The result equals the unsplit call up to fp32 summation order. */
+  int32_t kv_splits;
 } ppa_params;
+
+/*
+ * Partial attention states to combine (log-sum-exp merge): part s holds, per
+ * (row, head), an output o_s normalized over its own key set and that set's
+ * log-denominator lse_s (natural log; -inf for an empty set).  The merge
+ * writes out = sum_s e^{lse_s - L} o_s with L = log(sum_s e^{lse_s} +
+ * [sinks] e^{sinks[h]}), and L to lse_out.  Use: combining calls that each
+ * saw a slice of the KV (context parallelism), sinks given only here.
+ */
+typedef struct ppa_merge_params {
+  uint32_t abi_version;
+  uint32_t struct_size;
+  int32_t num_parts;          /* >= 1 */
+  int32_t num_rows;           /* >= 0 (tokens) */
+  int32_t num_heads;          /* >= 1 */
+  int32_t head_dim;           /* 64 or 128 */
+  const float* o_parts;       /* [num_parts, num_rows, num_heads, head_dim] fp32, contiguous */
+  const float* lse_parts;     /* [num_parts, num_rows, num_heads] fp32, contiguous */
+  const float* sinks;         /* [num_heads] fp32 or NULL */
+  void* out;                  /* [num_rows, num_heads, head_dim], dtype out_dtype (bf16) */
+  int32_t out_dtype;
+  int64_t out_strides[3];     /* elements; out_strides[2] == 1, the others even */
+  float* lse_out;             /* [num_rows, num_heads] fp32 or NULL */
+  int64_t lse_out_strides[2];
+} ppa_merge_params;
 
 /* ABI guards for bindings: the version this library was built with and
    sizeof(ppa_params). */
@@ -249,8 +291,10 @@ int32_t ppa_validate_page_table_csr_host(const ppa_params* p, const int32_t* seq
                                          const int32_t* kv_indptr, const int32_t* kv_indices,
                                          const int32_t* kv_last_page_len, char* msg, size_t msg_len);
 
-/* Bytes of workspace the balanced schedule uses (a small constant; p may be
-   NULL). */
+/* Bytes of workspace a call needs: 256 for the balanced schedule's counters,
+   plus the partial outputs and log-sum-exps of split-KV (kv_splits > 1:
+   kv_splits * num_tokens * num_qo_heads * (head_dim + 1) * 4 bytes, each
+   array rounded up to 256).  p may be NULL (then 256). */
 size_t ppa_workspace_bytes(const ppa_params* p);
 
 /*
@@ -262,6 +306,17 @@ size_t ppa_workspace_bytes(const ppa_params* p);
  * and table columns are clamped, query rows are bounded by num_tokens).
  */
 int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream);
+
+/*
+ * Combine partial attention states (see ppa_merge_params); enqueued on
+ * `stream`, no host synchronisation, no allocation.  Returns PPA_ERR_ABI,
+ * PPA_ERR_NULL_POINTER, PPA_ERR_SHAPE, PPA_ERR_HEAD_DIM, PPA_ERR_DTYPE,
+ * PPA_ERR_STRIDE or PPA_ERR_ALIGNMENT for bad arguments.
+ */
+int32_t ppa_merge_attention_states(const ppa_merge_params* m, void* stream);
+
+/* sizeof(ppa_merge_params) of this build, for bindings. */
+size_t ppa_merge_params_size(void);
 
 /*
  * Address-unit check: copies the first seq_lens[b] K (kv_idx 0) or V

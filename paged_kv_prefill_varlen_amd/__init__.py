@@ -8,7 +8,8 @@ only marshals torch tensors into ``ppa_params``.  Every step of the
 attention runs in the HIP kernels; there is no fallback: importing this
 package without the built library raises ImportError.
 """
-from .binding import (PPA_ABI_VERSION, WORKSPACE_BYTES, PpaError, PpaParams, batch_context_with_kv_cache,  # noqa: F401
+from .binding import (PPA_ABI_VERSION, WORKSPACE_BYTES, PpaError, PpaMergeParams, ppa_merge_attention_states,
+                      ppa_merge_params_size, PpaParams, batch_context_with_kv_cache,  # noqa: F401
                       library_path, make_params, ppa_abi_version, ppa_gather_paged_kv,
                       ppa_paged_prefill_attention, ppa_params_size, ppa_strerror,
                       ppa_validate_metadata_host, ppa_validate_page_table_csr_host, ppa_validate_shapes,

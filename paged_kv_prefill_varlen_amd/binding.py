@@ -14,7 +14,7 @@ from typing import Optional, Sequence, Tuple, Union
 import numpy as np
 import torch
 
-PPA_ABI_VERSION = 2
+PPA_ABI_VERSION = 3
 
 # enums of ppa.h
 PPA_DTYPE_BF16 = 1
@@ -79,6 +79,28 @@ class PpaParams(ctypes.Structure):
         ("kv_indices", c_void_p),
         ("kv_indices_len", c_int64),
         ("kv_last_page_len", c_void_p),
+        ("lse", c_void_p),
+        ("lse_strides", c_int64 * 2),
+        ("kv_splits", c_int32),
+    ]
+
+
+class PpaMergeParams(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", c_uint32),
+        ("struct_size", c_uint32),
+        ("num_parts", c_int32),
+        ("num_rows", c_int32),
+        ("num_heads", c_int32),
+        ("head_dim", c_int32),
+        ("o_parts", c_void_p),
+        ("lse_parts", c_void_p),
+        ("sinks", c_void_p),
+        ("out", c_void_p),
+        ("out_dtype", c_int32),
+        ("out_strides", c_int64 * 3),
+        ("lse_out", c_void_p),
+        ("lse_out_strides", c_int64 * 2),
     ]
 
 
@@ -105,6 +127,8 @@ def _load():
         "ppa_workspace_bytes": (c_size_t, [P]),
         "ppa_paged_prefill_attention": (c_int32, [P, c_void_p]),
         "ppa_gather_paged_kv": (c_int32, [P, c_int32, c_void_p, c_int64, c_void_p]),
+        "ppa_merge_attention_states": (c_int32, [ctypes.POINTER(PpaMergeParams), c_void_p]),
+        "ppa_merge_params_size": (c_size_t, []),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -112,6 +136,9 @@ def _load():
         fn.argtypes = args
     if lib.ppa_abi_version() != PPA_ABI_VERSION:
         raise ImportError(f"{_LIB_PATH}: ABI version {lib.ppa_abi_version()}, binding expects {PPA_ABI_VERSION}")
+    if lib.ppa_merge_params_size() != ctypes.sizeof(PpaMergeParams):
+        raise ImportError(f"{_LIB_PATH}: sizeof(ppa_merge_params) {lib.ppa_merge_params_size()} != binding's "
+                          f"{ctypes.sizeof(PpaMergeParams)}")
     if lib.ppa_params_size() != ctypes.sizeof(PpaParams):
         raise ImportError(f"{_LIB_PATH}: sizeof(ppa_params) {lib.ppa_params_size()} != binding's "
                           f"{ctypes.sizeof(PpaParams)}")
@@ -225,6 +252,47 @@ def ppa_gather_paged_kv(params: PpaParams, kv_idx: int, dst: torch.Tensor, strea
         raise PpaError(st, msg)
 
 
+def ppa_merge_params_size() -> int:
+    return int(_lib.ppa_merge_params_size())
+
+
+def ppa_merge_attention_states(o_parts: torch.Tensor, lse_parts: torch.Tensor, out: torch.Tensor,
+                               lse_out: Optional[torch.Tensor] = None, sinks: Optional[torch.Tensor] = None,
+                               stream=None) -> None:
+    """Log-sum-exp merge of partial states: ``o_parts`` fp32 ``[S, rows,
+    heads, D]`` and ``lse_parts`` fp32 ``[S, rows, heads]`` (contiguous),
+    into ``out`` bf16 ``[rows, heads, D]`` and optionally ``lse_out`` fp32
+    ``[rows, heads]``; ``sinks`` fp32 ``[heads]`` adds one denominator term."""
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise TypeError("o_parts and lse_parts must be float32")
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
+        raise ValueError("o_parts and lse_parts must be contiguous")
+    if o_parts.dim() != 4 or lse_parts.shape != o_parts.shape[:3] or tuple(out.shape) != tuple(o_parts.shape[1:]):
+        raise ValueError("shapes: o_parts [S, rows, heads, D], lse_parts [S, rows, heads], out [rows, heads, D]")
+    m = PpaMergeParams()
+    m.abi_version = PPA_ABI_VERSION
+    m.struct_size = ctypes.sizeof(PpaMergeParams)
+    m.num_parts, m.num_rows, m.num_heads, m.head_dim = (int(x) for x in o_parts.shape)
+    m.o_parts = _ptr(o_parts)
+    m.lse_parts = _ptr(lse_parts)
+    if sinks is not None:
+        if sinks.dtype != torch.float32 or sinks.numel() != m.num_heads or not sinks.is_contiguous():
+            raise ValueError("sinks must be a contiguous float32 tensor of num_heads values")
+        m.sinks = _ptr(sinks)
+    m.out = _ptr(out)
+    m.out_dtype = _dt(out)
+    m.out_strides[:] = list(out.stride())
+    if lse_out is not None:
+        if lse_out.dtype != torch.float32 or tuple(lse_out.shape) != tuple(o_parts.shape[1:3]):
+            raise ValueError("lse_out must be float32 [rows, heads]")
+        m.lse_out = _ptr(lse_out)
+        m.lse_out_strides[:] = list(lse_out.stride())
+    h = _stream_handle(out.device, stream)
+    st = _lib.ppa_merge_attention_states(ctypes.byref(m), c_void_p(h))
+    if st != 0:
+        raise PpaError(st, "merge arguments rejected")
+
+
 # --------------------------------------------------------------------------
 # marshalling torch tensors -> ppa_params
 # --------------------------------------------------------------------------
@@ -255,7 +323,8 @@ def make_params(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.
                 cum_seq_lens_kv: Optional[torch.Tensor], window_left: int, out: torch.Tensor,
                 kv_layout: str = "HND", sinks=None, kv_indptr: Optional[torch.Tensor] = None,
                 kv_indices: Optional[torch.Tensor] = None,
-                kv_last_page_len: Optional[torch.Tensor] = None) -> PpaParams:
+                kv_last_page_len: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                kv_splits: int = 0) -> PpaParams:
     """Fill a PpaParams from torch tensors (the FlashInfer API page's argument
     list).  With kv_indptr / kv_indices the flat (CSR) page table is used and
     block_tables may be None.  Keeps no reference to the tensors: the caller
@@ -358,6 +427,12 @@ def make_params(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.
     p.out = _ptr(out)
     p.out_dtype = _dt(out)
     p.out_strides[:] = list(out.stride())
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(query.shape[:2]):
+            raise ValueError("lse must be float32 [num_tokens, num_qo_heads]")
+        p.lse = _ptr(lse)
+        p.lse_strides[:] = list(lse.stride())
+    p.kv_splits = int(kv_splits)
     return p
 
 
@@ -368,18 +443,21 @@ def batch_context_with_kv_cache(query: torch.Tensor, kv_cache, workspace_buffer:
                                 window_left: int = -1, out: Optional[torch.Tensor] = None,
                                 out_dtype=None, kv_layout: str = "HND", sinks=None,
                                 validate: bool = False, stream=None, kv_indptr=None, kv_indices=None,
-                                kv_last_page_len=None) -> torch.Tensor:
+                                kv_last_page_len=None, lse: Optional[torch.Tensor] = None,
+                                kv_splits: int = 0) -> torch.Tensor:
     """Batched paged prefill attention; argument list of the API page
     (without the nvfp4 output and PDL options), plus the optional flat page
     table (kv_indptr / kv_indices / kv_last_page_len) in place of
-    block_tables.  ``validate=True`` also runs the deep metadata check on host
-    copies (a device-to-host sync)."""
+    block_tables, an optional fp32 ``lse`` [num_tokens, num_qo_heads] output
+    (natural-log softmax denominators) and ``kv_splits`` (split-KV; needs a
+    workspace of ``ppa_workspace_bytes`` bytes).  ``validate=True`` also runs
+    the deep metadata check on host copies (a device-to-host sync)."""
     if out is None:
         dt = query.dtype if out_dtype is None else out_dtype
         out = torch.empty(query.shape, dtype=dt, device=query.device)
     p = make_params(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_q_len, max_kv_len,
                     bmm1_scale, bmm2_scale, batch_size, cum_seq_lens_q, cum_seq_lens_kv, window_left,
-                    out, kv_layout, sinks, kv_indptr, kv_indices, kv_last_page_len)
+                    out, kv_layout, sinks, kv_indptr, kv_indices, kv_last_page_len, lse, kv_splits)
     if validate:
         st, msg = ppa_validate_metadata_host(p, cum_seq_lens_q, cum_seq_lens_kv, seq_lens, block_tables)
         if st == 0 and p.page_table_form == PPA_PAGE_TABLE_CSR:

@@ -61,6 +61,7 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 constexpr int kBK = 64;            // keys per tile
 constexpr int kWaves = 8;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kMinScale = 1.17549435e-38f;  // FLT_MIN
@@ -100,8 +101,14 @@ struct AttnArgs {
   const float* bmm2_ptr;
   const float* sinks;
   uint32_t* sched;     // persistent schedule: counters in the workspace
-  int32_t n_items;     // n_qt * batch * num_kv_heads * n_hg
+  int32_t n_items;     // n_qt * kv_splits * batch * num_kv_heads * n_hg
   int32_t n_queues;    // 1 or kSchedQueues
+  int32_t num_qo_heads;
+  float* lse;          // [tokens, H_q] natural-log denominators, or NULL
+  int64_t lse_tok, lse_head;
+  int32_t kv_splits;   // key-tile chunks per work item (1: none)
+  float* o_part;       // split mode: [kv_splits, tokens, H_q, D] partial outputs
+  float* lse_part;     // split mode: [kv_splits, tokens, H_q] partial log-denominators
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -321,9 +328,12 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   __shared__ __attribute__((aligned(16))) __bf16 vlds[2][T::V_ELEMS];
 
   // ---- which work item --------------------------------------------------
+  // item = (query tile from the last, key chunk, request, kv head, head group)
   const int R = a.batch * a.num_kv_heads * a.n_hg;
-  const int qt = a.n_qt - 1 - item / R;
+  const int S = a.kv_splits;
   const int rest = item % R;
+  const int split = (item / R) % S;
+  const int qt = a.n_qt - 1 - item / R / S;
   const int b = rest / (a.num_kv_heads * a.n_hg);
   const int hk = (rest / a.n_hg) % a.num_kv_heads;
   const int hg = rest % a.n_hg;
@@ -397,8 +407,14 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   const int pos_last = prefix + t0 + ntok - 1;
   const int key_hi = pos_last < kv_len - 1 ? pos_last : kv_len - 1;
   const int key_lo = W >= 0 ? (pos_first - W > 0 ? pos_first - W : 0) : 0;
-  const int tile_lo = key_lo / kBK;
-  const int tile_hi = key_hi >= 0 ? key_hi / kBK : -1;
+  int tile_lo = key_lo / kBK;
+  int tile_hi = key_hi >= 0 ? key_hi / kBK : -1;
+  if (S > 1 && tile_hi >= tile_lo) {   // this chunk's share of the key tiles
+    const int n = tile_hi - tile_lo + 1;
+    const int first = tile_lo;
+    tile_lo = first + (split * n) / S;
+    tile_hi = first + ((split + 1) * n) / S - 1;
+  }
 
   PageTable pt;
   request_table(pt, b, a.block_tables, a.bt_row_stride, a.bt_cols, a.kv_indptr, a.kv_indices, a.kv_indices_len);
@@ -525,9 +541,27 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   if (!rvalid) return;
   const int h = h0 + hd;
   const float mb = m_run == kNegInf ? 0.f : m_run;
+  const int64_t trow = q0 + t0 + tok;
+  if (S > 1) {
+    // partial state of this key chunk (no sink; a row with no key here
+    // gets 0 and -inf): output normalized over the chunk, log-denominator
+    const float pinv = l > 0.f ? bmm2 / l : 0.f;
+    const int64_t prow = (static_cast<int64_t>(split) * a.num_tokens + trow) * a.num_qo_heads + h;
+    float* dst = a.o_part + prow * D;
+    for (int md = 0; md < MD; ++md)
+      for (int g = 0; g < 4; ++g) {
+        const int d = md * 32 + 8 * g + 4 * half;
+        typedef __attribute__((ext_vector_type(4))) float f32x4;
+        *reinterpret_cast<f32x4*>(dst + d) = f32x4{oacc[md][4 * g] * pinv, oacc[md][4 * g + 1] * pinv,
+                                                   oacc[md][4 * g + 2] * pinv, oacc[md][4 * g + 3] * pinv};
+      }
+    if (half == 0) a.lse_part[prow] = l > 0.f ? mb * kLn2 + __builtin_logf(l) : kNegInf;
+    return;
+  }
   if (a.sinks) l += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - mb);
+  if (a.lse != nullptr && half == 0) a.lse[trow * a.lse_tok + static_cast<int64_t>(h) * a.lse_head] = mb * kLn2 + __builtin_logf(l);
   const float inv = bmm2 / l;
-  uint16_t* orow = a.out + static_cast<int64_t>(q0 + t0 + tok) * a.o_tok + static_cast<int64_t>(h) * a.o_head;
+  uint16_t* orow = a.out + trow * a.o_tok + static_cast<int64_t>(h) * a.o_head;
   for (int md = 0; md < MD; ++md) {
     for (int g = 0; g < 4; ++g) {
       const int d = md * 32 + 8 * g + 4 * half;
@@ -628,6 +662,71 @@ int log2_exact(int x) {
   return s;
 }
 
+// ---- log-sum-exp merge of partial states ------------------------------------
+// One wave per (row, head): the maximum of the parts' log-denominators (and
+// the sink), the weights e^{lse_s - max}, their sum, the weighted sum of the
+// parts' outputs; each lane owns D / 64 consecutive dims.
+struct MergeArgs {
+  const float* o_parts;     // [parts, rows, heads, D]
+  const float* lse_parts;   // [parts, rows, heads]
+  int32_t parts, rows, heads;
+  const int32_t* row_limit; // rows at or past *row_limit are skipped, or NULL
+  const float* sinks;       // [heads] or NULL
+  uint16_t* out;
+  int64_t o_row, o_head;
+  float* lse_out;
+  int64_t l_row, l_head;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs m) {
+  constexpr int E = D / 64;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= static_cast<int64_t>(m.rows) * m.heads) return;
+  const int row = static_cast<int>(w / m.heads);
+  const int h = static_cast<int>(w % m.heads);
+  if (m.row_limit != nullptr && row >= *m.row_limit) return;
+  const int64_t part_stride = static_cast<int64_t>(m.rows) * m.heads;
+  float mx = m.sinks ? m.sinks[h] : kNegInf;
+  for (int s = 0; s < m.parts; ++s) mx = fmaxf(mx, m.lse_parts[s * part_stride + w]);
+  float acc[E];
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  float den = 0.f;
+  if (mx > kNegInf) {
+    for (int s = 0; s < m.parts; ++s) {
+      const float ws = __expf(m.lse_parts[s * part_stride + w] - mx);
+      den += ws;
+      if (ws > 0.f) {
+        const float* src = m.o_parts + (s * part_stride + w) * D + lane * E;
+        for (int e = 0; e < E; ++e) acc[e] += ws * src[e];
+      }
+    }
+    if (m.sinks) den += __expf(m.sinks[h] - mx);
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  uint16_t* orow = m.out + row * m.o_row + h * m.o_head + lane * E;
+  if constexpr (E == 2) {
+    *reinterpret_cast<uint32_t*>(orow) = pack_bf16(acc[0] * inv, acc[1] * inv);
+  } else {
+    *orow = static_cast<uint16_t>(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
+  }
+  if (m.lse_out != nullptr && lane == 0)
+    m.lse_out[row * m.l_row + h * m.l_head] = den > 0.f ? mx + __builtin_logf(den) : kNegInf;
+}
+
+hipError_t launch_merge(const MergeArgs& m, int head_dim, hipStream_t stream) {
+  const int64_t waves = static_cast<int64_t>(m.rows) * m.heads;
+  if (waves == 0) return hipSuccess;
+  const int64_t blocks = (waves + 3) / 4;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, m);
+  else
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, m);
+  return hipGetLastError();
+}
+
 // Workgroups of a persistent kernel that the device holds at once (cached per
 // device and kernel).
 template <int D, bool FP8, bool UPAGE>
@@ -718,8 +817,20 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
   a.bmm2_ptr = p->bmm2_scale_ptr;
   a.sinks = p->sinks;
   a.sched = static_cast<uint32_t*>(p->workspace);
+  a.num_qo_heads = p->num_qo_heads;
+  a.lse = p->lse;
+  a.lse_tok = p->lse_strides[0];
+  a.lse_head = p->lse_strides[1];
+  a.kv_splits = p->kv_splits > 1 ? p->kv_splits : 1;
+  if (a.kv_splits > 1) {
+    // workspace: counters, then the partial outputs, then their log-denominators
+    uint8_t* ws = static_cast<uint8_t*>(p->workspace);
+    const size_t rows = static_cast<size_t>(a.kv_splits) * p->num_tokens * p->num_qo_heads;
+    a.o_part = reinterpret_cast<float*>(ws + 256);
+    a.lse_part = reinterpret_cast<float*>(ws + 256 + (rows * p->head_dim * sizeof(float) + 255) / 256 * 256);
+  }
 
-  const int64_t grid = static_cast<int64_t>(a.n_qt) * a.batch * a.num_kv_heads * a.n_hg;
+  const int64_t grid = static_cast<int64_t>(a.n_qt) * a.kv_splits * a.batch * a.num_kv_heads * a.n_hg;
   if (grid > 0x7fffffff) return PPA_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -738,7 +849,55 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
     e = fp8 ? launch<128, true>(a, g, s, upage) : launch<128, false>(a, g, s, upage);
   else
     e = fp8 ? launch<64, true>(a, g, s, upage) : launch<64, false>(a, g, s, upage);
+  if (e == hipSuccess && a.kv_splits > 1) {
+    MergeArgs m{};
+    m.o_parts = a.o_part;
+    m.lse_parts = a.lse_part;
+    m.parts = a.kv_splits;
+    m.rows = p->num_tokens;
+    m.heads = p->num_qo_heads;
+    m.row_limit = p->cum_seq_lens_q + p->batch_size;
+    m.sinks = p->sinks;
+    m.out = static_cast<uint16_t*>(p->out);
+    m.o_row = a.o_tok;
+    m.o_head = a.o_head;
+    m.lse_out = p->lse;
+    m.l_row = p->lse_strides[0];
+    m.l_head = p->lse_strides[1];
+    e = launch_merge(m, p->head_dim, s);
+  }
   return e == hipSuccess ? PPA_OK : PPA_ERR_HIP;
+}
+
+extern "C" int32_t ppa_merge_attention_states(const ppa_merge_params* mp, void* stream) {
+  if (mp == nullptr) return PPA_ERR_NULL_POINTER;
+  if (mp->abi_version != PPA_ABI_VERSION || mp->struct_size != sizeof(ppa_merge_params)) return PPA_ERR_ABI;
+  if (mp->num_parts < 1 || mp->num_rows < 0 || mp->num_heads < 1) return PPA_ERR_SHAPE;
+  if (mp->head_dim != 64 && mp->head_dim != 128) return PPA_ERR_HEAD_DIM;
+  if (mp->out_dtype != PPA_DTYPE_BF16) return PPA_ERR_DTYPE;
+  if (mp->num_rows == 0) return PPA_OK;
+  if (mp->o_parts == nullptr || mp->lse_parts == nullptr || mp->out == nullptr) return PPA_ERR_NULL_POINTER;
+  if (mp->out_strides[2] != 1 || mp->out_strides[0] < 0 || mp->out_strides[1] < 0 ||
+      (mp->out_strides[0] & 1) != 0 || (mp->out_strides[1] & 1) != 0)
+    return PPA_ERR_STRIDE;
+  if (mp->lse_out != nullptr && (mp->lse_out_strides[0] < 0 || mp->lse_out_strides[1] < 0)) return PPA_ERR_STRIDE;
+  auto mis = [](const void* x, uintptr_t a) { return (reinterpret_cast<uintptr_t>(x) & (a - 1)) != 0; };
+  if (mis(mp->o_parts, 4) || mis(mp->lse_parts, 4) || mis(mp->out, 4) || mis(mp->sinks, 4) || mis(mp->lse_out, 4))
+    return PPA_ERR_ALIGNMENT;
+  MergeArgs m{};
+  m.o_parts = mp->o_parts;
+  m.lse_parts = mp->lse_parts;
+  m.parts = mp->num_parts;
+  m.rows = mp->num_rows;
+  m.heads = mp->num_heads;
+  m.sinks = mp->sinks;
+  m.out = static_cast<uint16_t*>(mp->out);
+  m.o_row = mp->out_strides[0];
+  m.o_head = mp->out_strides[1];
+  m.lse_out = mp->lse_out;
+  m.l_row = mp->lse_out_strides[0];
+  m.l_head = mp->lse_out_strides[1];
+  return launch_merge(m, mp->head_dim, static_cast<hipStream_t>(stream)) == hipSuccess ? PPA_OK : PPA_ERR_HIP;
 }
 
 extern "C" int32_t ppa_gather_paged_kv(const ppa_params* p, int32_t kv_idx, void* dst, int64_t dst_rows,

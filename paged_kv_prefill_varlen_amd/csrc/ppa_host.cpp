@@ -123,8 +123,13 @@ const char* ppa_strerror(int32_t status) {
 }
 
 size_t ppa_workspace_bytes(const ppa_params* p) {
-  (void)p;
-  return 256;   // scheduler counters (9 x uint32), rounded up
+  size_t bytes = 256;   // scheduler counters (9 x uint32), rounded up
+  if (p != nullptr && p->kv_splits > 1 && p->num_tokens > 0 && p->num_qo_heads > 0 && p->head_dim > 0) {
+    const size_t rows = static_cast<size_t>(p->kv_splits) * p->num_tokens * p->num_qo_heads;
+    auto round = [](size_t x) { return (x + 255) / 256 * 256; };
+    bytes += round(rows * p->head_dim * sizeof(float)) + round(rows * sizeof(float));
+  }
+  return bytes;
 }
 
 int32_t ppa_validate_shapes(const ppa_params* p, char* msg, size_t msg_len) {
@@ -165,6 +170,8 @@ int32_t ppa_validate_shapes(const ppa_params* p, char* msg, size_t msg_len) {
   if (p->page_size < 1 || p->page_size > 65536 || (p->page_size & (p->page_size - 1)) != 0)
     return fail(PPA_ERR_PAGE_SIZE, msg, msg_len, "page_size %d", p->page_size);
   if (p->window_left < -1) return fail(PPA_ERR_WINDOW, msg, msg_len, "window_left %d", p->window_left);
+  if (p->kv_splits < 0 || p->kv_splits > 256)
+    return fail(PPA_ERR_SHAPE, msg, msg_len, "kv_splits %d outside [0, 256]", p->kv_splits);
   if (p->max_q_len > p->max_kv_len)
     return fail(PPA_ERR_LENGTHS, msg, msg_len, "max_q_len %d > max_kv_len %d", p->max_q_len,
                 p->max_kv_len);
@@ -228,7 +235,14 @@ int32_t ppa_validate_shapes(const ppa_params* p, char* msg, size_t msg_len) {
     return fail(PPA_ERR_ALIGNMENT, msg, msg_len, "kv cache");
   if ((reinterpret_cast<uintptr_t>(p->sinks) & 3u) != 0)
     return fail(PPA_ERR_ALIGNMENT, msg, msg_len, "sinks");
+  if ((reinterpret_cast<uintptr_t>(p->lse) & 3u) != 0)
+    return fail(PPA_ERR_ALIGNMENT, msg, msg_len, "lse");
+  if (p->lse != nullptr && (p->lse_strides[0] < 0 || p->lse_strides[1] < 0))
+    return fail(PPA_ERR_STRIDE, msg, msg_len, "lse strides must be non-negative");
 
+  if (p->kv_splits > 1 && p->workspace == nullptr)
+    return fail(PPA_ERR_WORKSPACE, msg, msg_len, "kv_splits %d needs a workspace of %zu bytes", p->kv_splits,
+                ppa_workspace_bytes(p));
   if (p->workspace != nullptr && p->workspace_bytes < ppa_workspace_bytes(p))
     return fail(PPA_ERR_WORKSPACE, msg, msg_len, "workspace of %zu bytes, need %zu",
                 p->workspace_bytes, ppa_workspace_bytes(p));
@@ -335,5 +349,7 @@ int32_t ppa_validate_page_table_csr_host(const ppa_params* p, const int32_t* seq
   }
   return PPA_OK;
 }
+
+size_t ppa_merge_params_size(void) { return sizeof(ppa_merge_params); }
 
 }  // extern "C"

@@ -40,15 +40,30 @@ def workspace(device="cuda") -> torch.Tensor:
     return _WORKSPACES[key]
 
 
+def split_workspace(dcase: dict, kv_splits: int) -> torch.Tensor:
+    """A zeroed workspace large enough for split-KV with this case."""
+    import paged_kv_prefill_varlen_amd as ppa
+    p = ppa.PpaParams()
+    p.num_tokens, p.num_qo_heads, p.head_dim = (int(x) for x in dcase["query"].shape)
+    p.kv_splits = kv_splits
+    return torch.zeros(ppa.ppa_workspace_bytes(p), dtype=torch.uint8, device=dcase["query"].device)
+
+
 def run_gpu(dcase: dict, out: torch.Tensor = None, bmm1=None, bmm2=None, stream=None,
-            validate=True, schedule="persistent") -> torch.Tensor:
+            validate=True, schedule="persistent", lse: torch.Tensor = None, kv_splits: int = 0,
+            ws: torch.Tensor = None) -> torch.Tensor:
     """schedule: "persistent" (workspace given: balanced persistent workgroups)
-    or "grid" (no workspace: one workgroup per work item)."""
+    or "grid" (no workspace: one workgroup per work item).  With kv_splits > 1
+    a workspace of the needed size is allocated unless ``ws`` is given."""
     import paged_kv_prefill_varlen_amd as ppa
     if out is None:
         out = torch.empty_like(dcase["query"]).view(torch.int16).fill_(GUARD).view(torch.bfloat16)
-    ws = workspace(dcase["query"].device) if schedule == "persistent" else None
     assert schedule in ("persistent", "grid")
+    if ws is None:
+        if kv_splits > 1:
+            ws = split_workspace(dcase, kv_splits)
+        elif schedule == "persistent":
+            ws = workspace(dcase["query"].device)
     flat = dcase.get("kv_indptr") is not None
     ppa.batch_context_with_kv_cache(
         dcase["query"], dcase["kv_cache"], ws, None if flat else dcase["block_tables"], dcase["seq_lens"],
@@ -58,7 +73,8 @@ def run_gpu(dcase: dict, out: torch.Tensor = None, bmm1=None, bmm2=None, stream=
         dcase["batch_size"], dcase["cum_seq_lens_q"], dcase["cum_seq_lens_kv"],
         window_left=dcase["window_left"], out=out, kv_layout=dcase["kv_layout"],
         sinks=dcase["sinks"], validate=validate, stream=stream, kv_indptr=dcase.get("kv_indptr"),
-        kv_indices=dcase.get("kv_indices"), kv_last_page_len=dcase.get("kv_last_page_len"))
+        kv_indices=dcase.get("kv_indices"), kv_last_page_len=dcase.get("kv_last_page_len"), lse=lse,
+        kv_splits=kv_splits)
     return out
 
 

@@ -377,3 +377,62 @@ def test_csr_rejections():
     with pytest.raises(ValueError):
         B.make_params(c["q"], c["kv"], None, None, c["sl"], c["max_q"], c["max_kv"], 0.125, 1.0, c["B"],
                       c["cuq"], c["cukv"], c["W"], c["out"], c["layout"], None)
+
+
+
+# --------------------------------------------------------------------------
+# log-sum-exp output, split-KV and merge arguments
+# --------------------------------------------------------------------------
+
+def test_split_and_lse_rejections():
+    c = _case()
+    E = ERR
+    assert _shapes(_params(c, kv_splits=-1))[0] == E["PPA_ERR_SHAPE"]
+    assert _shapes(_params(c, kv_splits=257))[0] == E["PPA_ERR_SHAPE"]
+    assert _shapes(_params(c, kv_splits=1))[0] == OK   # 0 and 1 both mean no split
+    assert _shapes(_params(c, kv_splits=4))[0] == E["PPA_ERR_WORKSPACE"]   # no workspace
+    p = _params(c, kv_splits=4)
+    need = B.ppa_workspace_bytes(p)
+    T, H, D = c["q"].shape
+    assert need == 256 + ((4 * T * H * D * 4 + 255) // 256) * 256 + ((4 * T * H * 4 + 255) // 256) * 256
+    ws = torch.zeros(need + 16, dtype=torch.uint8)
+    assert _shapes(_params(c, kv_splits=4, workspace=ws.data_ptr(), workspace_bytes=need))[0] == OK
+    assert _shapes(_params(c, kv_splits=4, workspace=ws.data_ptr(), workspace_bytes=need - 1))[0] == \
+        E["PPA_ERR_WORKSPACE"]
+    lse = torch.zeros(T * H + 1, dtype=torch.float32)
+    assert _shapes(_params(c, lse=lse.data_ptr(), lse_strides=[H, 1]))[0] == OK
+    assert _shapes(_params(c, lse=lse.data_ptr() + 2, lse_strides=[H, 1]))[0] == E["PPA_ERR_ALIGNMENT"]
+    assert _shapes(_params(c, lse=lse.data_ptr(), lse_strides=[-1, 1]))[0] == E["PPA_ERR_STRIDE"]
+
+
+def test_merge_argument_rejections():
+    """Bad merge arguments are rejected before anything is launched."""
+    E = ERR
+    o = torch.zeros(2, 3, 4, 64)
+    l = torch.zeros(2, 3, 4)
+    out = torch.zeros(3, 4, 64, dtype=torch.bfloat16)
+
+    def m(**over):
+        p = B.PpaMergeParams()
+        p.abi_version, p.struct_size = B.PPA_ABI_VERSION, ctypes.sizeof(B.PpaMergeParams)
+        p.num_parts, p.num_rows, p.num_heads, p.head_dim = 2, 3, 4, 64
+        p.o_parts, p.lse_parts, p.out = o.data_ptr(), l.data_ptr(), out.data_ptr()
+        p.out_dtype = B.PPA_DTYPE_BF16
+        p.out_strides[:] = [256, 64, 1]
+        for k, v in over.items():
+            if isinstance(getattr(p, k), ctypes.Array):
+                getattr(p, k)[:] = v
+            else:
+                setattr(p, k, v)
+        return int(B._lib.ppa_merge_attention_states(ctypes.byref(p), None))
+
+    assert m(abi_version=1) == E["PPA_ERR_ABI"]
+    assert m(num_parts=0) == E["PPA_ERR_SHAPE"]
+    assert m(num_heads=0) == E["PPA_ERR_SHAPE"]
+    assert m(head_dim=96) == E["PPA_ERR_HEAD_DIM"]
+    assert m(out_dtype=B.PPA_DTYPE_FP32) == E["PPA_ERR_DTYPE"]
+    assert m(o_parts=None) == E["PPA_ERR_NULL_POINTER"]
+    assert m(out_strides=[256, 64, 2]) == E["PPA_ERR_STRIDE"]
+    assert m(out_strides=[255, 64, 1]) == E["PPA_ERR_STRIDE"]
+    assert m(lse_parts=l.data_ptr() + 2) == E["PPA_ERR_ALIGNMENT"]
+    assert m(num_rows=0) == OK   # nothing to do, nothing launched

@@ -16,8 +16,9 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (assert_close, errors, guard_rows_untouched, run_gpu, to_device, workspace)
-from oracle.case_io import decode_tensor, oracle_inputs, run_oracle, run_oracle_rows
+from gpu_helpers import (assert_close, errors, guard_rows_untouched, run_gpu, split_workspace, to_device,
+                         workspace)
+from oracle.case_io import decode_tensor, oracle_inputs, run_oracle, run_oracle_lse, run_oracle_rows
 from workloads import make_case, make_custom_case
 from workloads.cases import relayout, to_flat_page_table
 
@@ -361,3 +362,123 @@ def test_flat_page_table_gather():
         torch.cuda.synchronize()
         want = torch.cat(logical, dim=0)
         assert torch.equal(dst.cpu().view(torch.uint8), want.contiguous().view(torch.uint8))
+
+
+# --------------------------------------------------------------------------
+# log-sum-exp output, split-KV and the merge of partial states
+# --------------------------------------------------------------------------
+
+# lse = log(sum of bf16-rounded weights) + max: the rounding of each weight
+# (relative 2^-9) bounds the sum's relative error, so |d lse| <= ~2e-3.
+TOL_LSE = 5e-3
+
+LSE_CASES = ["g2_d64_nhd_combined", "g8_window0_sinks", "g16_window63_sinks", "empty_requests",
+             "long_prefix", "window_many_tiles", "neg_bmm1", "zero_bmm1", "fp8_d64_nhd_window_sinks"]
+
+
+def _edge(name):
+    return make_custom_case(name=name, batch=len(EDGE[name]["q_lens"]), seed=zlib.crc32(name.encode()) % 10000,
+                            **EDGE[name])
+
+
+def _lse_close(lse, want, written, what):
+    got = lse.detach().cpu().numpy()[written]
+    w = want[written]
+    assert np.isfinite(got).all(), f"{what}: non-finite lse"
+    err = np.abs(got - w).max() if got.size else 0.0
+    assert err <= TOL_LSE, f"{what}: lse max |err| {err:.3e}"
+    return err
+
+
+@pytest.mark.parametrize("name", LSE_CASES)
+def test_lse_output(name):
+    case = _edge(name)
+    want, written = run_oracle(case)
+    want_lse = run_oracle_lse(case)
+    d = to_device(case)
+    lse = torch.full(tuple(d["query"].shape[:2]), float("nan"), dtype=torch.float32, device="cuda")
+    out = run_gpu(d, lse=lse)
+    plain = run_gpu(d)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), plain.view(torch.int16)), "lse output changed the output"
+    err = _lse_close(lse, want_lse, written, name)
+    assert torch.isnan(lse.cpu()[~torch.from_numpy(written)]).all(), "lse written outside the requests"
+    _say(f"  {name}: lse max err {err:.2e}")
+
+
+SPLIT_CASES = ["mha_d128_p16", "g8_window0_sinks", "g16_window63_sinks", "empty_requests", "long_prefix",
+               "window_many_tiles", "fp8_d128", "page_size_1", "single_token"]
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7])
+@pytest.mark.parametrize("name", SPLIT_CASES)
+def test_split_kv(name, splits):
+    case = _edge(name)
+    want, written = run_oracle(case)
+    want_lse = run_oracle_lse(case)
+    d = to_device(case)
+    lse = torch.full(tuple(d["query"].shape[:2]), float("nan"), dtype=torch.float32, device="cuda")
+    ws = None
+    out = run_gpu(d, lse=lse, kv_splits=splits)
+    torch.cuda.synchronize()
+    assert guard_rows_untouched(out, written)
+    mx, mean = assert_close(out, want, written, fp8=case["kv_dtype"] != "bf16", what=f"{name} S={splits}")
+    err = _lse_close(lse, want_lse, written, f"{name} S={splits}")
+    _say(f"  {name} S={splits}: max {mx:.2e} mean {mean:.2e} lse {err:.2e}")
+
+
+def test_split_kv_chunked_config():
+    case = make_case("chunked")
+    want, written = run_oracle(case)
+    d = to_device(case)
+    for splits in (2, 4):
+        out = run_gpu(d, kv_splits=splits)
+        torch.cuda.synchronize()
+        assert guard_rows_untouched(out, written)
+        mx, mean = assert_close(out, want, written, what=f"chunked S={splits}")
+        _say(f"  chunked S={splits}: max {mx:.2e} mean {mean:.2e}")
+
+
+def test_split_kv_workspace_reused_and_zeroed():
+    """Split calls of different sizes share one (large enough) workspace; the
+    scheduler counters at its start return to zero after each call."""
+    import paged_kv_prefill_varlen_amd as ppa
+    a, b = _edge("long_prefix"), _edge("g2_d64_nhd_combined")
+    da, db = to_device(a), to_device(b)
+    ws = split_workspace(da, 5)
+    wa, wra = run_oracle(a)
+    wb, wrb = run_oracle(b)
+    for _ in range(2):
+        oa = run_gpu(da, kv_splits=5, ws=ws, validate=False)
+        ob = run_gpu(db, kv_splits=3, ws=ws, validate=False)
+        torch.cuda.synchronize()
+        assert_close(oa, wa, wra, what="long_prefix S=5")
+        assert_close(ob, wb, wrb, what="g2 S=3")
+        assert not ws[:ppa.WORKSPACE_BYTES].any()
+
+
+def test_merge_entry_point():
+    import paged_kv_prefill_varlen_amd as ppa
+    from oracle.paged_attention import merge_states
+    rng = np.random.default_rng(77)
+    for S, rows, heads, D in ((1, 5, 3, 64), (4, 33, 8, 128), (9, 7, 2, 64)):
+        o = rng.standard_normal((S, rows, heads, D)).astype(np.float32)
+        lse = (rng.standard_normal((S, rows, heads)) * 3).astype(np.float32)
+        lse[0, 0, :] = -np.inf   # empty parts
+        if S > 1:
+            lse[:, 1, 0] = -np.inf   # a row with no keys in any part
+        sinks = rng.standard_normal(heads).astype(np.float32)
+        for with_sink in (False, True):
+            out = torch.empty((rows, heads, D), dtype=torch.bfloat16, device="cuda")
+            lse_out = torch.empty((rows, heads), dtype=torch.float32, device="cuda")
+            ppa.ppa_merge_attention_states(torch.from_numpy(o).cuda(), torch.from_numpy(lse).cuda(), out, lse_out,
+                                           torch.from_numpy(sinks).cuda() if with_sink else None)
+            torch.cuda.synchronize()
+            wo, wl = merge_states(o.astype(np.float64), lse.astype(np.float64),
+                                  sinks[None, :].astype(np.float64) if with_sink else None)
+            got = decode_tensor(out.cpu())
+            assert np.abs(got - wo).max() <= 1e-2 * max(1.0, np.abs(wo).max())
+            gl = lse_out.cpu().numpy()
+            fin = np.isfinite(wl)
+            assert np.array_equal(np.isfinite(gl), fin)
+            assert np.abs(gl[fin] - wl[fin]).max() < 1e-4

@@ -37,6 +37,8 @@ WORKLOAD_TEXT = {
                   "heads, head_dim 64, page 16, NHD split, seed 1004"),
     "fp8_long_prefix": ("long-prefix fp8 KV: batch 1, q 8192 over kv 32768, 64 q / 8 kv heads, head_dim 128, "
                         "page 64, HND split, e4m3fn K/V with per-tensor scales, seed 1005"),
+    "decode": ("decode-shaped: batch 16, 1 new token over an 8191-token cached prefix, 32 q / 8 kv heads, "
+               "head_dim 128, page 64, HND split, seed 1100 (HBM-bound; reported as K/V GB/s)"),
 }
 
 
@@ -147,6 +149,7 @@ def main():
     ap.add_argument("--config", default="chunked", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--kv-splits", type=int, default=0, help="split-KV chunks per work item (0: none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -177,10 +180,14 @@ def main():
     sinks = None if case["sinks"] is None else case["sinks"].to(dev)
     out = torch.empty_like(q)
     # zeroed scheduler workspace: persistent workgroups pull balanced work
-    workspace = torch.zeros(ppa.WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    # (larger with split-KV: it also holds the partial states)
+    p = ppa.make_params(q, kv, None, bt, sl, case["max_q_len"], case["max_kv_len"], case["bmm1_scale"],
+                        case["bmm2_scale"], case["batch_size"], cuq, cukv, case["window_left"], out,
+                        case["kv_layout"], sinks, kv_splits=args.kv_splits)
+    workspace = torch.zeros(ppa.ppa_workspace_bytes(p), dtype=torch.uint8, device=dev)
     p = ppa.make_params(q, kv, workspace, bt, sl, case["max_q_len"], case["max_kv_len"], case["bmm1_scale"],
                         case["bmm2_scale"], case["batch_size"], cuq, cukv, case["window_left"], out,
-                        case["kv_layout"], sinks)
+                        case["kv_layout"], sinks, kv_splits=args.kv_splits)
     st, msg = ppa.ppa_validate_metadata_host(p, case["cum_seq_lens_q"], case["cum_seq_lens_kv"],
                                              case["seq_lens"], case["block_tables"])
     if st != 0:
@@ -213,6 +220,19 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     kernel_tflops = flops / (launch_ms * 1e-3) / 1e12
     fp8 = case["kv_dtype"] != "bf16"
+    hbm = args.config == "decode"
+    alg_bytes = algorithmic_bytes(case)
+    if hbm:   # decode streams K/V once: report bandwidth against the HBM roofline
+        kernel_gbs = alg_bytes / (launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(kernel_gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(kernel_tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": stored_traffic(args.config)}
+    roof.update({"algorithmic_bytes": alg_bytes, "kernel_ms": round(launch_ms, 5),
+                 "kernel": "paged_prefill_persistent<%d,%s>%s" % (case["head_dim"], "fp8" if fp8 else "bf16",
+                                                                  " + merge" if args.kv_splits > 1 else "")})
     line = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -228,20 +248,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config,
                    "query_tokens": tokens, "causal_gflop": round(flops / 1e9, 3),
-                   "parallelism": "none (one GPU)"},
+                   "kv_splits": args.kv_splits, "parallelism": "none (one GPU)"},
         "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(kernel_tflops, 3),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": stored_traffic(args.config),
-            "algorithmic_bytes": algorithmic_bytes(case),
-            "kernel_ms": round(launch_ms, 5),
-            "kernel": "paged_prefill_persistent<%d,%s>" % (case["head_dim"], "fp8" if fp8 else "bf16"),
-        },
+        "roofline": roof,
         "cpu_baseline": None,
     }
     if not args.no_cpu:

@@ -482,3 +482,19 @@ def test_merge_entry_point():
             fin = np.isfinite(wl)
             assert np.array_equal(np.isfinite(gl), fin)
             assert np.abs(gl[fin] - wl[fin]).max() < 1e-4
+
+
+@pytest.mark.parametrize("splits", [0, 8, 32])
+def test_decode_config(splits):
+    """The decode-shaped batch (one new token per request over an 8K prefix),
+    whole output and lse against the oracle, with and without split-KV."""
+    case = make_case("decode")
+    want, written = run_oracle(case)
+    want_lse = run_oracle_lse(case)
+    d = to_device(case)
+    lse = torch.full(tuple(d["query"].shape[:2]), float("nan"), dtype=torch.float32, device="cuda")
+    out = run_gpu(d, lse=lse, kv_splits=splits)
+    torch.cuda.synchronize()
+    mx, mean = assert_close(out, want, written, what=f"decode S={splits}")
+    err = _lse_close(lse, want_lse, written, f"decode S={splits}")
+    _say(f"  decode S={splits}: max {mx:.2e} mean {mean:.2e} lse {err:.2e}")

@@ -105,6 +105,13 @@ SPECS = {
 }
 SPEC_ORDER = ["tiny", "chunked", "llama3_8b", "swa_sinks", "fp8_long_prefix"]
 
+# Decode-shaped batch for the split-KV measurement (one new token per request
+# over an 8K cached prefix; not one of the five prefill workloads).
+SPECS["decode"] = Spec(
+    name="decode", batch=16, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+    page_size=64, kv_layout="HND", kv_form="split",
+    q_lens=(1,) * 16, prefix_lens=(8191,) * 16, seed=1100)
+
 
 def spec_by_index(i: int) -> Spec:
     """0-based position in the workload list."""

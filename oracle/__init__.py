@@ -4,7 +4,8 @@ Only the tests, the smoke check and the bench's CPU-baseline leg may import
 this package.  The library's own code never does: it must fail loudly when
 its HIP extension is missing rather than fall back to anything here.
 """
-from .paged_attention import (E4M3FN_TABLE, attention_one_request, attention_rows,  # noqa: F401
+from .paged_attention import (E4M3FN_TABLE, append_paged_kv, attention_one_request, attention_rows,  # noqa: F401
+                              encode_e4m3fn,
                               decode_bf16, decode_e4m3fn, e4m3fn_value, gather_paged_kv,
                               log_sum_exp_rows, merge_states, paged_prefill_attention,
                               paged_prefill_lse, partial_state)

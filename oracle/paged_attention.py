@@ -81,6 +81,25 @@ def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
     return E4M3FN_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
+def encode_e4m3fn(y: np.ndarray) -> np.ndarray:
+    """Real values -> OCP float8 e4m3fn codes: the nearest representable
+    value, ties to the even code (the even mantissa), magnitudes beyond the
+    largest finite value 448 saturated to it, NaN to the NaN code with the
+    input's sign.  ``y`` is taken exactly (pass the fp32 value to encode)."""
+    y = np.asarray(y, dtype=np.float64)
+    grid = E4M3FN_TABLE[:127]           # codes 0x00 .. 0x7E, ascending, 0 .. 448
+    a = np.minimum(np.abs(y), grid[-1])
+    hi = np.searchsorted(grid, a, side="left")          # first grid value >= a
+    hi = np.clip(hi, 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo = a - grid[lo]
+    d_hi = grid[hi] - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(take_hi, hi, lo).astype(np.uint8)
+    code = np.where(np.isnan(y), np.uint8(0x7F), code)
+    return np.where(np.signbit(y), code | np.uint8(0x80), code).astype(np.uint8)
+
+
 # ---------------------------------------------------------------------------
 # 2. Page gather
 # ---------------------------------------------------------------------------
@@ -198,6 +217,37 @@ def request_pages(b: int, block_tables: Optional[np.ndarray], kv_indptr: Optiona
     if kv_indptr is not None:
         return np.asarray(kv_indices)[int(kv_indptr[b]):int(kv_indptr[b + 1])]
     return np.asarray(block_tables[b])
+
+
+def append_paged_kv(planes, kv_layout: str, page_size: int, k_new_codes: np.ndarray, v_new_codes: np.ndarray,
+                    slot_mapping: np.ndarray, kv_dtype: str, k_scale: float = 1.0, v_scale: float = 1.0):
+    """Write new tokens' K and V into a paged cache (the KV save step before
+    attention: TokenSpeed backend source, ``_save_kv_and_prepare_q`` with
+    ``out_cache_loc``): token i goes to page ``slot_mapping[i] // page_size``,
+    slot ``slot_mapping[i] % page_size``; a negative entry skips the token.
+    ``planes`` are the cache's K and V code arrays (one array for both when
+    they share storage), ``k_new_codes`` / ``v_new_codes`` bf16 codes
+    ``[n, H_kv, D]``.  A bf16 cache stores the codes as they are; an fp8
+    cache stores ``encode_e4m3fn(fp32(x) / fp32(scale))``.  Returns new code
+    arrays; the inputs are not modified."""
+    out = [np.array(p, copy=True) for p in planes]
+    for kv_idx, (new, scale) in enumerate(((k_new_codes, k_scale), (v_new_codes, v_scale))):
+        dst = out[min(kv_idx, len(out) - 1)]
+        if kv_dtype == "bf16":
+            vals = np.asarray(new, dtype=np.uint16)
+        else:
+            x = decode_bf16(new).astype(np.float32)
+            vals = encode_e4m3fn(x / np.float32(scale))
+        for i, loc in enumerate(np.asarray(slot_mapping)):
+            loc = int(loc)
+            if loc < 0:
+                continue
+            pid, slot = loc // page_size, loc % page_size
+            if kv_layout == "HND":
+                dst[pid, :, slot, :] = vals[i]
+            else:
+                dst[pid, slot, :, :] = vals[i]
+    return out
 
 
 # ---------------------------------------------------------------------------

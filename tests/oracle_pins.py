@@ -525,6 +525,68 @@ def pin_merge_identities():
     assert np.allclose(po, base_o, rtol=1e-13, atol=1e-13) and np.allclose(pl, base_l, rtol=1e-13, atol=1e-13)
 
 
+def pin_e4m3fn_encode():
+    """The encoder inverts the decoder on every finite code, agrees with
+    torch's float8_e4m3fn cast wherever that cast is finite (random values,
+    exact midpoints between neighbours, subnormals), and saturates beyond
+    448 where the cast would give NaN."""
+    finite = [c for c in range(256) if not np.isnan(OA.E4M3FN_TABLE[c])]
+    codes = np.array(finite, dtype=np.uint8)
+    assert np.array_equal(OA.encode_e4m3fn(OA.E4M3FN_TABLE[codes]), codes)
+    rng = np.random.default_rng(901)
+    y = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(40.0),
+        (rng.random(5000).astype(np.float32) * np.float32(2.0 ** -6)),
+        # exact midpoints between consecutive positive grid values (ties)
+        ((OA.E4M3FN_TABLE[1:126] + OA.E4M3FN_TABLE[2:127]) / 2).astype(np.float32),
+        np.array([0.0, -0.0, 2.0 ** -10, 3 * 2.0 ** -10, 463.99], dtype=np.float32),
+    ])
+    y = y[np.abs(y) < 464]
+    want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(OA.encode_e4m3fn(y), want)
+    sat = OA.encode_e4m3fn(np.array([448.0, 470.0, 1e9, -1e9, np.inf], dtype=np.float32))
+    assert sat.tolist() == [0x7E, 0x7E, 0x7E, 0xFE, 0x7E]
+    assert OA.encode_e4m3fn(np.array([np.nan]))[0] & 0x7F == 0x7F
+
+
+def pin_append_then_gather():
+    """Appended tokens are what a page gather reads back at their sequence
+    positions (bf16: the new values; fp8: the encoded x / scale), tokens with
+    a negative slot are skipped, and every other slot keeps its contents."""
+    case = _tiny(902, q_lens=(5, 3), prefix_lens=(7, 2), batch=2, page_size=4, kv_layout="NHD")
+    rng = np.random.default_rng(903)
+    P = case["page_size"]
+    for kv_dtype, scale in (("bf16", 1.0), ("fp8_e4m3fn", 0.37)):
+        planes = [rng.integers(0, 1 << (16 if kv_dtype == "bf16" else 8),
+                               size=tuple(case["kv_cache"][0].shape)).astype(
+            np.uint16 if kv_dtype == "bf16" else np.uint8) for _ in range(2)]
+        n = sum(case["q_lens"])
+        k_new = torch.randn(n, 2, 8).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        v_new = torch.randn(n, 2, 8).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        bt = case["block_tables"].numpy()
+        slots, t = [], 0
+        for b, (q, kv) in enumerate(zip(case["q_lens"], case["kv_lens"])):
+            for i in range(q):
+                pos = kv - q + i
+                slots.append(int(bt[b, pos // P]) * P + pos % P)
+        slots = np.array(slots)
+        slots[2] = -1                      # skipped
+        out = OA.append_paged_kv(planes, "NHD", P, k_new, v_new, slots, kv_dtype, scale, scale)
+        for kv_idx, new in ((0, k_new), (1, v_new)):
+            changed = np.zeros(planes[kv_idx].shape, dtype=bool)
+            for i, loc in enumerate(slots):
+                if loc < 0:
+                    continue
+                got = out[kv_idx][loc // P, loc % P]
+                if kv_dtype == "bf16":
+                    assert np.array_equal(got, new[i])
+                else:
+                    x = OA.decode_bf16(new[i]).astype(np.float32) / np.float32(scale)
+                    assert np.array_equal(got, OA.encode_e4m3fn(x))
+                changed[loc // P, loc % P] = True
+            assert np.array_equal(out[kv_idx][~changed], planes[kv_idx][~changed])
+
+
 ALL_PINS = [
     pin_bf16_decode_all_codes,
     pin_e4m3fn_decode_all_codes,
@@ -549,4 +611,6 @@ ALL_PINS = [
     pin_lse_brute_force,
     pin_merge_of_key_splits_is_full,
     pin_merge_identities,
+    pin_e4m3fn_encode,
+    pin_append_then_gather,
 ]

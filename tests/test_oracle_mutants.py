@@ -134,6 +134,19 @@ MUTANTS["lse_sink_ignored"] = ("log_sum_exp_rows", lambda s, valid, sink: _orig_
 MUTANTS["merge_sink_ignored"] = ("merge_states", lambda o, lse, sink=None: _orig_merge(o, lse, None))
 MUTANTS["merge_plain_mean"] = ("merge_states",
                                lambda o, lse, sink=None: (np.mean(o, axis=0), _orig_merge(o, lse, sink)[1]))
+_orig_encode = OA.encode_e4m3fn
+
+
+def _encode_truncating(y):
+    # rounds toward zero instead of to nearest
+    y = np.asarray(y, dtype=np.float64)
+    grid = OA.E4M3FN_TABLE[:127]
+    code = np.clip(np.searchsorted(grid, np.minimum(np.abs(y), 448.0), side="right") - 1, 0, 126).astype(np.uint8)
+    return np.where(np.signbit(y), code | np.uint8(0x80), code)
+
+
+MUTANTS["encode_truncates"] = ("encode_e4m3fn", _encode_truncating)
+MUTANTS["encode_ties_away"] = ("encode_e4m3fn", lambda y: _orig_encode(np.asarray(y, dtype=np.float64) * (1 + 1e-12)))
 MUTANTS["partial_ignores_key_range"] = ("partial_state",
                                         lambda q, k, v, b1, b2, w, k0, k1: _orig_partial(q, k, v, b1, b2, w, 0,
                                                                                          k.shape[0]))

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PPA_ABI_VERSION 3
+#define PPA_ABI_VERSION 4
 
 typedef enum ppa_status {
   PPA_OK = 0,
@@ -222,6 +222,35 @@ typedef struct ppa_params {
 } ppa_params;
 
 /*
+ * New tokens to write into a paged cache before attention (the KV save step
+ * of the TokenSpeed backend source: K and V written at out_cache_loc, with
+ * per-tensor scales for an fp8 cache).  The cache itself is described by a
+ * ppa_params (its cache, page and head fields; the rest is not read).
+ */
+typedef struct ppa_append_params {
+  uint32_t abi_version;
+  uint32_t struct_size;
+  const void* k_new;            /* [num_new, num_kv_heads, head_dim], dtype new_dtype (bf16) */
+  const void* v_new;
+  int32_t new_dtype;
+  int32_t num_new;              /* >= 0 */
+  int64_t k_new_strides[3];     /* elements; innermost 1, the others 16-byte multiples */
+  int64_t v_new_strides[3];
+  /* [num_new] int64 DEVICE array: page_id * page_size + slot of each token
+     (out_cache_loc); a negative entry skips the token, and an entry whose
+     page is >= num_pages is skipped by the device as well. */
+  const int64_t* slot_mapping;
+  /* fp8 e4m3fn cache: the stored code is e4m3fn(fp32(x) / fp32(scale)),
+     nearest value with ties to even, magnitudes beyond 448 saturated to 448,
+     NaN kept.  A bf16 cache stores x as it is.  *_ptr, when not NULL, point
+     to device fp32 scalars that replace the values. */
+  float k_scale;
+  float v_scale;
+  const float* k_scale_ptr;
+  const float* v_scale_ptr;
+} ppa_append_params;
+
+/*
  * Partial attention states to combine (log-sum-exp merge): part s holds, per
  * (row, head), an output o_s normalized over its own key set and that set's
  * log-denominator lse_s (natural log; -inf for an empty set).  The merge
@@ -317,6 +346,25 @@ int32_t ppa_merge_attention_states(const ppa_merge_params* m, void* stream);
 
 /* sizeof(ppa_merge_params) of this build, for bindings. */
 size_t ppa_merge_params_size(void);
+
+/*
+ * Host-only check of an append: the cache description in `cache` (dtypes,
+ * layout, form (the one-plane combined form is rejected: K and V would share
+ * the slots), heads, head_dim, page size, pages, cache pointers, strides,
+ * alignment) and the new tokens in `a` (pointers, bf16 dtype, strides,
+ * alignment).
+ */
+int32_t ppa_validate_append(const ppa_params* cache, const ppa_append_params* a, char* msg, size_t msg_len);
+
+/*
+ * Write the new tokens of `a` into the cache described by `cache`:
+ * ppa_validate_append, then one kernel on `stream`.  No host
+ * synchronisation, no allocation.  Tokens sharing a slot race.
+ */
+int32_t ppa_append_paged_kv(const ppa_params* cache, const ppa_append_params* a, void* stream);
+
+/* sizeof(ppa_append_params) of this build, for bindings. */
+size_t ppa_append_params_size(void);
 
 /*
  * Address-unit check: copies the first seq_lens[b] K (kv_idx 0) or V

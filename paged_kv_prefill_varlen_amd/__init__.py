@@ -8,7 +8,9 @@ only marshals torch tensors into ``ppa_params``.  Every step of the
 attention runs in the HIP kernels; there is no fallback: importing this
 package without the built library raises ImportError.
 """
-from .binding import (PPA_ABI_VERSION, WORKSPACE_BYTES, PpaError, PpaMergeParams, ppa_merge_attention_states,
+from .binding import (PPA_ABI_VERSION, WORKSPACE_BYTES, PpaAppendParams, PpaError, PpaMergeParams,
+                      append_paged_kv_cache, make_append_params, ppa_append_paged_kv, ppa_append_params_size,
+                      ppa_merge_attention_states, ppa_validate_append,
                       ppa_merge_params_size, PpaParams, batch_context_with_kv_cache,  # noqa: F401
                       library_path, make_params, ppa_abi_version, ppa_gather_paged_kv,
                       ppa_paged_prefill_attention, ppa_params_size, ppa_strerror,

@@ -14,7 +14,7 @@ from typing import Optional, Sequence, Tuple, Union
 import numpy as np
 import torch
 
-PPA_ABI_VERSION = 3
+PPA_ABI_VERSION = 4
 
 # enums of ppa.h
 PPA_DTYPE_BF16 = 1
@@ -85,6 +85,24 @@ class PpaParams(ctypes.Structure):
     ]
 
 
+class PpaAppendParams(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", c_uint32),
+        ("struct_size", c_uint32),
+        ("k_new", c_void_p),
+        ("v_new", c_void_p),
+        ("new_dtype", c_int32),
+        ("num_new", c_int32),
+        ("k_new_strides", c_int64 * 3),
+        ("v_new_strides", c_int64 * 3),
+        ("slot_mapping", c_void_p),
+        ("k_scale", c_float),
+        ("v_scale", c_float),
+        ("k_scale_ptr", c_void_p),
+        ("v_scale_ptr", c_void_p),
+    ]
+
+
 class PpaMergeParams(ctypes.Structure):
     _fields_ = [
         ("abi_version", c_uint32),
@@ -129,6 +147,9 @@ def _load():
         "ppa_gather_paged_kv": (c_int32, [P, c_int32, c_void_p, c_int64, c_void_p]),
         "ppa_merge_attention_states": (c_int32, [ctypes.POINTER(PpaMergeParams), c_void_p]),
         "ppa_merge_params_size": (c_size_t, []),
+        "ppa_append_params_size": (c_size_t, []),
+        "ppa_validate_append": (c_int32, [P, ctypes.POINTER(PpaAppendParams), c_char_p, c_size_t]),
+        "ppa_append_paged_kv": (c_int32, [P, ctypes.POINTER(PpaAppendParams), c_void_p]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -136,6 +157,9 @@ def _load():
         fn.argtypes = args
     if lib.ppa_abi_version() != PPA_ABI_VERSION:
         raise ImportError(f"{_LIB_PATH}: ABI version {lib.ppa_abi_version()}, binding expects {PPA_ABI_VERSION}")
+    if lib.ppa_append_params_size() != ctypes.sizeof(PpaAppendParams):
+        raise ImportError(f"{_LIB_PATH}: sizeof(ppa_append_params) {lib.ppa_append_params_size()} != binding's "
+                          f"{ctypes.sizeof(PpaAppendParams)}")
     if lib.ppa_merge_params_size() != ctypes.sizeof(PpaMergeParams):
         raise ImportError(f"{_LIB_PATH}: sizeof(ppa_merge_params) {lib.ppa_merge_params_size()} != binding's "
                           f"{ctypes.sizeof(PpaMergeParams)}")
@@ -293,6 +317,55 @@ def ppa_merge_attention_states(o_parts: torch.Tensor, lse_parts: torch.Tensor, o
         raise PpaError(st, "merge arguments rejected")
 
 
+def ppa_append_params_size() -> int:
+    return int(_lib.ppa_append_params_size())
+
+
+def make_append_params(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                       k_scale=1.0, v_scale=1.0) -> PpaAppendParams:
+    """New tokens' K / V (bf16 ``[n, H_kv, D]``) and their int64 slots
+    (``page * page_size + slot``; negative skips); scales are floats or
+    one-element fp32 device tensors."""
+    if k_new.dim() != 3 or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [num_new, num_kv_heads, head_dim] of one shape")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1 or not slot_mapping.is_contiguous():
+        raise TypeError("slot_mapping must be a contiguous 1-D int64 tensor")
+    if slot_mapping.numel() != k_new.shape[0]:
+        raise ValueError("slot_mapping needs one entry per new token")
+    a = PpaAppendParams()
+    a.abi_version = PPA_ABI_VERSION
+    a.struct_size = ctypes.sizeof(PpaAppendParams)
+    a.k_new, a.v_new = _ptr(k_new), _ptr(v_new)
+    a.new_dtype = _dt(k_new) if k_new.dtype == v_new.dtype else 0
+    a.num_new = int(k_new.shape[0])
+    a.k_new_strides[:] = list(k_new.stride())
+    a.v_new_strides[:] = list(v_new.stride())
+    a.slot_mapping = _ptr(slot_mapping)
+    for name, val in (("k", k_scale), ("v", v_scale)):
+        if isinstance(val, torch.Tensor):
+            if val.dtype != torch.float32 or val.numel() != 1:
+                raise TypeError(f"{name}_scale tensor must be one float32 element")
+            setattr(a, f"{name}_scale_ptr", _ptr(val))
+            setattr(a, f"{name}_scale", 0.0)
+        else:
+            setattr(a, f"{name}_scale", float(val))
+    return a
+
+
+def ppa_validate_append(cache: PpaParams, a: PpaAppendParams) -> Tuple[int, str]:
+    buf = ctypes.create_string_buffer(512)
+    st = _lib.ppa_validate_append(ctypes.byref(cache), ctypes.byref(a), buf, len(buf))
+    return int(st), buf.value.decode()
+
+
+def ppa_append_paged_kv(cache: PpaParams, a: PpaAppendParams, stream=None, device=None) -> None:
+    h = _stream_handle(device or torch.device("cuda"), stream)
+    st = _lib.ppa_append_paged_kv(ctypes.byref(cache), ctypes.byref(a), c_void_p(h))
+    if st != 0:
+        _, msg = ppa_validate_append(cache, a)
+        raise PpaError(st, msg)
+
+
 # --------------------------------------------------------------------------
 # marshalling torch tensors -> ppa_params
 # --------------------------------------------------------------------------
@@ -434,6 +507,19 @@ def make_params(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.
         p.lse_strides[:] = list(lse.stride())
     p.kv_splits = int(kv_splits)
     return p
+
+
+def append_paged_kv_cache(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor, kv_cache,
+                          kv_layout: str = "HND", k_scale=1.0, v_scale=1.0, stream=None) -> None:
+    """Write new tokens' K and V into the paged cache at ``slot_mapping``
+    (page * page_size + slot per token, negative skips).  fp8 caches store
+    e4m3fn(x / scale), nearest-even, saturated at 448."""
+    q_stub = torch.empty((1, 1, k_new.shape[2]), dtype=torch.bfloat16, device=k_new.device)
+    i32 = torch.zeros(2, dtype=torch.int32, device=k_new.device)
+    bt = torch.zeros((1, 1), dtype=torch.int32, device=k_new.device)
+    cache = make_params(q_stub, kv_cache, None, bt, i32[:1], 0, 0, 1.0, 1.0, 0, i32, None, -1, q_stub, kv_layout)
+    a = make_append_params(k_new, v_new, slot_mapping, k_scale, v_scale)
+    ppa_append_paged_kv(cache, a, stream, k_new.device)
 
 
 def batch_context_with_kv_cache(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.Tensor],

@@ -869,6 +869,106 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
   return e == hipSuccess ? PPA_OK : PPA_ERR_HIP;
 }
 
+// ---- KV append: new tokens' K and V into their page slots -------------------
+namespace ppa {
+namespace {
+
+struct AppendArgs {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int64_t kn_tok, kn_head, vn_tok, vn_head;
+  const int64_t* slots;
+  PagedPlane k, v;
+  int32_t num_new, heads, chunks, page_shift, num_pages;
+  float k_scale, v_scale;
+  const float* k_scale_ptr;
+  const float* v_scale_ptr;
+};
+
+// x / scale -> e4m3fn code: saturated to +-448 first (NaN kept), then the
+// hardware conversion (round to nearest even).
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+  auto sat = [](float x) { return fabsf(x) > 448.f ? copysignf(448.f, x) : x; };
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), r, true);
+  return static_cast<uint32_t>(r);
+}
+
+// One thread per 8 consecutive elements of one (token, kv head, K or V) row.
+template <bool FP8>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(a.num_new) * a.heads * 2 * a.chunks;
+  if (u >= total) return;
+  const int c = static_cast<int>(u % a.chunks);
+  int64_t r = u / a.chunks;
+  const int plane = static_cast<int>(r & 1);
+  r >>= 1;
+  const int h = static_cast<int>(r % a.heads);
+  const int64_t i = r / a.heads;
+  const int64_t loc = a.slots[i];
+  if (loc < 0) return;
+  const int64_t page = loc >> a.page_shift;
+  if (page >= a.num_pages) return;
+  const int64_t slot = loc & ((int64_t{1} << a.page_shift) - 1);
+  const uint16_t* src = plane ? a.v_new + i * a.vn_tok + h * a.vn_head : a.k_new + i * a.kn_tok + h * a.kn_head;
+  const u32x4 x = *reinterpret_cast<const u32x4*>(src + c * 8);
+  const PagedPlane& pl = plane ? a.v : a.k;
+  const int64_t off = page * pl.page_stride + h * pl.head_stride + slot * pl.tok_stride + c * 8;
+  uint8_t* base = const_cast<uint8_t*>(pl.base);
+  if constexpr (!FP8) {
+    *reinterpret_cast<u32x4*>(base + off * 2) = x;
+  } else {
+    const float s = plane ? (a.v_scale_ptr ? *a.v_scale_ptr : a.v_scale) : (a.k_scale_ptr ? *a.k_scale_ptr : a.k_scale);
+    float f[8];
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = __builtin_bit_cast(float, x[e] << 16) / s;
+      f[2 * e + 1] = __builtin_bit_cast(float, x[e] & 0xffff0000u) / s;
+    }
+    *reinterpret_cast<u32x2*>(base + off) = u32x2{fp8x4(f[0], f[1], f[2], f[3]), fp8x4(f[4], f[5], f[6], f[7])};
+  }
+}
+
+}  // namespace
+}  // namespace ppa
+
+extern "C" int32_t ppa_append_paged_kv(const ppa_params* p, const ppa_append_params* ap, void* stream) {
+  char msg[8];
+  const int32_t st = ppa_validate_append(p, ap, msg, sizeof msg);
+  if (st != PPA_OK) return st;
+  if (ap->num_new == 0) return PPA_OK;
+  CacheView cv;
+  resolve_cache(p, &cv);
+  AppendArgs a{};
+  a.k_new = static_cast<const uint16_t*>(ap->k_new);
+  a.v_new = static_cast<const uint16_t*>(ap->v_new);
+  a.kn_tok = ap->k_new_strides[0];
+  a.kn_head = ap->k_new_strides[1];
+  a.vn_tok = ap->v_new_strides[0];
+  a.vn_head = ap->v_new_strides[1];
+  a.slots = ap->slot_mapping;
+  a.k = PagedPlane{static_cast<const uint8_t*>(cv.k_base), cv.k_page, cv.k_head, cv.k_tok};
+  a.v = PagedPlane{static_cast<const uint8_t*>(cv.v_base), cv.v_page, cv.v_head, cv.v_tok};
+  a.num_new = ap->num_new;
+  a.heads = p->num_kv_heads;
+  a.chunks = p->head_dim / 8;
+  a.page_shift = log2_exact(p->page_size);
+  a.num_pages = p->num_pages;
+  a.k_scale = ap->k_scale;
+  a.v_scale = ap->v_scale;
+  a.k_scale_ptr = ap->k_scale_ptr;
+  a.v_scale_ptr = ap->v_scale_ptr;
+  const int64_t total = static_cast<int64_t>(a.num_new) * a.heads * 2 * a.chunks;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > 0x7fffffff) return PPA_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->kv_dtype == PPA_DTYPE_FP8_E4M3FN)
+    hipLaunchKernelGGL(append_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? PPA_OK : PPA_ERR_HIP;
+}
+
 extern "C" int32_t ppa_merge_attention_states(const ppa_merge_params* mp, void* stream) {
   if (mp == nullptr) return PPA_ERR_NULL_POINTER;
   if (mp->abi_version != PPA_ABI_VERSION || mp->struct_size != sizeof(ppa_merge_params)) return PPA_ERR_ABI;

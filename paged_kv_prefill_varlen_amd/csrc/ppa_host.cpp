@@ -352,4 +352,59 @@ int32_t ppa_validate_page_table_csr_host(const ppa_params* p, const int32_t* seq
 
 size_t ppa_merge_params_size(void) { return sizeof(ppa_merge_params); }
 
+size_t ppa_append_params_size(void) { return sizeof(ppa_append_params); }
+
+int32_t ppa_validate_append(const ppa_params* p, const ppa_append_params* a, char* msg, size_t msg_len) {
+  if (msg != nullptr && msg_len > 0) msg[0] = '\0';
+  if (p == nullptr || a == nullptr) return fail(PPA_ERR_NULL_POINTER, msg, msg_len, "params is NULL");
+  if (p->abi_version != PPA_ABI_VERSION || p->struct_size != sizeof(ppa_params) ||
+      a->abi_version != PPA_ABI_VERSION || a->struct_size != sizeof(ppa_append_params))
+    return fail(PPA_ERR_ABI, msg, msg_len, "abi_version / struct_size mismatch");
+  if (p->kv_dtype != PPA_DTYPE_BF16 && p->kv_dtype != PPA_DTYPE_FP8_E4M3FN)
+    return fail(PPA_ERR_DTYPE, msg, msg_len, "kv dtype %d: bf16 or fp8 e4m3fn", p->kv_dtype);
+  if (a->new_dtype != PPA_DTYPE_BF16)
+    return fail(PPA_ERR_DTYPE, msg, msg_len, "new K/V dtype %d: only bf16", a->new_dtype);
+  if (p->kv_layout != PPA_KV_LAYOUT_HND && p->kv_layout != PPA_KV_LAYOUT_NHD)
+    return fail(PPA_ERR_LAYOUT, msg, msg_len, "kv_layout %d", p->kv_layout);
+  if (p->kv_form != PPA_KV_SPLIT && p->kv_form != PPA_KV_COMBINED)
+    return fail(PPA_ERR_LAYOUT, msg, msg_len, "kv_form %d", p->kv_form);
+  if (p->kv_form == PPA_KV_COMBINED && p->kv_planes != 2)
+    return fail(PPA_ERR_LAYOUT, msg, msg_len, "append needs separate K and V planes (kv_cache dim 1 is %d)",
+                p->kv_planes);
+  if (p->num_kv_heads <= 0) return fail(PPA_ERR_HEADS, msg, msg_len, "num_kv_heads %d", p->num_kv_heads);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(PPA_ERR_HEAD_DIM, msg, msg_len, "head_dim %d", p->head_dim);
+  if (p->page_size < 1 || p->page_size > 65536 || (p->page_size & (p->page_size - 1)) != 0)
+    return fail(PPA_ERR_PAGE_SIZE, msg, msg_len, "page_size %d", p->page_size);
+  if (a->num_new < 0 || p->num_pages < 0) return fail(PPA_ERR_SHAPE, msg, msg_len, "negative size");
+  if (a->num_new == 0) return PPA_OK;
+  if (p->num_pages < 1) return fail(PPA_ERR_SHAPE, msg, msg_len, "num_pages is 0");
+  if (a->k_new == nullptr || a->v_new == nullptr || a->slot_mapping == nullptr)
+    return fail(PPA_ERR_NULL_POINTER, msg, msg_len, "k_new / v_new / slot_mapping");
+  if (p->kv_form == PPA_KV_SPLIT ? (p->k_cache == nullptr || p->v_cache == nullptr) : p->kv_cache == nullptr)
+    return fail(PPA_ERR_NULL_POINTER, msg, msg_len, "kv cache");
+  const int kb = ppa::dtype_bytes(p->kv_dtype);
+  for (int w = 0; w < 2; ++w) {
+    PlaneStrides st = plane_strides(p, w);
+    if (st.dim != 1)
+      return fail(PPA_ERR_STRIDE, msg, msg_len, "%s cache head_dim stride must be 1", w ? "V" : "K");
+    if (!row_stride_ok(st.page, p->num_pages, kb) || !row_stride_ok(st.head, p->num_kv_heads, kb) ||
+        !row_stride_ok(st.tok, p->page_size, kb))
+      return fail(PPA_ERR_STRIDE, msg, msg_len,
+                  "%s cache page/head/token strides must be non-negative 16-byte multiples", w ? "V" : "K");
+    const int64_t* ns = w ? a->v_new_strides : a->k_new_strides;
+    if (ns[2] != 1 || !row_stride_ok(ns[0], a->num_new, 2) || !row_stride_ok(ns[1], p->num_kv_heads, 2))
+      return fail(PPA_ERR_STRIDE, msg, msg_len, "%s_new strides: head_dim stride 1, others 16-byte multiples",
+                  w ? "v" : "k");
+  }
+  if (p->kv_form == PPA_KV_COMBINED && !row_stride_ok(p->kv_cache_strides[1], 2, kb))
+    return fail(PPA_ERR_STRIDE, msg, msg_len, "kv_cache plane stride must be a 16-byte multiple");
+  if (!aligned16(a->k_new) || !aligned16(a->v_new) ||
+      (p->kv_form == PPA_KV_SPLIT ? (!aligned16(p->k_cache) || !aligned16(p->v_cache)) : !aligned16(p->kv_cache)))
+    return fail(PPA_ERR_ALIGNMENT, msg, msg_len, "k_new / v_new / kv cache");
+  if ((reinterpret_cast<uintptr_t>(a->slot_mapping) & 7u) != 0)
+    return fail(PPA_ERR_ALIGNMENT, msg, msg_len, "slot_mapping");
+  return PPA_OK;
+}
+
 }  // extern "C"

@@ -436,3 +436,48 @@ def test_merge_argument_rejections():
     assert m(out_strides=[255, 64, 1]) == E["PPA_ERR_STRIDE"]
     assert m(lse_parts=l.data_ptr() + 2) == E["PPA_ERR_ALIGNMENT"]
     assert m(num_rows=0) == OK   # nothing to do, nothing launched
+
+
+# --------------------------------------------------------------------------
+# KV append arguments
+# --------------------------------------------------------------------------
+
+def test_append_validation():
+    E = ERR
+    c = _case(combined=False)
+    cache = _params(c)
+    k_new = torch.zeros(6, 2, 64, dtype=torch.bfloat16)
+    v_new = torch.zeros(6, 2, 64, dtype=torch.bfloat16)
+    slots = torch.arange(6, dtype=torch.int64)
+    a = B.make_append_params(k_new, v_new, slots)
+    assert B.ppa_validate_append(cache, a) == (OK, "")
+
+    def chk(cache_over=None, **over):
+        p = _params(c, **(cache_over or {}))
+        x = B.make_append_params(k_new, v_new, slots)
+        for k, v in over.items():
+            if isinstance(getattr(x, k), ctypes.Array):
+                getattr(x, k)[:] = v
+            else:
+                setattr(x, k, v)
+        return B.ppa_validate_append(p, x)[0]
+
+    assert chk(abi_version=1) == E["PPA_ERR_ABI"]
+    assert chk(new_dtype=B.PPA_DTYPE_FP32) == E["PPA_ERR_DTYPE"]
+    assert chk(slot_mapping=None) == E["PPA_ERR_NULL_POINTER"]
+    assert chk(k_new_strides=[128, 64, 2]) == E["PPA_ERR_STRIDE"]
+    assert chk(v_new_strides=[129, 64, 1]) == E["PPA_ERR_STRIDE"]
+    assert chk(slot_mapping=slots.data_ptr() + 4) == E["PPA_ERR_ALIGNMENT"]
+    assert chk(k_new=k_new.data_ptr() + 2) == E["PPA_ERR_ALIGNMENT"]
+    assert chk(num_new=-1) == E["PPA_ERR_SHAPE"]
+    assert chk(num_new=0, slot_mapping=None) == OK          # nothing to write
+    assert chk(cache_over=dict(kv_dtype=B.PPA_DTYPE_FP32)) == E["PPA_ERR_DTYPE"]
+    assert chk(cache_over=dict(head_dim=96)) == E["PPA_ERR_HEAD_DIM"]
+    assert chk(cache_over=dict(page_size=3)) == E["PPA_ERR_PAGE_SIZE"]
+    assert chk(cache_over=dict(k_cache=None)) == E["PPA_ERR_NULL_POINTER"]
+    # a one-plane combined cache cannot take K and V in separate slots
+    c1 = _case(combined=True)
+    p1 = _params(c1, kv_planes=1)
+    assert B.ppa_validate_append(p1, a)[0] == E["PPA_ERR_LAYOUT"]
+    with pytest.raises(TypeError):
+        B.make_append_params(k_new, v_new, slots.to(torch.int32))

@@ -39,6 +39,10 @@ WORKLOAD_TEXT = {
                         "page 64, HND split, e4m3fn K/V with per-tensor scales, seed 1005"),
     "decode": ("decode-shaped: batch 16, 1 new token over an 8191-token cached prefix, 32 q / 8 kv heads, "
                "head_dim 128, page 64, HND split, seed 1100 (HBM-bound; reported as K/V GB/s)"),
+    "append_fp8": ("KV append: the 32768 new tokens of the Llama-3-8B-shaped batch (16 x 2048, 8 kv heads, "
+                   "head_dim 128) quantised into an e4m3fn paged cache (page 64, HND split) at their slots"),
+    "append_bf16": ("KV append: the 32768 new tokens of the Llama-3-8B-shaped batch (16 x 2048, 8 kv heads, "
+                    "head_dim 128) copied into a bf16 paged cache (page 64, HND split) at their slots"),
 }
 
 
@@ -141,6 +145,69 @@ def copy_calibration(nbytes: int = 1 << 28, reps: int = 3) -> None:
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def bench_append(args) -> None:
+    """Time ppa_append_paged_kv (HBM-bound): new K/V read, cache written."""
+    import torch
+
+    import paged_kv_prefill_varlen_amd as ppa
+    from workloads import make_case
+
+    fp8 = args.config == "append_fp8"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = make_case("llama3_8b", kv_dtype="fp8_e4m3fn" if fp8 else "bf16")
+    P = case["page_size"]
+    bt = case["block_tables"].numpy()
+    slots = []
+    for b, (q, kv) in enumerate(zip(case["q_lens"], case["kv_lens"])):
+        pos = np.arange(kv - q, kv)
+        slots.append(bt[b, pos // P].astype(np.int64) * P + pos % P)
+    slots = torch.from_numpy(np.concatenate(slots)).to(dev)
+    n = slots.numel()
+    H, D = case["num_kv_heads"], case["head_dim"]
+    g = torch.Generator(device=dev).manual_seed(5)
+    k_new = torch.randn((n, H, D), generator=g, device=dev).to(torch.bfloat16)
+    v_new = torch.randn((n, H, D), generator=g, device=dev).to(torch.bfloat16)
+    kv = tuple(t.to(dev) for t in case["kv_cache"])
+    q_stub = torch.empty((1, 1, D), dtype=torch.bfloat16, device=dev)
+    i32 = torch.zeros(2, dtype=torch.int32, device=dev)
+    cache = ppa.make_params(q_stub, kv, None, torch.zeros((1, 1), dtype=torch.int32, device=dev), i32[:1], 0, 0,
+                            1.0, 1.0, 0, i32, None, -1, q_stub, "HND")
+    a = ppa.make_append_params(k_new, v_new, slots, 0.02, 0.03)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        ppa.ppa_append_paged_kv(cache, a, stream.cuda_stream)
+    torch.cuda.synchronize(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        ppa.ppa_append_paged_kv(cache, a, stream.cuda_stream)
+        ends[i].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize(dev)
+    launch_ms = float(np.mean([x.elapsed_time(y) for x, y in zip(starts, ends)]))
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    eb = 1 if fp8 else 2
+    alg = n * H * D * 2 * 2 + n * H * D * eb * 2 + n * 8   # read new K/V, write cache, slots
+    gbs = alg / (ms_per_step * 1e-3) / 1e9
+    kgbs = alg / (launch_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "KV append GB/s (new K/V read + cache written)", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8" if fp8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config, "tokens": n,
+                   "parallelism": "none (one GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": None, "algorithmic_bytes": alg,
+                     "kernel_ms": round(launch_ms, 5), "kernel": "append_kernel<%s>" % ("fp8" if fp8 else "bf16")},
+        "cpu_baseline": None,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +228,10 @@ def main():
               f"(the kernel shards by kv head or request with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.config.startswith("append"):
+        bench_append(args)
+        return
 
     import torch
 

@@ -19,6 +19,7 @@ import os
 import numpy as np
 import torch
 
+import oracle.mxfp4 as MX
 import oracle.paged_attention as OA
 from oracle.case_io import decode_tensor, oracle_inputs
 from workloads import make_custom_case
@@ -587,7 +588,126 @@ def pin_append_then_gather():
             assert np.array_equal(out[kv_idx][~changed], planes[kv_idx][~changed])
 
 
+# --------------------------------------------------------------------------
+# MXFP4 output encoding
+# --------------------------------------------------------------------------
+
+
+def _mx_golden():
+    with open(os.path.join(GOLDEN, "mxfp4_examples.json")) as f:
+        return json.load(f)
+
+
+def pin_mx_formats_golden():
+    """E2M1 codes and E8M0 bytes decode to the format definition's values;
+    E8M0 also agrees with torch's float8_e8m0fnu on all 256 bytes."""
+    g = _mx_golden()
+    for code, val in g["e2m1"].items():
+        assert _same(MX.E2M1_TABLE[int(code, 16)], float(val)), f"e2m1 {code}"
+    for b, val in g["e8m0"].items():
+        assert _same(MX.e8m0_value(int(b, 16)), float(val)), f"e8m0 {b}"
+    bytes_ = np.arange(256, dtype=np.uint8)
+    theirs = torch.from_numpy(bytes_.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert _same(MX.e8m0_value(bytes_), theirs), "e8m0 decode differs from torch's"
+
+
+def pin_mx_hand_examples():
+    """Hand-worked blocks (scale byte and packed codes) reproduce."""
+    for ex in _mx_golden()["blocks"]:
+        y = np.array([float(v) for v in ex["y"]], dtype=np.float64)
+        packed, sb = MX.mxfp4_output(y[None, :], ex["vec"], float(ex["g"]))
+        want = [int(v, 16) for v in ex["packed"]]
+        assert sb.tolist() == [[int(ex["scale"], 16)]], (ex["working"], sb)
+        assert packed[0].tolist() == want, (ex["working"], [hex(v) for v in packed[0]])
+
+
+def pin_e2m1_encode_brute_force():
+    """The encoder equals an exhaustive nearest search over the 8 magnitudes
+    (ties to the even code, clamp at 6, sign of v < 0), on random values,
+    every midpoint and values past the largest."""
+    rng = np.random.default_rng(911)
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float64)
+    mids = (mags[1:] + mags[:-1]) / 2
+    v = np.concatenate([rng.uniform(-8, 8, 4000), mids, -mids, mags, -mags, [6.01, 9.0, 1e30, -1e30, 0.2499, 0.2501]])
+    got = MX.encode_e2m1(v)
+    for x, c in zip(v, got):
+        a = min(abs(x), 6.0)
+        dist = np.abs(mags - a)
+        best = np.flatnonzero(dist == dist.min())
+        want = int(best[0]) if len(best) == 1 else int(best[best % 2 == 0][0])
+        if x < 0:
+            want |= 8
+        assert int(c) == want, (x, int(c), want)
+
+
+def pin_mx_scale_exponent():
+    """Scale byte b gives amax / 2^(b - 127) in [4, 8) for every normal amax
+    (so the block's largest element lands in E2M1's top binade), read here
+    through frexp; zero and tiny maxima clamp to byte 0, inf gives 0xFF."""
+    rng = np.random.default_rng(912)
+    amax = (rng.random(5000) * 2.0 ** rng.integers(-120, 120, 5000)).astype(np.float32)
+    amax = amax[amax > 2.0 ** -120]
+    b = MX.mx_scale_byte(amax).astype(np.int64)
+    for a, bb in zip(amax.astype(np.float64), b):
+        m, e = math.frexp(a)                        # a = m 2^e, m in [0.5, 1)
+        assert bb - 127 == (e - 1) - 2, (a, bb)
+        assert 4.0 <= a / 2.0 ** (bb - 127) < 8.0
+    assert MX.mx_scale_byte(np.float32(0.0)) == 0
+    assert MX.mx_scale_byte(np.float32(2.0 ** -140)) == 0
+    assert MX.mx_scale_byte(np.float32(np.inf)) == 255
+
+
+def pin_mx_roundtrip():
+    """Representable blocks survive quantize -> dequantize exactly; random
+    blocks come back within half the local E2M1 spacing times the scale (or
+    at the +-6 clamp); scaling a block by 2^k moves the byte by k and keeps
+    the codes."""
+    rng = np.random.default_rng(913)
+    vec = 32
+    codes = rng.integers(0, 16, size=(64, vec))
+    codes[codes == 8] = 0                                    # -0 encodes as +0 (sign from v < 0)
+    codes[:, 0] = rng.choice([6, 7, 14, 15], size=64)       # a magnitude in [4, 6] fixes the exponent
+    e = rng.integers(-20, 20, size=(64, 1))
+    y = (MX.E2M1_TABLE[codes] * 2.0 ** e).astype(np.float32)
+    packed, sb = MX.quantize_mxfp4(y, vec)
+    assert _same(MX.dequantize_mxfp4(packed, sb, vec), y.astype(np.float64))
+    assert MX.encode_e2m1(np.array([-0.0]))[0] == 0
+    y = (rng.standard_normal((200, 64)) * 10.0 ** rng.uniform(-3, 3, (200, 1))).astype(np.float32)
+    for v in (16, 32):
+        packed, sb = MX.quantize_mxfp4(y, v)
+        back = MX.dequantize_mxfp4(packed, sb, v)
+        scale = np.repeat(MX.e8m0_value(sb), v, axis=-1)
+        t = np.abs(y.astype(np.float64)) / scale
+        half = np.where(t < 2, 0.25, np.where(t < 4, 0.5, 1.0))
+        err = np.abs(back - y)
+        ok = (err <= half * scale) | ((t > 6) & (np.abs(back) == 6 * scale))
+        assert ok.all()
+        p2, s2 = MX.quantize_mxfp4((y * np.float32(2.0 ** 5)).astype(np.float32), v)
+        assert np.array_equal(p2, packed) and np.array_equal(s2.astype(int), sb.astype(int) + 5)
+
+
+def pin_mx_output_of_attention():
+    """The MXFP4 output of an attention case dequantizes (code * 2^E / g) to
+    the dense output within the format's error, for g = 1 and g != 1."""
+    case = _tiny(914, q_lens=(5, 9), prefix_lens=(3, 0), batch=2, head_dim=32)
+    o, written = _run(case)
+    o = o[written]
+    for g in (1.0, 0.125, 48.0):
+        for v in (16, 32):
+            packed, sb = MX.mxfp4_output(o, v, g)
+            back = MX.dequantize_mxfp4(packed, sb, v, g)
+            blk = np.abs(o.reshape(o.shape[:-1] + (o.shape[-1] // v, v))).max(axis=-1)
+            tol = np.repeat(blk, v, axis=-1) / 4.0 + 1e-30   # half the largest spacing at the block's scale
+            assert (np.abs(back - o) <= tol).all(), (g, v)
+
+
 ALL_PINS = [
+    pin_mx_formats_golden,
+    pin_mx_hand_examples,
+    pin_e2m1_encode_brute_force,
+    pin_mx_scale_exponent,
+    pin_mx_roundtrip,
+    pin_mx_output_of_attention,
     pin_bf16_decode_all_codes,
     pin_e4m3fn_decode_all_codes,
     pin_number_format_golden,

@@ -163,3 +163,54 @@ def test_mutant_is_caught(name, monkeypatch):
         except Exception as exc:  # an AssertionError, or the mutant breaking outright
             caught.append((pin.__name__, type(exc).__name__))
     assert caught, f"no pin detects the planted mistake {name!r}"
+
+
+# ---- MXFP4 output encoding (oracle.mxfp4) -----------------------------------
+
+import oracle.mxfp4 as MX  # noqa: E402
+
+_mx_encode = MX.encode_e2m1
+_mx_scale = MX.mx_scale_byte
+_mx_quant = MX.quantize_mxfp4
+_mx_out = MX.mxfp4_output
+
+
+def _mx_round_log2_scale(amax):
+    # scale exponent from round(log2(amax)) instead of floor
+    a = np.asarray(amax, dtype=np.float64)
+    with np.errstate(divide="ignore"):
+        e = np.round(np.log2(np.where(a > 0, a, 1.0))) - 2
+    return np.where(np.isinf(a), 255, np.clip(e + 127, 0, 254)).astype(np.uint8)
+
+
+def _mx_swapped_nibbles(y, vec):
+    packed, sb = _mx_quant(y, vec)
+    return ((packed >> 4) | (packed << 4)).astype(np.uint8), sb
+
+
+MX_MUTANTS = {
+    "e2m1_ties_away": ("encode_e2m1", lambda v: _mx_encode(np.asarray(v, dtype=np.float64) * (1 + 1e-12))),
+    "e2m1_truncates": ("encode_e2m1", lambda v: _mx_encode(
+        np.sign(np.asarray(v, dtype=np.float64)) * np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])[
+            np.clip(np.searchsorted([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.minimum(np.abs(v), 6), side="right") - 1,
+                    0, 7)])),
+    "e2m1_sign_dropped": ("encode_e2m1", lambda v: _mx_encode(np.abs(np.asarray(v, dtype=np.float64)))),
+    "scale_one_low": ("mx_scale_byte", lambda a: np.where(_mx_scale(a) == 255, 255,
+                                                          np.maximum(_mx_scale(a).astype(int) - 1, 0)).astype(np.uint8)),
+    "scale_rounds_log2": ("mx_scale_byte", _mx_round_log2_scale),
+    "nibbles_swapped": ("quantize_mxfp4", _mx_swapped_nibbles),
+    "o_sf_scale_ignored": ("mxfp4_output", lambda o, vec, g=1.0: _mx_out(o, vec, 1.0)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MX_MUTANTS))
+def test_mx_mutant_is_caught(name, monkeypatch):
+    attr, repl = MX_MUTANTS[name]
+    monkeypatch.setattr(MX, attr, repl)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except Exception as exc:
+            caught.append((pin.__name__, type(exc).__name__))
+    assert caught, f"no pin detects the planted mistake {name!r}"

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PPA_ABI_VERSION 4
+#define PPA_ABI_VERSION 5
 
 typedef enum ppa_status {
   PPA_OK = 0,
@@ -70,7 +70,12 @@ typedef enum ppa_status {
 typedef enum ppa_dtype {
   PPA_DTYPE_BF16 = 1,          /* bfloat16                                          */
   PPA_DTYPE_FP8_E4M3FN = 2,    /* OCP float8 e4m3fn (no infinities, max 448)        */
-  PPA_DTYPE_FP32 = 3
+  PPA_DTYPE_FP32 = 3,
+  /* OCP Microscaling FP4 (MXFP4), output only: E2M1 element codes (sign,
+     2 exponent bits with bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5,
+     2, 3, 4, 6), two per byte with element 2i in the low nibble, plus one
+     E8M0 scale byte (2^(b - 127), 0xFF = NaN) per o_sf_vec_size elements. */
+  PPA_DTYPE_MXFP4 = 4
 } ppa_dtype;
 
 typedef enum ppa_kv_layout {
@@ -175,8 +180,12 @@ typedef struct ppa_params {
   /* Per-query-head fp32 sink logits [num_qo_heads], or NULL for none. */
   const float* sinks;
 
-  /* out [num_tokens, num_qo_heads, head_dim], dtype out_dtype (bf16).  Only
-     rows [cum_seq_lens_q[0], cum_seq_lens_q[batch_size]) are written. */
+  /* out [num_tokens, num_qo_heads, head_dim], dtype out_dtype: bf16, or
+     PPA_DTYPE_MXFP4 (see out_sf below), when out holds packed bytes
+     [num_tokens, num_qo_heads, head_dim / 2].  Strides count out's own
+     units (bf16 elements, or bytes for MXFP4); the last is 1 and the other
+     two are non-negative 16-byte multiples.  Only rows [cum_seq_lens_q[0],
+     cum_seq_lens_q[batch_size]) are written. */
   void* out;
   int32_t out_dtype;
   int64_t out_strides[3];
@@ -219,6 +228,29 @@ typedef struct ppa_params {
      bytes; a merge pass in the same call combines them and adds the sink
      once.  The result equals the unsplit call up to fp32 summation order. */
   int32_t kv_splits;
+
+  /* FP4 output (FlashInfer API page for trtllm_batch_context_with_kv_cache,
+     parameters out (an FP4 tensor), out_dtype, o_sf_scale and
+     o_sf_vec_size; the pages' NVIDIA FP4 format is carried out here as OCP
+     MXFP4).  Read only when out_dtype == PPA_DTYPE_MXFP4.  Per row, the
+     output o (fp32, after bmm2_scale and the softmax normalisation) becomes
+     y = fp32(o * o_sf_scale); every o_sf_vec_size consecutive elements of y
+     along head_dim form a block with scale 2^E, E = floor(log2(max |y|)) - 2
+     (clamped below at -127; an all-zero block stores byte 0, an infinite
+     maximum the NaN byte 0xFF with zero codes); each element is stored as
+     the E2M1 code nearest to y / 2^E (ties to the even code, saturated at
+     6, sign bit set when y < 0).  A reader recovers o ~ code * 2^E /
+     o_sf_scale.
+       out_sf         E8M0 scale bytes [num_tokens, num_qo_heads,
+                      head_dim / o_sf_vec_size], caller-owned device memory
+       out_sf_strides token and head strides in bytes (non-negative); the
+                      block index is contiguous
+       o_sf_scale     finite and > 0 (1 = plain MXFP4)
+       o_sf_vec_size  16 or 32 (32 is the OCP block size) */
+  uint8_t* out_sf;
+  int64_t out_sf_strides[2];
+  float o_sf_scale;
+  int32_t o_sf_vec_size;
 } ppa_params;
 
 /*
@@ -268,11 +300,17 @@ typedef struct ppa_merge_params {
   const float* o_parts;       /* [num_parts, num_rows, num_heads, head_dim] fp32, contiguous */
   const float* lse_parts;     /* [num_parts, num_rows, num_heads] fp32, contiguous */
   const float* sinks;         /* [num_heads] fp32 or NULL */
-  void* out;                  /* [num_rows, num_heads, head_dim], dtype out_dtype (bf16) */
+  void* out;                  /* [num_rows, num_heads, head_dim], dtype out_dtype: bf16, or MXFP4
+                                 packed bytes [num_rows, num_heads, head_dim / 2] */
   int32_t out_dtype;
-  int64_t out_strides[3];     /* elements; out_strides[2] == 1, the others even */
+  int64_t out_strides[3];     /* out's units (bf16 elements / bytes); out_strides[2] == 1, the others even */
   float* lse_out;             /* [num_rows, num_heads] fp32 or NULL */
   int64_t lse_out_strides[2];
+  /* MXFP4 output, as in ppa_params (read only when out_dtype == PPA_DTYPE_MXFP4) */
+  uint8_t* out_sf;
+  int64_t out_sf_strides[2];
+  float o_sf_scale;
+  int32_t o_sf_vec_size;
 } ppa_merge_params;
 
 /* ABI guards for bindings: the version this library was built with and

@@ -8,7 +8,7 @@ only marshals torch tensors into ``ppa_params``.  Every step of the
 attention runs in the HIP kernels; there is no fallback: importing this
 package without the built library raises ImportError.
 """
-from .binding import (PPA_ABI_VERSION, WORKSPACE_BYTES, PpaAppendParams, PpaError, PpaMergeParams,
+from .binding import (PPA_ABI_VERSION, PPA_DTYPE_MXFP4, WORKSPACE_BYTES, MxFp4Output, empty_mxfp4, PpaAppendParams, PpaError, PpaMergeParams,
                       append_paged_kv_cache, make_append_params, ppa_append_paged_kv, ppa_append_params_size,
                       ppa_merge_attention_states, ppa_validate_append,
                       ppa_merge_params_size, PpaParams, batch_context_with_kv_cache,  # noqa: F401

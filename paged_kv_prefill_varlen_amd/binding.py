@@ -9,17 +9,18 @@ from __future__ import annotations
 import ctypes
 import os
 from ctypes import c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint32, c_void_p
-from typing import Optional, Sequence, Tuple, Union
+from typing import NamedTuple, Optional, Sequence, Tuple, Union
 
 import numpy as np
 import torch
 
-PPA_ABI_VERSION = 4
+PPA_ABI_VERSION = 5
 
 # enums of ppa.h
 PPA_DTYPE_BF16 = 1
 PPA_DTYPE_FP8_E4M3FN = 2
 PPA_DTYPE_FP32 = 3
+PPA_DTYPE_MXFP4 = 4
 PPA_KV_LAYOUT_HND = 0
 PPA_KV_LAYOUT_NHD = 1
 PPA_KV_SPLIT = 0
@@ -82,6 +83,10 @@ class PpaParams(ctypes.Structure):
         ("lse", c_void_p),
         ("lse_strides", c_int64 * 2),
         ("kv_splits", c_int32),
+        ("out_sf", c_void_p),
+        ("out_sf_strides", c_int64 * 2),
+        ("o_sf_scale", c_float),
+        ("o_sf_vec_size", c_int32),
     ]
 
 
@@ -119,7 +124,58 @@ class PpaMergeParams(ctypes.Structure):
         ("out_strides", c_int64 * 3),
         ("lse_out", c_void_p),
         ("lse_out_strides", c_int64 * 2),
+        ("out_sf", c_void_p),
+        ("out_sf_strides", c_int64 * 2),
+        ("o_sf_scale", c_float),
+        ("o_sf_vec_size", c_int32),
     ]
+
+
+class MxFp4Output(NamedTuple):
+    """An MXFP4 output: ``data`` uint8 ``[rows, heads, head_dim / 2]`` (two
+    E2M1 codes per byte, element 2i in the low nibble), ``scale`` uint8
+    ``[rows, heads, head_dim / vec_size]`` (E8M0 block scales), and the
+    ``o_sf_scale`` g the output was multiplied by (o ~ code * 2^E / g)."""
+    data: torch.Tensor
+    scale: torch.Tensor
+    vec_size: int = 32
+    o_sf_scale: float = 1.0
+
+
+def empty_mxfp4(rows: int, heads: int, head_dim: int, device, vec_size: int = 32,
+                o_sf_scale: float = 1.0) -> MxFp4Output:
+    """Allocate an MXFP4 output for ``rows`` x ``heads`` rows of ``head_dim``."""
+    if head_dim % vec_size != 0:
+        raise ValueError("head_dim must be a multiple of vec_size")
+    return MxFp4Output(torch.empty((rows, heads, head_dim // 2), dtype=torch.uint8, device=device),
+                       torch.empty((rows, heads, head_dim // vec_size), dtype=torch.uint8, device=device),
+                       int(vec_size), float(o_sf_scale))
+
+
+def _set_out(p, out, shape) -> None:
+    """Point a PpaParams / PpaMergeParams at a bf16 tensor or an MxFp4Output
+    of logical shape ``shape`` = (rows, heads, head_dim)."""
+    rows, heads, d = (int(x) for x in shape)
+    if isinstance(out, MxFp4Output):
+        if out.data.dtype != torch.uint8 or tuple(out.data.shape) != (rows, heads, d // 2):
+            raise ValueError("MXFP4 data must be uint8 [rows, heads, head_dim / 2]")
+        if out.scale.dtype != torch.uint8 or tuple(out.scale.shape) != (rows, heads, d // max(1, out.vec_size)):
+            raise ValueError("MXFP4 scale must be uint8 [rows, heads, head_dim / vec_size]")
+        if out.scale.stride(2) != 1:
+            raise ValueError("MXFP4 scale bytes of a row must be contiguous")
+        p.out = _ptr(out.data)
+        p.out_dtype = PPA_DTYPE_MXFP4
+        p.out_strides[:] = list(out.data.stride())
+        p.out_sf = _ptr(out.scale)
+        p.out_sf_strides[:] = list(out.scale.stride()[:2])
+        p.o_sf_scale = float(out.o_sf_scale)
+        p.o_sf_vec_size = int(out.vec_size)
+    else:
+        if out.dim() != 3 or tuple(out.shape) != (rows, heads, d):
+            raise ValueError("out must have shape [rows, heads, head_dim]")
+        p.out = _ptr(out)
+        p.out_dtype = _dt(out)
+        p.out_strides[:] = list(out.stride())
 
 
 class PpaError(RuntimeError):
@@ -285,13 +341,13 @@ def ppa_merge_attention_states(o_parts: torch.Tensor, lse_parts: torch.Tensor, o
                                stream=None) -> None:
     """Log-sum-exp merge of partial states: ``o_parts`` fp32 ``[S, rows,
     heads, D]`` and ``lse_parts`` fp32 ``[S, rows, heads]`` (contiguous),
-    into ``out`` bf16 ``[rows, heads, D]`` and optionally ``lse_out`` fp32
+    into ``out`` (bf16 ``[rows, heads, D]`` or an ``MxFp4Output``) and optionally ``lse_out`` fp32
     ``[rows, heads]``; ``sinks`` fp32 ``[heads]`` adds one denominator term."""
     if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
         raise TypeError("o_parts and lse_parts must be float32")
     if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
         raise ValueError("o_parts and lse_parts must be contiguous")
-    if o_parts.dim() != 4 or lse_parts.shape != o_parts.shape[:3] or tuple(out.shape) != tuple(o_parts.shape[1:]):
+    if o_parts.dim() != 4 or lse_parts.shape != o_parts.shape[:3]:
         raise ValueError("shapes: o_parts [S, rows, heads, D], lse_parts [S, rows, heads], out [rows, heads, D]")
     m = PpaMergeParams()
     m.abi_version = PPA_ABI_VERSION
@@ -303,15 +359,13 @@ def ppa_merge_attention_states(o_parts: torch.Tensor, lse_parts: torch.Tensor, o
         if sinks.dtype != torch.float32 or sinks.numel() != m.num_heads or not sinks.is_contiguous():
             raise ValueError("sinks must be a contiguous float32 tensor of num_heads values")
         m.sinks = _ptr(sinks)
-    m.out = _ptr(out)
-    m.out_dtype = _dt(out)
-    m.out_strides[:] = list(out.stride())
+    _set_out(m, out, o_parts.shape[1:])
     if lse_out is not None:
         if lse_out.dtype != torch.float32 or tuple(lse_out.shape) != tuple(o_parts.shape[1:3]):
             raise ValueError("lse_out must be float32 [rows, heads]")
         m.lse_out = _ptr(lse_out)
         m.lse_out_strides[:] = list(lse_out.stride())
-    h = _stream_handle(out.device, stream)
+    h = _stream_handle(o_parts.device, stream)
     st = _lib.ppa_merge_attention_states(ctypes.byref(m), c_void_p(h))
     if st != 0:
         raise PpaError(st, "merge arguments rejected")
@@ -495,11 +549,7 @@ def make_params(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.
             raise ValueError("sinks must be a contiguous float32 tensor of num_qo_heads values")
         p.sinks = _ptr(sinks)
 
-    if out.dim() != 3 or tuple(out.shape) != tuple(query.shape):
-        raise ValueError("out must have the shape of query")
-    p.out = _ptr(out)
-    p.out_dtype = _dt(out)
-    p.out_strides[:] = list(out.stride())
+    _set_out(p, out, query.shape)
     if lse is not None:
         if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(query.shape[:2]):
             raise ValueError("lse must be float32 [num_tokens, num_qo_heads]")
@@ -530,14 +580,25 @@ def batch_context_with_kv_cache(query: torch.Tensor, kv_cache, workspace_buffer:
                                 out_dtype=None, kv_layout: str = "HND", sinks=None,
                                 validate: bool = False, stream=None, kv_indptr=None, kv_indices=None,
                                 kv_last_page_len=None, lse: Optional[torch.Tensor] = None,
-                                kv_splits: int = 0) -> torch.Tensor:
+                                kv_splits: int = 0, o_sf_scale: Optional[float] = None,
+                                o_sf_vec_size: Optional[int] = None):
     """Batched paged prefill attention; argument list of the API page
-    (without the nvfp4 output and PDL options), plus the optional flat page
-    table (kv_indptr / kv_indices / kv_last_page_len) in place of
-    block_tables, an optional fp32 ``lse`` [num_tokens, num_qo_heads] output
-    (natural-log softmax denominators) and ``kv_splits`` (split-KV; needs a
-    workspace of ``ppa_workspace_bytes`` bytes).  ``validate=True`` also runs
-    the deep metadata check on host copies (a device-to-host sync)."""
+    (without the PDL option), plus the optional flat page table (kv_indptr /
+    kv_indices / kv_last_page_len) in place of block_tables, an optional fp32
+    ``lse`` [num_tokens, num_qo_heads] output (natural-log softmax
+    denominators) and ``kv_splits`` (split-KV; needs a workspace of
+    ``ppa_workspace_bytes`` bytes).  The FP4 output of the API page is given
+    as OCP MXFP4: ``out_dtype="mxfp4"`` (or an ``MxFp4Output`` as ``out``)
+    with ``o_sf_scale`` (default 1) and ``o_sf_vec_size`` (16 or 32, default
+    32) returns an ``MxFp4Output``.  ``validate=True`` also runs the deep
+    metadata check on host copies (a device-to-host sync)."""
+    if isinstance(out_dtype, str):
+        if out_dtype.lower() != "mxfp4":
+            raise ValueError(f"out_dtype {out_dtype!r}: the FP4 output here is 'mxfp4' (OCP MX, E8M0 scales)")
+        if out is None:
+            out = empty_mxfp4(query.shape[0], query.shape[1], query.shape[2], query.device,
+                              32 if o_sf_vec_size is None else int(o_sf_vec_size),
+                              1.0 if o_sf_scale is None else float(o_sf_scale))
     if out is None:
         dt = query.dtype if out_dtype is None else out_dtype
         out = torch.empty(query.shape, dtype=dt, device=query.device)

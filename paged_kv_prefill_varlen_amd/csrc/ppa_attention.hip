@@ -109,6 +109,10 @@ struct AttnArgs {
   int32_t kv_splits;   // key-tile chunks per work item (1: none)
   float* o_part;       // split mode: [kv_splits, tokens, H_q, D] partial outputs
   float* lse_part;     // split mode: [kv_splits, tokens, H_q] partial log-denominators
+  int32_t out_mx;      // 0: bf16 out; 16 or 32: MXFP4 out (packed bytes) with that block size
+  uint8_t* out_sf;     // MXFP4: E8M0 scale bytes [tokens, H_q, D / out_mx]
+  int64_t sf_tok, sf_head;
+  float o_sf_scale;    // MXFP4: y = fp32(o) * o_sf_scale before blocking
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -153,6 +157,36 @@ __device__ __forceinline__ float pair_sum(float x) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_add_f32 %0, %0, %1"
                : "+v"(a), "+v"(b));
   return a;
+}
+
+// ---- MXFP4 output (OCP Microscaling FP4) -------------------------------------
+// E2M1 code of v, an element already divided by its block scale: the nearest
+// of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even code (each comparison puts
+// its midpoint on the even side: 0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0,
+// 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4), saturated at 6; sign bit for v < 0.
+// NaN fails every comparison and gives code 0.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = __builtin_fabsf(v);
+  const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
+                     (a > 5.f);
+  return v < 0.f ? (c | 8u) : c;
+}
+
+// E8M0 byte of the scale 2^E of a block with maximum magnitude amax:
+// E = floor(log2(amax)) - 2 (2 = exponent of E2M1's largest value), read
+// from the fp32 exponent field (a normal amax has floor(log2) = field - 127,
+// so the byte E + 127 is field - 2), clamped at byte 0 (zero and tiny
+// maxima); an infinite maximum gives the NaN byte 255.
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+  const uint32_t ex = (__builtin_bit_cast(uint32_t, amax) >> 23) & 0xffu;
+  return ex == 255u ? 255u : (ex > 2u ? ex - 2u : 0u);
+}
+
+// 2^-E for scale byte b (the float whose exponent field is 254 - b), exact
+// for every byte a finite maximum gives; 0 for the NaN byte, which turns every
+// element of such a block into code 0.
+__device__ __forceinline__ float mx_inv_scale(uint32_t b) {
+  return b == 255u ? 0.f : __builtin_bit_cast(float, (254u - b) << 23);
 }
 
 // Tile geometry.  Every wave stages 8 consecutive keys of both K and V of a
@@ -312,6 +346,39 @@ __device__ __forceinline__ void store_kv(const uint32_t* kraw, const uint32_t* v
     const int d = dg * T::V_DPT + 2 * i;
     *reinterpret_cast<u32x2*>(vlds + vt_offset(d, key0, T::VS)) = u32x2{lo01, lo23};
     *reinterpret_cast<u32x2*>(vlds + vt_offset(d + 1, key0, T::VS)) = u32x2{hi01, hi23};
+  }
+}
+
+// MXFP4 store of one output row from the PV accumulators.  Lane (col, half)
+// holds dims md*32 + 8g + 4half + e (e = 0..3) of its row, so a block of VEC
+// dims is split between the lane and its partner lane ^ 32, which hold the
+// same row: the block maximum is the pair maximum of the two lanes' maxima.
+// y = fp32(fp32(acc * inv) * g); codes go out 4 per 16-bit store, the
+// scale byte from the half-0 lane.
+template <int D, int VEC>
+__device__ __forceinline__ void store_mxfp4_row(const f32x16* oacc, float inv, float g, uint8_t* orow,
+                                                uint8_t* sfrow, int half) {
+  constexpr int GB = VEC / 8;   // 8-dim groups per block
+  for (int b = 0; b < D / VEC; ++b) {
+    const int md = b * VEC / 32;
+    const int g0 = (b * VEC % 32) / 8;
+    float y[GB][4];
+    float amax = 0.f;
+    for (int gg = 0; gg < GB; ++gg)
+      for (int e = 0; e < 4; ++e) {
+        y[gg][e] = (oacc[md][4 * (g0 + gg) + e] * inv) * g;
+        amax = fmaxf(amax, __builtin_fabsf(y[gg][e]));
+      }
+    amax = pair_max(amax);
+    const uint32_t sb = mx_scale_byte(amax);
+    const float rs = mx_inv_scale(sb);
+    for (int gg = 0; gg < GB; ++gg) {
+      uint32_t w = 0;
+      for (int e = 0; e < 4; ++e) w |= e2m1_code(y[gg][e] * rs) << (4 * e);
+      const int d = md * 32 + 8 * (g0 + gg) + 4 * half;
+      *reinterpret_cast<uint16_t*>(orow + d / 2) = static_cast<uint16_t>(w);
+    }
+    if (half == 0) sfrow[b] = static_cast<uint8_t>(sb);
   }
 }
 
@@ -561,6 +628,13 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   if (a.sinks) l += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - mb);
   if (a.lse != nullptr && half == 0) a.lse[trow * a.lse_tok + static_cast<int64_t>(h) * a.lse_head] = mb * kLn2 + __builtin_logf(l);
   const float inv = bmm2 / l;
+  if (a.out_mx != 0) {
+    uint8_t* orow8 = reinterpret_cast<uint8_t*>(a.out) + trow * a.o_tok + static_cast<int64_t>(h) * a.o_head;
+    uint8_t* sfrow = a.out_sf + trow * a.sf_tok + static_cast<int64_t>(h) * a.sf_head;
+    if (a.out_mx == 16) store_mxfp4_row<D, 16>(oacc, inv, a.o_sf_scale, orow8, sfrow, half);
+    else store_mxfp4_row<D, 32>(oacc, inv, a.o_sf_scale, orow8, sfrow, half);
+    return;
+  }
   uint16_t* orow = a.out + trow * a.o_tok + static_cast<int64_t>(h) * a.o_head;
   for (int md = 0; md < MD; ++md) {
     for (int g = 0; g < 4; ++g) {
@@ -676,7 +750,39 @@ struct MergeArgs {
   int64_t o_row, o_head;
   float* lse_out;
   int64_t l_row, l_head;
+  int32_t out_mx;           // 0: bf16 out; 16 or 32: MXFP4 out with that block size
+  uint8_t* out_sf;
+  int64_t sf_row, sf_head;
+  float o_sf_scale;
 };
+
+// MXFP4 store of one merged row: lane l holds elements [l E, l E + E), so a
+// block of VEC elements spans VEC / E consecutive lanes (an aligned group,
+// reduced with xor shuffles).  All 64 lanes of the wave take part.
+template <int D>
+__device__ __forceinline__ void merge_store_mxfp4(const float* acc, float inv, const MergeArgs& m, int row, int h,
+                                                  int lane) {
+  constexpr int E = D / 64;
+  const int L = m.out_mx / E;   // lanes per block: 8, 16 or 32
+  float y[E];
+  float amax = 0.f;
+  for (int e = 0; e < E; ++e) {
+    y[e] = (acc[e] * inv) * m.o_sf_scale;
+    amax = fmaxf(amax, __builtin_fabsf(y[e]));
+  }
+  for (int off = 1; off < L; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const uint32_t sb = mx_scale_byte(amax);
+  const float rs = mx_inv_scale(sb);
+  uint8_t* orow = reinterpret_cast<uint8_t*>(m.out) + row * m.o_row + h * m.o_head;
+  if constexpr (E == 2) {
+    orow[lane] = static_cast<uint8_t>(e2m1_code(y[0] * rs) | (e2m1_code(y[1] * rs) << 4));
+  } else {
+    const uint32_t c = e2m1_code(y[0] * rs);
+    const uint32_t next = static_cast<uint32_t>(__shfl_down(static_cast<int>(c), 1));
+    if ((lane & 1) == 0) orow[lane >> 1] = static_cast<uint8_t>(c | (next << 4));
+  }
+  if (lane % L == 0) m.out_sf[row * m.sf_row + h * m.sf_head + lane / L] = static_cast<uint8_t>(sb);
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs m) {
@@ -705,11 +811,15 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs m) {
     if (m.sinks) den += __expf(m.sinks[h] - mx);
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  uint16_t* orow = m.out + row * m.o_row + h * m.o_head + lane * E;
-  if constexpr (E == 2) {
-    *reinterpret_cast<uint32_t*>(orow) = pack_bf16(acc[0] * inv, acc[1] * inv);
+  if (m.out_mx != 0) {
+    merge_store_mxfp4<D>(acc, inv, m, row, h, lane);
   } else {
-    *orow = static_cast<uint16_t>(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
+    uint16_t* orow = m.out + row * m.o_row + h * m.o_head + lane * E;
+    if constexpr (E == 2) {
+      *reinterpret_cast<uint32_t*>(orow) = pack_bf16(acc[0] * inv, acc[1] * inv);
+    } else {
+      *orow = static_cast<uint16_t>(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
+    }
   }
   if (m.lse_out != nullptr && lane == 0)
     m.lse_out[row * m.l_row + h * m.l_head] = den > 0.f ? mx + __builtin_logf(den) : kNegInf;
@@ -821,6 +931,13 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
   a.lse = p->lse;
   a.lse_tok = p->lse_strides[0];
   a.lse_head = p->lse_strides[1];
+  if (p->out_dtype == PPA_DTYPE_MXFP4) {
+    a.out_mx = p->o_sf_vec_size;
+    a.out_sf = p->out_sf;
+    a.sf_tok = p->out_sf_strides[0];
+    a.sf_head = p->out_sf_strides[1];
+    a.o_sf_scale = p->o_sf_scale;
+  }
   a.kv_splits = p->kv_splits > 1 ? p->kv_splits : 1;
   if (a.kv_splits > 1) {
     // workspace: counters, then the partial outputs, then their log-denominators
@@ -864,6 +981,11 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
     m.lse_out = p->lse;
     m.l_row = p->lse_strides[0];
     m.l_head = p->lse_strides[1];
+    m.out_mx = a.out_mx;
+    m.out_sf = a.out_sf;
+    m.sf_row = a.sf_tok;
+    m.sf_head = a.sf_head;
+    m.o_sf_scale = a.o_sf_scale;
     e = launch_merge(m, p->head_dim, s);
   }
   return e == hipSuccess ? PPA_OK : PPA_ERR_HIP;
@@ -974,9 +1096,15 @@ extern "C" int32_t ppa_merge_attention_states(const ppa_merge_params* mp, void* 
   if (mp->abi_version != PPA_ABI_VERSION || mp->struct_size != sizeof(ppa_merge_params)) return PPA_ERR_ABI;
   if (mp->num_parts < 1 || mp->num_rows < 0 || mp->num_heads < 1) return PPA_ERR_SHAPE;
   if (mp->head_dim != 64 && mp->head_dim != 128) return PPA_ERR_HEAD_DIM;
-  if (mp->out_dtype != PPA_DTYPE_BF16) return PPA_ERR_DTYPE;
+  const bool mx = mp->out_dtype == PPA_DTYPE_MXFP4;
+  if (mp->out_dtype != PPA_DTYPE_BF16 && !mx) return PPA_ERR_DTYPE;
+  if (mx && ((mp->o_sf_vec_size != 16 && mp->o_sf_vec_size != 32) ||
+             !(mp->o_sf_scale > 0.f && mp->o_sf_scale <= 3.402823466e38f)))
+    return PPA_ERR_SHAPE;
   if (mp->num_rows == 0) return PPA_OK;
   if (mp->o_parts == nullptr || mp->lse_parts == nullptr || mp->out == nullptr) return PPA_ERR_NULL_POINTER;
+  if (mx && mp->out_sf == nullptr) return PPA_ERR_NULL_POINTER;
+  if (mx && (mp->out_sf_strides[0] < 0 || mp->out_sf_strides[1] < 0)) return PPA_ERR_STRIDE;
   if (mp->out_strides[2] != 1 || mp->out_strides[0] < 0 || mp->out_strides[1] < 0 ||
       (mp->out_strides[0] & 1) != 0 || (mp->out_strides[1] & 1) != 0)
     return PPA_ERR_STRIDE;
@@ -997,6 +1125,13 @@ extern "C" int32_t ppa_merge_attention_states(const ppa_merge_params* mp, void* 
   m.lse_out = mp->lse_out;
   m.l_row = mp->lse_out_strides[0];
   m.l_head = mp->lse_out_strides[1];
+  if (mx) {
+    m.out_mx = mp->o_sf_vec_size;
+    m.out_sf = mp->out_sf;
+    m.sf_row = mp->out_sf_strides[0];
+    m.sf_head = mp->out_sf_strides[1];
+    m.o_sf_scale = mp->o_sf_scale;
+  }
   return launch_merge(m, mp->head_dim, static_cast<hipStream_t>(stream)) == hipSuccess ? PPA_OK : PPA_ERR_HIP;
 }
 

@@ -142,8 +142,13 @@ int32_t ppa_validate_shapes(const ppa_params* p, char* msg, size_t msg_len) {
   // dtypes
   if (p->query_dtype != PPA_DTYPE_BF16)
     return fail(PPA_ERR_DTYPE, msg, msg_len, "query dtype %d: only bf16 is supported", p->query_dtype);
-  if (p->out_dtype != PPA_DTYPE_BF16)
-    return fail(PPA_ERR_DTYPE, msg, msg_len, "out dtype %d: only bf16 is supported", p->out_dtype);
+  if (p->out_dtype != PPA_DTYPE_BF16 && p->out_dtype != PPA_DTYPE_MXFP4)
+    return fail(PPA_ERR_DTYPE, msg, msg_len, "out dtype %d: bf16 or mxfp4", p->out_dtype);
+  const bool mxfp4 = p->out_dtype == PPA_DTYPE_MXFP4;
+  if (mxfp4 && p->o_sf_vec_size != 16 && p->o_sf_vec_size != 32)
+    return fail(PPA_ERR_SHAPE, msg, msg_len, "o_sf_vec_size %d: 16 or 32", p->o_sf_vec_size);
+  if (mxfp4 && !(p->o_sf_scale > 0.f && p->o_sf_scale <= 3.402823466e38f))
+    return fail(PPA_ERR_SHAPE, msg, msg_len, "o_sf_scale must be finite and > 0");
   if (p->kv_dtype != PPA_DTYPE_BF16 && p->kv_dtype != PPA_DTYPE_FP8_E4M3FN)
     return fail(PPA_ERR_DTYPE, msg, msg_len, "kv dtype %d: bf16 or fp8 e4m3fn", p->kv_dtype);
 
@@ -211,11 +216,15 @@ int32_t ppa_validate_shapes(const ppa_params* p, char* msg, size_t msg_len) {
   const int D = p->head_dim;
   if (p->query_strides[2] != 1 || p->out_strides[2] != 1)
     return fail(PPA_ERR_STRIDE, msg, msg_len, "query / out head_dim stride must be 1");
+  const int ob = mxfp4 ? 1 : 2;   // bytes per unit of out
   if (!row_stride_ok(p->query_strides[0], p->num_tokens, 2) ||
       !row_stride_ok(p->query_strides[1], p->num_qo_heads, 2) ||
-      !row_stride_ok(p->out_strides[0], p->num_tokens, 2) ||
-      !row_stride_ok(p->out_strides[1], p->num_qo_heads, 2))
+      !row_stride_ok(p->out_strides[0], p->num_tokens, ob) ||
+      !row_stride_ok(p->out_strides[1], p->num_qo_heads, ob))
     return fail(PPA_ERR_STRIDE, msg, msg_len, "query / out token and head strides must be 16-byte multiples");
+  if (mxfp4 && p->out_sf == nullptr) return fail(PPA_ERR_NULL_POINTER, msg, msg_len, "out_sf");
+  if (mxfp4 && (p->out_sf_strides[0] < 0 || p->out_sf_strides[1] < 0))
+    return fail(PPA_ERR_STRIDE, msg, msg_len, "out_sf strides must be non-negative");
   for (int w = 0; w < 2; ++w) {
     PlaneStrides s = plane_strides(p, w);
     if (s.dim != 1 && D > 1)

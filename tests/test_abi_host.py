@@ -438,6 +438,67 @@ def test_merge_argument_rejections():
     assert m(num_rows=0) == OK   # nothing to do, nothing launched
 
 
+def test_mxfp4_output_validation():
+    """MXFP4 output (the API page's FP4 out with o_sf_scale / o_sf_vec_size):
+    a valid description passes; each defect has its own status."""
+    E = ERR
+    for D in (64, 128):
+        c = _case(D=D)
+        T, H, _ = c["q"].shape
+        for vec in (16, 32):
+            c["out"] = B.empty_mxfp4(T, H, D, "cpu", vec, 0.5)
+            p = _params(c)
+            assert p.out_dtype == B.PPA_DTYPE_MXFP4 and p.o_sf_vec_size == vec and p.o_sf_scale == 0.5
+            assert list(p.out_strides) == [H * D // 2, D // 2, 1]
+            assert list(p.out_sf_strides) == [H * (D // vec), D // vec]
+            assert _shapes(p) == (OK, "")
+            assert _meta(p, c)[0] == OK
+    c = _case(D=64)
+    T, H, D = c["q"].shape
+    c["out"] = B.empty_mxfp4(T, H, D, "cpu")
+    assert _shapes(_params(c, out_sf=None))[0] == E["PPA_ERR_NULL_POINTER"]
+    for vec in (0, 8, 64):
+        assert _shapes(_params(c, o_sf_vec_size=vec))[0] == E["PPA_ERR_SHAPE"]
+    for g in (0.0, -1.0, float("inf"), float("nan")):
+        assert _shapes(_params(c, o_sf_scale=g))[0] == E["PPA_ERR_SHAPE"]
+    assert _shapes(_params(c, out_strides=[H * D // 2 + 8, D // 2, 1]))[0] == E["PPA_ERR_STRIDE"]
+    assert _shapes(_params(c, out_strides=[H * D // 2, D // 2, 2]))[0] == E["PPA_ERR_STRIDE"]
+    assert _shapes(_params(c, out_sf_strides=[-1, 2]))[0] == E["PPA_ERR_STRIDE"]
+    assert _shapes(_params(c, kv_splits=2, workspace=0))[0] == E["PPA_ERR_WORKSPACE"]
+    # the binding refuses shapes that do not match the query
+    with pytest.raises(ValueError):
+        _params(dict(c, out=B.empty_mxfp4(T, H, 128, "cpu")))
+    with pytest.raises(ValueError):
+        B.batch_context_with_kv_cache(c["q"], c["kv"], None, c["bt"], c["sl"], c["max_q"], c["max_kv"], 1.0, 1.0,
+                                      c["B"], c["cuq"], c["cukv"], out_dtype="nvfp4")
+
+
+def test_merge_mxfp4_rejections():
+    E = ERR
+    o = torch.zeros(2, 3, 4, 64)
+    l = torch.zeros(2, 3, 4)
+    mx = B.empty_mxfp4(3, 4, 64, "cpu")
+
+    def m(**over):
+        p = B.PpaMergeParams()
+        p.abi_version, p.struct_size = B.PPA_ABI_VERSION, ctypes.sizeof(B.PpaMergeParams)
+        p.num_parts, p.num_rows, p.num_heads, p.head_dim = 2, 3, 4, 64
+        p.o_parts, p.lse_parts = o.data_ptr(), l.data_ptr()
+        B._set_out(p, mx, (3, 4, 64))
+        for k, v in over.items():
+            if isinstance(getattr(p, k), ctypes.Array):
+                getattr(p, k)[:] = v
+            else:
+                setattr(p, k, v)
+        return int(B._lib.ppa_merge_attention_states(ctypes.byref(p), None))
+
+    assert m(o_sf_vec_size=8) == E["PPA_ERR_SHAPE"]
+    assert m(o_sf_scale=0.0) == E["PPA_ERR_SHAPE"]
+    assert m(out_sf=None) == E["PPA_ERR_NULL_POINTER"]
+    assert m(out_sf_strides=[-8, 2]) == E["PPA_ERR_STRIDE"]
+    assert m(num_rows=0) == OK
+
+
 # --------------------------------------------------------------------------
 # KV append arguments
 # --------------------------------------------------------------------------

@@ -17,8 +17,10 @@ Microscaling (MX) FP4 format that gfx950 supports, and takes these readings:
   E2M1's largest normal value, and E clamped below at -127 (so an all-zero
   block gets byte 0);  an infinite amax gives the NaN scale byte;
 * element code = the nearest E2M1 value to y / 2^E, ties to the even code,
-  magnitudes above 6 saturated to 6, the sign bit set when y < 0 (so a NaN
-  element encodes as +0);
+  magnitudes above 6 saturated to 6, the sign bit copied from y (so -0
+  encodes as the code for -0); a NaN element, which E2M1 cannot hold,
+  converts like an infinity of its sign, to +-6 (the convention of a
+  saturating conversion);
 * ``o_sf_scale`` = g multiplies the output before blocking,
   y = fp32(fp32(o) * g): the scale factors of g*o are g times those of o,
   and a reader dequantizes as code * 2^E / g;
@@ -51,17 +53,18 @@ E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
 
 def encode_e2m1(v: np.ndarray) -> np.ndarray:
     """Real values -> E2M1 codes (uint8 0..15): nearest representable
-    magnitude, ties to the even code, saturated at 6; sign bit for v < 0."""
+    magnitude, ties to the even code, saturated at 6 (NaN as well); the sign
+    bit is the sign bit of v."""
     v = np.asarray(v, dtype=np.float64)
     grid = E2M1_TABLE[:8]                          # codes 0..7, ascending 0..6
-    a = np.where(np.isnan(v), 0.0, np.minimum(np.abs(v), E2M1_MAX))
+    a = np.where(np.isnan(v), E2M1_MAX, np.minimum(np.abs(v), E2M1_MAX))
     hi = np.clip(np.searchsorted(grid, a, side="left"), 0, 7)
     lo = np.clip(hi - 1, 0, 7)
     d_lo = a - grid[lo]
     d_hi = grid[hi] - a
     take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
     code = np.where(take_hi, hi, lo).astype(np.uint8)
-    return np.where(v < 0, code | np.uint8(8), code).astype(np.uint8)
+    return np.where(np.signbit(v), code | np.uint8(8), code).astype(np.uint8)
 
 
 def e8m0_value(byte) -> np.ndarray:

@@ -58,8 +58,10 @@ def causal_pairs(case) -> int:
     return total
 
 
-def algorithmic_bytes(case) -> int:
-    """Compulsory HBM bytes: Q read + O written + every KV token some query reaches, once."""
+def algorithmic_bytes(case, out_elem_bytes: float = 2.0) -> int:
+    """Compulsory HBM bytes: Q read + O written (``out_elem_bytes`` per
+    element: 2 for bf16, 1/2 + 1/vec for MXFP4 codes and scales) + every KV
+    token some query reaches, once."""
     D, Hq, Hkv = case["head_dim"], case["num_qo_heads"], case["num_kv_heads"]
     eb = 1 if case["kv_dtype"] != "bf16" else 2
     W = case["window_left"]
@@ -70,7 +72,7 @@ def algorithmic_bytes(case) -> int:
             continue
         lo = 0 if W < 0 else max(0, kv - q - W)
         kv_reach += kv - lo
-    return tokens * Hq * D * 2 * 2 + kv_reach * Hkv * D * eb * 2
+    return int(tokens * Hq * D * (2 + out_elem_bytes)) + kv_reach * Hkv * D * eb * 2
 
 
 def cpu_baseline(case, budget_s: float = 12.0):
@@ -145,6 +147,62 @@ def copy_calibration(nbytes: int = 1 << 28, reps: int = 3) -> None:
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def traffic_summary(config: str, dirs) -> None:
+    """Write profiles/hbm_traffic_<config>.json from four rocprofv3 --pmc
+    output folders (csv): FETCH_SIZE and WRITE_SIZE of the workload's
+    attention kernel, then of the copy calibration.  The counters read KiB
+    per dispatch; each is scaled by the bytes the calibration's add kernel is
+    known to move (256 MiB each way) over what the same counter read for it."""
+    import csv
+    import statistics
+
+    def values(folder, counter, match, last=None):
+        with open(os.path.join(folder, "run_counter_collection.csv")) as f:
+            v = [float(r["Counter_Value"]) for r in csv.DictReader(f)
+                 if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
+        return v[-last:] if last else v
+
+    kern = lambda n: "paged_prefill" in n          # noqa: E731
+    add = lambda n: "elementwise" in n             # noqa: E731
+    fetch = values(dirs[0], "FETCH_SIZE", kern)
+    write = values(dirs[1], "WRITE_SIZE", kern)
+    cfetch = values(dirs[2], "FETCH_SIZE", add, 3)
+    cwrite = values(dirs[3], "WRITE_SIZE", add, 3)
+    kib = (1 << 28) / 1024
+    fs = kib / statistics.mean(cfetch)
+    ws = kib / statistics.mean(cwrite)
+    rd = statistics.mean(fetch) * 1024 * fs
+    wr = statistics.mean(write) * 1024 * ws
+    out = {
+        "kernel": "paged_prefill_persistent (the workload's bf16 or fp8 instance)",
+        "workload": config,
+        "fetch_kib_per_dispatch": [round(x, 1) for x in fetch],
+        "write_kib_per_dispatch": [round(x, 1) for x in write],
+        "calibration": {"kernel": "torch.add(src, 1.0, out=dst), float32, 256 MiB each way",
+                        "fetch_kib": [round(x, 1) for x in cfetch], "write_kib": [round(x, 1) for x in cwrite],
+                        "fetch_scale": round(fs, 5), "write_scale": round(ws, 5)},
+        "read_bytes": int(rd),
+        "write_bytes": int(wr),
+        "traffic_bytes": int(rd + wr),
+        "kernel_source_sha256": kernel_source_digest(),
+        "commands": [
+            "cd /tmp && export TMPDIR=/tmp",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch dir> -o run -- python3 bench.py "
+            f"--steps 2 --warmup 1 --no-cpu --config {config}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write dir> -o run -- python3 bench.py "
+            f"--steps 2 --warmup 1 --no-cpu --config {config}",
+            "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <copy dirs> -o run -- "
+            "python3 bench.py --copy-calibration",
+            f"python3 bench.py --config {config} --traffic-summary <fetch dir> <write dir> <copy fetch dir> "
+            "<copy write dir>",
+        ],
+    }
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{config}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps({"wrote": path, "traffic_bytes": out["traffic_bytes"]}))
+
+
 def bench_append(args) -> None:
     """Time ppa_append_paged_kv (HBM-bound): new K/V read, cache written."""
     import torch
@@ -217,9 +275,18 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--kv-splits", type=int, default=0, help="split-KV chunks per work item (0: none)")
+    ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "mxfp4"],
+                    help="output: bf16, or MXFP4 codes + E8M0 block scales")
+    ap.add_argument("--o-sf-vec-size", type=int, default=32, choices=[16, 32])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar="DIR",
+                    help="write profiles/hbm_traffic_<config>.json from rocprofv3 FETCH_SIZE / WRITE_SIZE "
+                         "folders of the workload and of --copy-calibration")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args.config, args.traffic_summary)
+        return
     if args.copy_calibration:
         copy_calibration()
         return
@@ -249,7 +316,10 @@ def main():
     cuq = case["cum_seq_lens_q"].to(dev)
     cukv = case["cum_seq_lens_kv"].to(dev)
     sinks = None if case["sinks"] is None else case["sinks"].to(dev)
-    out = torch.empty_like(q)
+    if args.out_dtype == "mxfp4":
+        out = ppa.empty_mxfp4(q.shape[0], q.shape[1], q.shape[2], dev, args.o_sf_vec_size, 1.0)
+    else:
+        out = torch.empty_like(q)
     # zeroed scheduler workspace: persistent workgroups pull balanced work
     # (larger with split-KV: it also holds the partial states)
     p = ppa.make_params(q, kv, None, bt, sl, case["max_q_len"], case["max_kv_len"], case["bmm1_scale"],
@@ -292,7 +362,7 @@ def main():
     kernel_tflops = flops / (launch_ms * 1e-3) / 1e12
     fp8 = case["kv_dtype"] != "bf16"
     hbm = args.config == "decode"
-    alg_bytes = algorithmic_bytes(case)
+    alg_bytes = algorithmic_bytes(case, 2.0 if args.out_dtype == "bf16" else 0.5 + 1.0 / args.o_sf_vec_size)
     if hbm:   # decode streams K/V once: report bandwidth against the HBM roofline
         kernel_gbs = alg_bytes / (launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -300,7 +370,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(kernel_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": stored_traffic(args.config)}
+                "traffic": stored_traffic(args.config) if args.out_dtype == "bf16" else None}
     roof.update({"algorithmic_bytes": alg_bytes, "kernel_ms": round(launch_ms, 5),
                  "kernel": "paged_prefill_persistent<%d,%s>%s" % (case["head_dim"], "fp8" if fp8 else "bf16",
                                                                   " + merge" if args.kv_splits > 1 else "")})
@@ -319,7 +389,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config,
                    "query_tokens": tokens, "causal_gflop": round(flops / 1e9, 3),
-                   "kv_splits": args.kv_splits, "parallelism": "none (one GPU)"},
+                   "kv_splits": args.kv_splits, "out": args.out_dtype if args.out_dtype == "bf16"
+                   else f"mxfp4/{args.o_sf_vec_size}", "parallelism": "none (one GPU)"},
         "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": roof,

@@ -160,17 +160,13 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 // ---- MXFP4 output (OCP Microscaling FP4) -------------------------------------
-// E2M1 code of v, an element already divided by its block scale: the nearest
-// of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even code (each comparison puts
-// its midpoint on the even side: 0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0,
-// 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4), saturated at 6; sign bit for v < 0.
-// NaN fails every comparison and gives code 0.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float a = __builtin_fabsf(v);
-  const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
-                     (a > 5.f);
-  return v < 0.f ? (c | 8u) : c;
-}
+// Elements are encoded by gfx950's scaled FP4 conversion
+// (v_cvt_scalef32_pk_fp4_f32: two fp32 values -> two E2M1 codes in one byte
+// of the result).  Measured on the device: it divides by 2^(exponent field of
+// the scale operand - 127), i.e. it reads the scale as an E8M0 value; rounds
+// to the nearest E2M1 value with ties to the even code; saturates at 6; copies
+// the sign bit (-0 gives the -0 code); and turns NaN into +-6.  That is the
+// encoding the oracle states.
 
 // E8M0 byte of the scale 2^E of a block with maximum magnitude amax:
 // E = floor(log2(amax)) - 2 (2 = exponent of E2M1's largest value), read
@@ -182,11 +178,17 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
   return ex == 255u ? 255u : (ex > 2u ? ex - 2u : 0u);
 }
 
-// 2^-E for scale byte b (the float whose exponent field is 254 - b), exact
-// for every byte a finite maximum gives; 0 for the NaN byte, which turns every
-// element of such a block into code 0.
-__device__ __forceinline__ float mx_inv_scale(uint32_t b) {
-  return b == 255u ? 0.f : __builtin_bit_cast(float, (254u - b) << 23);
+// The conversion's scale operand for byte b: the float 2^(b - 127) (for
+// b = 0 the subnormal 2^-127).  A block with the NaN byte gets zero codes
+// from the caller instead.
+__device__ __forceinline__ float mx_scale_operand(uint32_t b) {
+  return __builtin_bit_cast(float, b != 0u ? b << 23 : 0x00400000u);
+}
+
+// Four consecutive elements -> four codes in the low 16 bits.
+__device__ __forceinline__ uint32_t mx_pack4(float y0, float y1, float y2, float y3, float scale) {
+  const uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y0, y1, scale, 0);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y2, y3, scale, 1);
 }
 
 // Tile geometry.  Every wave stages 8 consecutive keys of both K and V of a
@@ -371,10 +373,10 @@ __device__ __forceinline__ void store_mxfp4_row(const f32x16* oacc, float inv, f
       }
     amax = pair_max(amax);
     const uint32_t sb = mx_scale_byte(amax);
-    const float rs = mx_inv_scale(sb);
+    const float sc = mx_scale_operand(sb);
     for (int gg = 0; gg < GB; ++gg) {
-      uint32_t w = 0;
-      for (int e = 0; e < 4; ++e) w |= e2m1_code(y[gg][e] * rs) << (4 * e);
+      uint32_t w = mx_pack4(y[gg][0], y[gg][1], y[gg][2], y[gg][3], sc);
+      w = sb == 255u ? 0u : w;
       const int d = md * 32 + 8 * (g0 + gg) + 4 * half;
       *reinterpret_cast<uint16_t*>(orow + d / 2) = static_cast<uint16_t>(w);
     }
@@ -772,14 +774,15 @@ __device__ __forceinline__ void merge_store_mxfp4(const float* acc, float inv, c
   }
   for (int off = 1; off < L; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   const uint32_t sb = mx_scale_byte(amax);
-  const float rs = mx_inv_scale(sb);
+  const float sc = mx_scale_operand(sb);
   uint8_t* orow = reinterpret_cast<uint8_t*>(m.out) + row * m.o_row + h * m.o_head;
   if constexpr (E == 2) {
-    orow[lane] = static_cast<uint8_t>(e2m1_code(y[0] * rs) | (e2m1_code(y[1] * rs) << 4));
-  } else {
-    const uint32_t c = e2m1_code(y[0] * rs);
-    const uint32_t next = static_cast<uint32_t>(__shfl_down(static_cast<int>(c), 1));
-    if ((lane & 1) == 0) orow[lane >> 1] = static_cast<uint8_t>(c | (next << 4));
+    const uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], sc, 0);
+    orow[lane] = static_cast<uint8_t>(sb == 255u ? 0u : w);
+  } else {   // the odd lane's element joins the even lane's byte
+    const float next = __shfl_down(y[0], 1);
+    const uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], next, sc, 0);
+    if ((lane & 1) == 0) orow[lane >> 1] = static_cast<uint8_t>(sb == 255u ? 0u : w);
   }
   if (lane % L == 0) m.out_sf[row * m.sf_row + h * m.sf_head + lane / L] = static_cast<uint8_t>(sb);
 }

@@ -52,6 +52,8 @@ namespace ppa {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short v4s16;
+typedef __attribute__((ext_vector_type(8))) short v8s16;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
@@ -194,12 +196,17 @@ __device__ __forceinline__ uint32_t mx_pack4(float y0, float y1, float y2, float
 // Tile geometry.  Every wave stages 8 consecutive keys of both K and V of a
 // 64-key tile, so the staging work is the same for all waves and, with pages
 // of >= 8 tokens, a wave's keys lie in one page whose id is wave-uniform.
-// K goes to LDS in natural [key][dim] layout (row stride padded by 16 bytes,
-// so the S operand reads, 16 different rows per 16 lanes, hit distinct
-// banks).  V goes as 4 consecutive keys x V_DPT dims per lane, transposed in
-// registers to [dim][key], with the 16-byte key chunks of each dim row XOR
-// swizzled by (dim >> 4) & 7 and rows padded by 16 bytes, which keeps both the
-// transposed writes and the MFMA operand reads free of bank conflicts.
+// bf16 cache: K and V tiles are copied from the pages into LDS without
+// passing through registers (fetch_kv_lds), in natural [key][dim] layout with
+// unpadded rows whose 16-byte chunks are XOR swizzled by key (kswz, vswz), in
+// a three-stage ring.  The PV operand, V^T, is read with LDS transpose loads.
+// fp8 cache: staged through registers (widened to bf16 once per workgroup);
+// K in natural layout with the row stride padded by 16 bytes, so the S
+// operand reads, 16 different rows per 16 lanes, hit distinct banks; V as 4
+// consecutive keys x V_DPT dims per lane, transposed in registers to
+// [dim][key], with the 16-byte key chunks of each dim row XOR swizzled by
+// (dim >> 4) & 7 and rows padded by 16 bytes, which keeps both the transposed
+// writes and the MFMA operand reads free of bank conflicts; two stages.
 template <int D, bool FP8>
 struct Tile {
   static constexpr int EB = FP8 ? 1 : 2;        // bytes per cache element
@@ -211,12 +218,14 @@ struct Tile {
   static constexpr int K_RPI = 64 / K_TPR;      // key rows per wave instruction
   static constexpr int V_DPT = D / 32;          // dims per lane (32 dim groups)
   static constexpr int V_KEY_BYTES = V_DPT * EB;   // raw bytes per key per lane
-  static constexpr int K_DW = K_LANE_BYTES / 4;
-  static constexpr int V_DW = (4 * V_KEY_BYTES + 3) / 4;
-  static constexpr int KS = D + 8;
+  static constexpr bool DMA = !FP8;             // bf16: pages -> LDS directly
+  static constexpr int STAGES = DMA ? 3 : 2;     // LDS ring depth
+  static constexpr int K_DW = DMA ? 1 : K_LANE_BYTES / 4;
+  static constexpr int V_DW = DMA ? 1 : (4 * V_KEY_BYTES + 3) / 4;
+  static constexpr int KS = DMA ? D : D + 8;
   static constexpr int VS = kBK + 8;
   static constexpr int K_ELEMS = kBK * KS;
-  static constexpr int V_ELEMS = D * VS;
+  static constexpr int V_ELEMS = DMA ? kBK * D : D * VS;
   static_assert(K_PASSES * K_RPI == 8, "K staging map");
 };
 
@@ -240,7 +249,98 @@ __device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src, bo
   }
 }
 
-// ---- staging: pages -> registers --------------------------------------------
+// ---- staging, bf16 cache: pages -> LDS directly --------------------------------
+// Swizzle keys: chunk c (16 bytes) of LDS row `key` sits in slot c ^ swz(key).
+// K: sixteen lanes read one chunk index of sixteen consecutive rows for the S
+// operand; key mod 16 (D = 128, 256-byte rows) or (key / 2) mod 8 (D = 64,
+// two rows per 256 bytes) puts them on distinct banks.  V: a transpose load
+// makes each 16-lane group read 4 consecutive keys x 32 bytes; 4 (key mod 4)
+// (D = 128) or 4 ((key / 2) mod 2) (D = 64) spreads the 32 lanes of a half
+// wave over 256 distinct bytes.
+template <int D>
+__device__ __forceinline__ int kswz(int key) {
+  return D == 128 ? (key & 15) : ((key >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int key) {
+  return D == 128 ? ((key & 3) << 2) : (((key >> 1) & 1) << 2);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// global_load_lds_dwordx4 moves 16 bytes per lane into LDS at the wave-uniform
+// base in M0, lane i at base + 16 i: one instruction fills 1 KB, 64 / (D / 8)
+// whole rows.  Each lane loads the global chunk that belongs at its slot.
+// The copies are issued from inline asm so that the compiler does not see an
+// LDS store in flight: it would otherwise wait for it before every LDS read
+// of the other stages.  The caller waits with vmcnt for them; vector memory
+// operations retire in order, so the compiler's own vmcnt waits stay correct
+// (at worst longer) with these in the count.  M0 is written here and nowhere
+// else in these kernels, and an LDS copy reading M0 needs one wait state
+// after the SALU write (the s_nop).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 in the clobber list: see above
+__device__ __forceinline__ void lds_copy16(uint32_t lds_base, const uint8_t* src) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy16(uint32_t lds_base, const uint8_t* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase),
+               "s"(lds_base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Copies issued per wave per tile (K and V): the vmcnt step of the ring.
+template <int D>
+constexpr int kDmaOps = 2 * (8 * D * 2 / 1024);
+
+// The wave's keys [kb, kb + 8) of K and V into the tile's LDS stage.  Fast
+// path (`id` is their page, the tile is not the last of the request): 32-bit
+// offsets from the wave-uniform page base.  General path: every lane
+// resolves its key through the page table, clamped to the sequence; a
+// clamped copy is a valid key whose weight the mask sets to exactly 0.
+template <int D, bool FAST>
+__device__ __forceinline__ void fetch_kv_lds(__bf16* kt, __bf16* vt, const AttnArgs& a, const PageTable& pt, int id,
+                                             int hk, int kb, int kv_len, int page_mask, int wave, int lane) {
+  constexpr int TPR = D / 8;      // 16-byte chunks per row
+  constexpr int RPI = 64 / TPR;   // rows per copy instruction
+  const uint8_t* kbase = a.k.base;
+  const uint8_t* vbase = a.v.base;
+  if (FAST) {
+    kbase += (static_cast<int64_t>(id) * a.k.page_stride + static_cast<int64_t>(hk) * a.k.head_stride) * 2;
+    vbase += (static_cast<int64_t>(id) * a.v.page_stride + static_cast<int64_t>(hk) * a.v.head_stride) * 2;
+  }
+  for (int p = 0; p < 8 / RPI; ++p) {
+    const int rl = p * RPI + lane / TPR;            // key of the wave, 0..7
+    const int row = 8 * wave + rl;                   // key of the tile
+    const int kc = (lane % TPR) ^ kswz<D>(row);
+    const int vc = (lane % TPR) ^ vswz<D>(row);
+    const uint32_t kdst = lds_addr(kt + (8 * wave + p * RPI) * D);
+    const uint32_t vdst = lds_addr(vt + (8 * wave + p * RPI) * D);
+    if (FAST) {
+      const int slot = (kb & page_mask) + rl;
+      lds_copy16(kdst, kbase, static_cast<uint32_t>((slot * static_cast<int>(a.k.tok_stride) + kc * 8) * 2));
+      lds_copy16(vdst, vbase, static_cast<uint32_t>((slot * static_cast<int>(a.v.tok_stride) + vc * 8) * 2));
+    } else {
+      const int key = kb + rl;
+      const int k = key < kv_len ? key : kv_len - 1;
+      const int pid = page_id(pt, k);
+      lds_copy16(kdst, token_row<2>(a.k, pid, page_mask, k, hk, kc * 8));
+      lds_copy16(vdst, token_row<2>(a.v, pid, page_mask, k, hk, vc * 8));
+    }
+  }
+}
+
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt not waited on), n < 16.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
+
+// ---- staging, fp8 cache: pages -> registers -------------------------------------
 // The wave's keys are [kb, kb + 8).  Fast path (`id` is their page, the tile is
 // not the last one of the request): rows are addressed by 32-bit offsets from
 // the wave-uniform page base.  General path: every lane resolves its own keys
@@ -393,8 +493,8 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   using T = Tile<D, FP8>;
   constexpr int KSTEPS = D / 16;   // MFMA K-steps over head_dim
   constexpr int MD = D / 32;       // 32-wide head_dim tiles of O^T
-  __shared__ __attribute__((aligned(16))) __bf16 klds[2][T::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) __bf16 vlds[2][T::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) __bf16 klds[T::STAGES][T::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) __bf16 vlds[T::STAGES][T::V_ELEMS];
 
   // ---- which work item --------------------------------------------------
   // item = (query tile from the last, key chunk, request, kv head, head group)
@@ -454,7 +554,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   const int wkey_lo = W >= 0 ? (wpos_first - W > 0 ? wpos_first - W : 0) : 0;
 
   bf16x8 qf[KSTEPS];   // B operand of S^T = K Q^T
-  {
+  auto load_q = [&]() {
     const uint16_t* qrow = a.q + static_cast<int64_t>(q0 + t0 + tok) * a.q_tok +
                            static_cast<int64_t>(h0 + hd) * a.q_head;
     for (int s = 0; s < KSTEPS; ++s) {
@@ -463,7 +563,11 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
       if (negate_q) x ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
       qf[s] = __builtin_bit_cast(bf16x8, x);
     }
-  }
+  };
+  // direct-copy path: Q is loaded after the first tile's copies are issued
+  // (below), and both are waited for together, so that no later compiler
+  // wait for Q covers the prefetched tiles
+  if constexpr (!T::DMA) load_q();
 
   f32x16 oacc[MD];
   for (int md = 0; md < MD; ++md) oacc[md] = f32x16{};
@@ -498,27 +602,59 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   // 16 ks + 8 half .. + 7; in the swizzled layout that key chunk is
   // 2 (ks ^ md) + (half ^ (col >> 4))
   const int vrow_base = col * T::VS + ((half ^ (col >> 4)) & 1) * 8;
+  // transpose-load addresses (direct-copy layout): group G = lane / 16,
+  // jj = lane % 16; key 8 (G / 2) + jj / 4 (+ 16 ks, + 4 for the second
+  // load), dims md*32 + 16 (G % 2) + 4 (jj % 4), i.e. 16-byte chunk
+  // 4 md + 2 (G % 2) + (jj % 4) / 2 at byte 8 (jj % 2) of it, in slot
+  // chunk ^ vswz(key) (vswz depends only on jj / 4 here)
+  int vt_lane = 0, vt_md[MD];
+  if constexpr (T::DMA) {
+    const int G = lane >> 4, jj = lane & 15;
+    const int key = 8 * (G >> 1) + (jj >> 2);
+    vt_lane = key * (2 * D) + (jj & 1) * 8;
+    for (int md = 0; md < MD; ++md) vt_md[md] = ((4 * md + 2 * (G & 1) + ((jj & 3) >> 1)) ^ vswz<D>(key)) * 16;
+  }
 
   auto wave_tile = [&](int j) {
     return wave_active && j * kBK <= wkey_hi && j * kBK + kBK - 1 >= wkey_lo;
   };
   auto page_of = [&](int j) { return UPAGE ? page_id_uniform(pt, uniform(j * kBK + 8 * wave)) : 0; };
   // copy the wave's 8 keys of tile j into registers; `id` is their page id
+  // LDS stage of tile j
+  auto stage = [&](int j) { return T::DMA ? (j - tile_lo) % 3 : (j - tile_lo) & 1; };
   auto stage_fetch = [&](int j, int id) {
     const int kb = j * kBK + 8 * wave;
-    if (UPAGE && j * kBK + kBK <= kv_len) fetch_kv<D, FP8, true>(kraw, vraw, a, pt, id, hk, kb, kv_len, page_mask, lane);
-    else fetch_kv<D, FP8, false>(kraw, vraw, a, pt, id, hk, kb, kv_len, page_mask, lane);
+    const bool fast = UPAGE && j * kBK + kBK <= kv_len;
+    if constexpr (T::DMA) {
+      const int st = stage(j);
+      if (fast) fetch_kv_lds<D, true>(klds[st], vlds[st], a, pt, id, hk, kb, kv_len, page_mask, wave, lane);
+      else fetch_kv_lds<D, false>(klds[st], vlds[st], a, pt, id, hk, kb, kv_len, page_mask, wave, lane);
+    } else {
+      if (fast) fetch_kv<D, FP8, true>(kraw, vraw, a, pt, id, hk, kb, kv_len, page_mask, lane);
+      else fetch_kv<D, FP8, false>(kraw, vraw, a, pt, id, hk, kb, kv_len, page_mask, lane);
+    }
   };
   auto stage_store = [&](int j) {
-    const int buf = (j - tile_lo) & 1;
+    const int buf = stage(j);
     store_kv<D, FP8>(kraw, vraw, klds[buf], vlds[buf], wave, lane);
   };
+  // S operand, direct-copy layout: lane (col, half) reads K rows krow_lane
+  // (+ 32) at chunk 2 s + half, whose slot is (2 s + half) ^ kswz(row); the
+  // swizzle key is the same for both rows
+  const int kx = T::DMA ? (kswz<D>(krow_lane) ^ half) : 0;
   auto gemm_s = [&](int j) {
-    const __bf16* kbuf = klds[(j - tile_lo) & 1] + krow_lane * T::KS + half * 8;
     bf16x8 kf[2][KSTEPS];
-    for (int s = 0; s < KSTEPS; ++s)
-      for (int mt = 0; mt < 2; ++mt)
-        kf[mt][s] = *reinterpret_cast<const bf16x8*>(kbuf + mt * 32 * T::KS + s * 16);
+    if constexpr (T::DMA) {
+      const __bf16* kbuf = klds[stage(j)] + krow_lane * D;
+      for (int s = 0; s < KSTEPS; ++s)
+        for (int mt = 0; mt < 2; ++mt)
+          kf[mt][s] = *reinterpret_cast<const bf16x8*>(kbuf + mt * 32 * D + ((2 * s) ^ kx) * 8);
+    } else {
+      const __bf16* kbuf = klds[stage(j)] + krow_lane * T::KS + half * 8;
+      for (int s = 0; s < KSTEPS; ++s)
+        for (int mt = 0; mt < 2; ++mt)
+          kf[mt][s] = *reinterpret_cast<const bf16x8*>(kbuf + mt * 32 * T::KS + s * 16);
+    }
     __builtin_amdgcn_sched_barrier(0);
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
@@ -526,11 +662,28 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
       for (int mt = 0; mt < 2; ++mt) sacc[mt] = mfma32(kf[mt][s], qf[s], sacc[mt]);
   };
   auto gemm_pv = [&](int j) {
-    const __bf16* vbuf = vlds[(j - tile_lo) & 1] + vrow_base;
     bf16x8 vf[MD][4];
-    for (int ks = 0; ks < 4; ++ks)
-      for (int md = 0; md < MD; ++md)
-        vf[md][ks] = *reinterpret_cast<const bf16x8*>(vbuf + md * 32 * T::VS + ((ks ^ md) & 3) * 16);
+    if constexpr (T::DMA) {
+      // V^T operand by transpose loads: in each 16-lane group, lane jj points
+      // at key +jj/4, dims +4 (jj%4) and receives keys +0..3 of dim +jj; two
+      // loads give the 8 keys 16 ks + 8 half + 0..7 of dim md*32 + col
+      const char* vbuf = reinterpret_cast<const char*>(vlds[stage(j)]) + vt_lane;
+      for (int ks = 0; ks < 4; ++ks)
+        for (int md = 0; md < MD; ++md) {
+          typedef __attribute__((address_space(3))) v4s16 lds_v4s16;
+          const char* p0 = vbuf + vt_md[md] + (16 * ks) * (2 * D);
+          const v4s16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16*)(
+              (__attribute__((address_space(3))) char*)p0));
+          const v4s16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16*)(
+              (__attribute__((address_space(3))) char*)(p0 + 4 * (2 * D))));
+          vf[md][ks] = __builtin_bit_cast(bf16x8, v8s16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        }
+    } else {
+      const __bf16* vbuf = vlds[stage(j)] + vrow_base;
+      for (int ks = 0; ks < 4; ++ks)
+        for (int md = 0; md < MD; ++md)
+          vf[md][ks] = *reinterpret_cast<const bf16x8*>(vbuf + md * 32 * T::VS + ((ks ^ md) & 3) * 16);
+    }
     __builtin_amdgcn_sched_barrier(0);
     for (int ks = 0; ks < 4; ++ks)
       for (int md = 0; md < MD; ++md) oacc[md] = mfma32(vf[md][ks], pb[ks], oacc[md]);
@@ -582,7 +735,32 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     l_part = sum;
   };
 
-  if (tile_lo <= tile_hi) {
+  if (T::DMA && tile_lo <= tile_hi) {
+    // three-stage ring: tile j + 2 is copied while tile j is computed; each
+    // wave waits for its own copies of tile j (those of tile j + 1 may stay in
+    // flight), then the barrier publishes the tile and frees stage j + 2,
+    // which every wave finished reading in the previous iteration
+    const int lo = tile_lo, hi = tile_hi;
+    stage_fetch(lo, page_of(lo));
+    load_q();
+    wait_vmcnt<0>();
+    if (lo + 1 <= hi) stage_fetch(lo + 1, page_of(lo + 1));
+    if (lo + 2 <= hi) id_next = page_of(lo + 2);
+    for (int j = lo; j <= hi; ++j) {
+      if (j + 1 <= hi) wait_vmcnt<kDmaOps<D>>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (j + 2 <= hi) {
+        stage_fetch(j + 2, id_next);
+        if (j + 3 <= hi) id_next = page_of(j + 3);
+      }
+      if (wave_tile(j)) {
+        gemm_s(j);
+        softmax(j);
+        gemm_pv(j);
+      }
+    }
+  } else if (tile_lo <= tile_hi) {
     const int lo = tile_lo, hi = tile_hi;
     stage_fetch(lo, page_of(lo));
     if (lo + 1 <= hi) id_next = page_of(lo + 1);

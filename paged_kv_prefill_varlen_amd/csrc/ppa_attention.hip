@@ -161,6 +161,8 @@ __device__ __forceinline__ float pair_sum(float x) {
   return a;
 }
 
+__constant__ int32_t kZeroPageId = 0;
+
 // ---- MXFP4 output (OCP Microscaling FP4) -------------------------------------
 // Elements are encoded by gfx950's scaled FP4 conversion
 // (v_cvt_scalef32_pk_fp4_f32: two fp32 values -> two E2M1 codes in one byte
@@ -555,11 +557,12 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
 
   bf16x8 qf[KSTEPS];   // B operand of S^T = K Q^T
   auto load_q = [&]() {
-    const uint16_t* qrow = a.q + static_cast<int64_t>(q0 + t0 + tok) * a.q_tok +
-                           static_cast<int64_t>(h0 + hd) * a.q_head;
+    // invalid rows load a valid row (the item's first) and are zeroed
+    const uint16_t* qrow = a.q + static_cast<int64_t>(q0 + t0 + (rvalid ? tok : 0)) * a.q_tok +
+                           static_cast<int64_t>(h0 + (rvalid ? hd : 0)) * a.q_head;
     for (int s = 0; s < KSTEPS; ++s) {
-      u32x4 x = u32x4{0, 0, 0, 0};
-      if (rvalid) x = *reinterpret_cast<const u32x4*>(qrow + s * 16 + half * 8);
+      u32x4 x = *reinterpret_cast<const u32x4*>(qrow + s * 16 + half * 8);
+      if (!rvalid) x = u32x4{0, 0, 0, 0};
       if (negate_q) x ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
       qf[s] = __builtin_bit_cast(bf16x8, x);
     }
@@ -619,6 +622,21 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     return wave_active && j * kBK <= wkey_hi && j * kBK + kBK - 1 >= wkey_lo;
   };
   auto page_of = [&](int j) { return UPAGE ? page_id_uniform(pt, uniform(j * kBK + 8 * wave)) : 0; };
+  // the same without branches (an empty table reads a constant zero), so
+  // that several lookups share one scalar round trip
+  auto page_of_nb = [&](int j) {
+    if (!UPAGE) return 0;
+    const int token = uniform(j * kBK + 8 * wave);
+    const bool empty = pt.cols <= 0;
+    int col = token >> pt.page_shift;
+    const int last = empty ? 0 : pt.cols - 1;
+    col = col < last ? col : last;
+    const __attribute__((address_space(4))) int32_t* row =
+        (const __attribute__((address_space(4))) int32_t*)(empty ? &kZeroPageId : pt.row);
+    int id = row[col];
+    id = id < 0 ? 0 : id;
+    return id < pt.num_pages ? id : pt.num_pages - 1;
+  };
   // copy the wave's 8 keys of tile j into registers; `id` is their page id
   // LDS stage of tile j
   auto stage = [&](int j) { return T::DMA ? (j - tile_lo) % 3 : (j - tile_lo) & 1; };
@@ -741,11 +759,14 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     // flight), then the barrier publishes the tile and frees stage j + 2,
     // which every wave finished reading in the previous iteration
     const int lo = tile_lo, hi = tile_hi;
-    stage_fetch(lo, page_of(lo));
+    // page ids of the first three tiles in one round trip; Q, then the first
+    // two tiles, without waiting in between
+    const int id0 = page_of_nb(lo);
+    const int id1 = page_of_nb(lo + 1 <= hi ? lo + 1 : hi);
+    id_next = page_of_nb(lo + 2 <= hi ? lo + 2 : hi);
     load_q();
-    wait_vmcnt<0>();
-    if (lo + 1 <= hi) stage_fetch(lo + 1, page_of(lo + 1));
-    if (lo + 2 <= hi) id_next = page_of(lo + 2);
+    stage_fetch(lo, id0);
+    if (lo + 1 <= hi) stage_fetch(lo + 1, id1);
     for (int j = lo; j <= hi; ++j) {
       if (j + 1 <= hi) wait_vmcnt<kDmaOps<D>>();
       else wait_vmcnt<0>();

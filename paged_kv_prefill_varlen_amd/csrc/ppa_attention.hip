@@ -509,12 +509,15 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   const int hk = (rest / a.n_hg) % a.num_kv_heads;
   const int hg = rest % a.n_hg;
 
-  int q1 = a.cu_q[b + 1];
-  int q0 = a.cu_q[b];
+  // request metadata through the constant address space: scalar loads, one
+  // round trip for all three (the kernel never writes these arrays)
+  typedef const __attribute__((address_space(4))) int32_t cint32;
+  int q1 = ((cint32*)(a.cu_q))[b + 1];
+  int q0 = ((cint32*)(a.cu_q))[b];
+  int kv_len = ((cint32*)(a.seq_lens))[b];
   q1 = q1 < a.num_tokens ? q1 : a.num_tokens;
   q0 = q0 < 0 ? 0 : (q0 < q1 ? q0 : q1);
   const int q_len = q1 - q0;
-  int kv_len = a.seq_lens[b];
   kv_len = kv_len < 0 ? 0 : kv_len;
   const int t0 = qt * a.tq;
   if (t0 >= q_len) return;
@@ -571,6 +574,8 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   // (below), and both are waited for together, so that no later compiler
   // wait for Q covers the prefetched tiles
   if constexpr (!T::DMA) load_q();
+  // the row's sink logit, read now so that the epilogue does not wait for it
+  const float sink = a.sinks ? a.sinks[h0 + (rvalid ? hd : 0)] : 0.f;
 
   f32x16 oacc[MD];
   for (int md = 0; md < MD; ++md) oacc[md] = f32x16{};
@@ -826,7 +831,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     if (half == 0) a.lse_part[prow] = l > 0.f ? mb * kLn2 + __builtin_logf(l) : kNegInf;
     return;
   }
-  if (a.sinks) l += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - mb);
+  if (a.sinks) l += __builtin_amdgcn_exp2f(sink * kLog2e - mb);
   if (a.lse != nullptr && half == 0) a.lse[trow * a.lse_tok + static_cast<int64_t>(h) * a.lse_head] = mb * kLn2 + __builtin_logf(l);
   const float inv = bmm2 / l;
   if (a.out_mx != 0) {

@@ -67,7 +67,9 @@ __device__ __forceinline__ void request_table(PageTable& pt, int b, const int32_
                                               int64_t bt_row_stride, int32_t bt_cols, const int32_t* kv_indptr,
                                               const int32_t* kv_indices, int64_t indices_len) {
   if (kv_indptr != nullptr) {
-    int64_t s0 = kv_indptr[b], s1 = kv_indptr[b + 1];
+    // scalar loads (constant address space): the kernel never writes the table
+    typedef const __attribute__((address_space(4))) int32_t cint32;
+    int64_t s0 = ((cint32*)(kv_indptr))[b], s1 = ((cint32*)(kv_indptr))[b + 1];
     s0 = s0 < 0 ? 0 : (s0 > indices_len ? indices_len : s0);
     s1 = s1 < s0 ? s0 : (s1 > indices_len ? indices_len : s1);
     pt.row = kv_indices + s0;

@@ -221,7 +221,7 @@ struct Tile {
   static constexpr int V_DPT = D / 32;          // dims per lane (32 dim groups)
   static constexpr int V_KEY_BYTES = V_DPT * EB;   // raw bytes per key per lane
   static constexpr bool DMA = !FP8;             // bf16: pages -> LDS directly
-  static constexpr int STAGES = DMA ? 3 : 2;     // LDS ring depth
+  static constexpr int STAGES = DMA ? 4 : 2;     // LDS ring depth
   static constexpr int K_DW = DMA ? 1 : K_LANE_BYTES / 4;
   static constexpr int V_DW = DMA ? 1 : (4 * V_KEY_BYTES + 3) / 4;
   static constexpr int KS = DMA ? D : D + 8;
@@ -644,7 +644,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   };
   // copy the wave's 8 keys of tile j into registers; `id` is their page id
   // LDS stage of tile j
-  auto stage = [&](int j) { return T::DMA ? (j - tile_lo) % 3 : (j - tile_lo) & 1; };
+  auto stage = [&](int j) { return T::DMA ? (j - tile_lo) & 3 : (j - tile_lo) & 1; };
   auto stage_fetch = [&](int j, int id) {
     const int kb = j * kBK + 8 * wave;
     const bool fast = UPAGE && j * kBK + kBK <= kv_len;
@@ -759,31 +759,36 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   };
 
   if (T::DMA && tile_lo <= tile_hi) {
-    // three-stage ring: tile j + 2 is copied while tile j is computed; each
-    // wave waits for its own copies of tile j (those of tile j + 1 may stay in
-    // flight), then the barrier publishes the tile and frees stage j + 2,
-    // which every wave finished reading in the previous iteration
+    // four-stage ring, two tiles per barrier: each wave waits for its copies
+    // of tiles j and j + 1, the barrier publishes them and frees the stages
+    // of tiles j - 2 and j - 1 (read before it), which receive j + 2, j + 3
     const int lo = tile_lo, hi = tile_hi;
-    // page ids of the first three tiles in one round trip; Q, then the first
-    // two tiles, without waiting in between
+    auto clampt = [&](int j) { return j <= hi ? j : hi; };
     const int id0 = page_of_nb(lo);
-    const int id1 = page_of_nb(lo + 1 <= hi ? lo + 1 : hi);
-    id_next = page_of_nb(lo + 2 <= hi ? lo + 2 : hi);
+    const int id1 = page_of_nb(clampt(lo + 1));
+    int idn0 = page_of_nb(clampt(lo + 2));
+    int idn1 = page_of_nb(clampt(lo + 3));
     load_q();
     stage_fetch(lo, id0);
     if (lo + 1 <= hi) stage_fetch(lo + 1, id1);
-    for (int j = lo; j <= hi; ++j) {
-      if (j + 1 <= hi) wait_vmcnt<kDmaOps<D>>();
-      else wait_vmcnt<0>();
+    for (int j = lo; j <= hi; j += 2) {
+      wait_vmcnt<0>();
       __syncthreads();
-      if (j + 2 <= hi) {
-        stage_fetch(j + 2, id_next);
-        if (j + 3 <= hi) id_next = page_of(j + 3);
+      if (j + 2 <= hi) stage_fetch(j + 2, idn0);
+      if (j + 3 <= hi) stage_fetch(j + 3, idn1);
+      if (j + 4 <= hi) {
+        idn0 = page_of_nb(j + 4);
+        idn1 = page_of_nb(clampt(j + 5));
       }
       if (wave_tile(j)) {
         gemm_s(j);
         softmax(j);
         gemm_pv(j);
+      }
+      if (j + 1 <= hi && wave_tile(j + 1)) {
+        gemm_s(j + 1);
+        softmax(j + 1);
+        gemm_pv(j + 1);
       }
     }
   } else if (tile_lo <= tile_hi) {

@@ -201,7 +201,8 @@ __device__ __forceinline__ uint32_t mx_pack4(float y0, float y1, float y2, float
 // bf16 cache: K and V tiles are copied from the pages into LDS without
 // passing through registers (fetch_kv_lds), in natural [key][dim] layout with
 // unpadded rows whose 16-byte chunks are XOR swizzled by key (kswz, vswz), in
-// a three-stage ring.  The PV operand, V^T, is read with LDS transpose loads.
+// a four-stage ring consumed two tiles per barrier.  The PV operand, V^T, is
+// read with LDS transpose loads.
 // fp8 cache: staged through registers (widened to bf16 once per workgroup);
 // K in natural layout with the row stride padded by 16 bytes, so the S
 // operand reads, 16 different rows per 16 lanes, hit distinct banks; V as 4
@@ -293,10 +294,6 @@ __device__ __forceinline__ void lds_copy16(uint32_t lds_base, const uint8_t* sba
                "s"(lds_base) : "memory", "m0");
 }
 #pragma clang diagnostic pop
-
-// Copies issued per wave per tile (K and V): the vmcnt step of the ring.
-template <int D>
-constexpr int kDmaOps = 2 * (8 * D * 2 / 1024);
 
 // The wave's keys [kb, kb + 8) of K and V into the tile's LDS stage.  Fast
 // path (`id` is their page, the tile is not the last of the request): 32-bit

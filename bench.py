@@ -75,6 +75,34 @@ def algorithmic_bytes(case, out_elem_bytes: float = 2.0) -> int:
     return int(tokens * Hq * D * (2 + out_elem_bytes)) + kv_reach * Hkv * D * eb * 2
 
 
+def executed_flops(case, rows_per_workgroup: int = 256, kbk: int = 64, wave_rows: int = 32) -> float:
+    """FLOPs of the MFMA work the kernel issues: every 32-row x 64-key
+    wave-tile it does not skip (masked parts of diagonal and window tiles
+    included), 4 * 32 * 64 * D each.  A count that follows the kernel's own
+    tile-range and skip rules, for reporting executed beside causal FLOPs."""
+    D, hq, hkv = case["head_dim"], case["num_qo_heads"], case["num_kv_heads"]
+    G = hq // hkv
+    gw = min(G, 16)
+    n_hg = (G + gw - 1) // gw
+    tq = rows_per_workgroup // gw
+    W = case["window_left"]
+    tiles = 0
+    for q_len, kv_len in zip(case["q_lens"], case["kv_lens"]):
+        prefix = kv_len - q_len
+        for t0 in range(0, q_len, tq):
+            ntok = min(tq, q_len - t0)
+            for w in range(rows_per_workgroup // wave_rows):
+                first = (w * wave_rows) // gw
+                if first >= ntok:
+                    continue
+                last = min((w * wave_rows + wave_rows - 1) // gw, ntok - 1)
+                khi = min(prefix + t0 + last, kv_len - 1)
+                klo = max(prefix + t0 + first - W, 0) if W >= 0 else 0
+                if khi >= klo:
+                    tiles += khi // kbk - klo // kbk + 1
+    return float(tiles) * hkv * n_hg * 4.0 * wave_rows * kbk * D
+
+
 def cpu_baseline(case, budget_s: float = 12.0):
     """Time the CPU oracle (as it stands) on whole passes over the same batch,
     repeated until about budget_s of work; report causal TFLOP/s."""
@@ -96,39 +124,86 @@ def cpu_baseline(case, budget_s: float = 12.0):
     for info in threadpool_info():
         if info.get("user_api") == "blas":
             threads = max(threads, int(info.get("num_threads", 0)))
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(flops / t_total / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads or len(os.sched_getaffinity(0)),
+        "host_cores": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": (f"float64 NumPy oracle, {passes} full pass(es) over the same batch "
                    f"({sum(case['q_lens'])} query tokens each), {t_total:.1f} s"),
     }
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the HIP sources and headers: ties stored counter readings
-    to the kernel they were taken on."""
+def _elf_sections(b: bytes, names) -> dict:
+    """Named sections of a little-endian ELF64 image."""
+    import struct
+    shoff, = struct.unpack_from("<Q", b, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", b, 0x3A)
+
+    def header(i):
+        return struct.unpack_from("<IIQQQQ", b, shoff + i * shentsize)
+
+    strtab = header(shstrndx)[4]
+    out = {}
+    for i in range(shnum):
+        name, _, _, _, off, size = header(i)
+        n = b[strtab + name: b.index(b"\0", strtab + name)].decode()
+        if n in names:
+            out[n] = b[off: off + size]
+    return out
+
+
+def kernel_code_digest(lib_path: str) -> str:
+    """sha256 over the gfx950 machine code (.text) and kernel descriptors
+    (.rodata) inside the library's offload bundle: ties stored counter
+    readings to the kernels they were taken on.  Host-only changes keep it
+    (the per-file id the compiler embeds lives in other sections)."""
     import hashlib
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "paged_kv_prefill_varlen_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode())
-                h.update(f.read())
+    import struct
+    with open(lib_path, "rb") as f:
+        b = f.read()
+    bundle = _elf_sections(b, {".hip_fatbin"}).get(".hip_fatbin", b"")
+    if bundle[:24] != b"__CLANG_OFFLOAD_BUNDLE__":
+        return ""
+    n, = struct.unpack_from("<Q", bundle, 24)
+    pos, h = 32, hashlib.sha256()
+    for _ in range(n):
+        off, size, tlen = struct.unpack_from("<QQQ", bundle, pos)
+        triple = bundle[pos + 24: pos + 24 + tlen].decode()
+        pos += 24 + tlen
+        if triple.endswith("gfx950"):
+            secs = _elf_sections(bundle[off: off + size], {".text", ".rodata"})
+            for k in sorted(secs):
+                h.update(k.encode())
+                h.update(secs[k])
     return h.hexdigest()
+
+
+def _library_path() -> str:
+    import paged_kv_prefill_varlen_amd as ppa
+    return ppa.library_path()
 
 
 def stored_traffic(config: str):
     """HBM bytes per launch from the committed counter summary for this
-    workload, or None when it is missing or was taken on other kernel sources."""
+    workload, or None when it is missing or was taken on other kernels."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{config}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_source_sha256") != kernel_source_digest():
+    if d.get("kernel_code_sha256") != kernel_code_digest(_library_path()):
         return None
     return d.get("traffic_bytes")
 
@@ -184,7 +259,7 @@ def traffic_summary(config: str, dirs) -> None:
         "read_bytes": int(rd),
         "write_bytes": int(wr),
         "traffic_bytes": int(rd + wr),
-        "kernel_source_sha256": kernel_source_digest(),
+        "kernel_code_sha256": kernel_code_digest(_library_path()),
         "commands": [
             "cd /tmp && export TMPDIR=/tmp",
             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch dir> -o run -- python3 bench.py "
@@ -274,7 +349,10 @@ def main():
     ap.add_argument("--config", default="chunked", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--kv-splits", type=int, default=0, help="split-KV chunks per work item (0: none)")
+    ap.add_argument("--kv-splits", default="auto",
+                    help="split-KV chunks per work item (0: none; auto: the library's planner, the default)")
+    ap.add_argument("--cold-iters", type=int, default=10,
+                    help="extra launches, each after writing a 512 MB buffer (cold caches); 0 to skip")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "mxfp4"],
                     help="output: bf16, or MXFP4 codes + E8M0 block scales")
     ap.add_argument("--o-sf-vec-size", type=int, default=32, choices=[16, 32])
@@ -322,13 +400,23 @@ def main():
         out = torch.empty_like(q)
     # zeroed scheduler workspace: persistent workgroups pull balanced work
     # (larger with split-KV: it also holds the partial states)
+    # "auto": the library's planner picks the split count for this shape and
+    # device, within a workspace sized for up to 256 splits (at most 256 MiB)
+    auto = args.kv_splits == "auto"
+    splits = 256 if auto else int(args.kv_splits)
     p = ppa.make_params(q, kv, None, bt, sl, case["max_q_len"], case["max_kv_len"], case["bmm1_scale"],
                         case["bmm2_scale"], case["batch_size"], cuq, cukv, case["window_left"], out,
-                        case["kv_layout"], sinks, kv_splits=args.kv_splits)
-    workspace = torch.zeros(ppa.ppa_workspace_bytes(p), dtype=torch.uint8, device=dev)
+                        case["kv_layout"], sinks, kv_splits=splits)
+    ws_bytes = ppa.ppa_workspace_bytes(p)
+    if auto:
+        ws_bytes = max(ppa.WORKSPACE_BYTES, min(ws_bytes, 256 << 20))
+    workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     p = ppa.make_params(q, kv, workspace, bt, sl, case["max_q_len"], case["max_kv_len"], case["bmm1_scale"],
                         case["bmm2_scale"], case["batch_size"], cuq, cukv, case["window_left"], out,
-                        case["kv_layout"], sinks, kv_splits=args.kv_splits)
+                        case["kv_layout"], sinks, kv_splits=0 if auto else splits)
+    if auto:
+        p.kv_splits = ppa.ppa_plan_kv_splits(p)
+    args.kv_splits = int(p.kv_splits)
     st, msg = ppa.ppa_validate_metadata_host(p, case["cum_seq_lens_q"], case["cum_seq_lens_kv"],
                                              case["seq_lens"], case["block_tables"])
     if st != 0:
@@ -353,17 +441,40 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize(dev)
     total_ms = t_begin.elapsed_time(t_end)
-    launch_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    launch_times = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    launch_ms = float(np.mean(launch_times))
     ms_per_step = total_ms / args.steps
+    # cold cache: a 512 MB buffer is written between launches (evicting L2
+    # and the Infinity Cache); only the launch itself is timed
+    cold_ms = None
+    if args.cold_iters > 0:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for i in range(args.cold_iters):
+            scratch.fill_(i & 0xFF)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            ppa.ppa_paged_prefill_attention(p, handle)
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            cold.append(e0.elapsed_time(e1))
+        cold_ms = float(np.median(cold))
+        del scratch
 
     flops = 4.0 * case["head_dim"] * case["num_qo_heads"] * causal_pairs(case)
     tokens = sum(case["q_lens"])
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     kernel_tflops = flops / (launch_ms * 1e-3) / 1e12
     fp8 = case["kv_dtype"] != "bf16"
-    hbm = args.config == "decode"
     alg_bytes = algorithmic_bytes(case, 2.0 if args.out_dtype == "bf16" else 0.5 + 1.0 / args.o_sf_vec_size)
-    if hbm:   # decode streams K/V once: report bandwidth against the HBM roofline
+    # the bound follows the arithmetic intensity: below the ridge
+    # (peak FLOP/s over HBM bytes/s) the compulsory bytes bound the kernel
+    ai = flops / alg_bytes
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    hbm = args.config == "decode" or ai < ridge
+    attainable = min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1e3)
+    if hbm:   # the compulsory bytes bound it: report bandwidth against HBM
         kernel_gbs = alg_bytes / (launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(kernel_gbs / PEAK_HBM_GBS, 4), "traffic": None}
@@ -372,6 +483,12 @@ def main():
                 "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": stored_traffic(args.config) if args.out_dtype == "bf16" else None}
     roof.update({"algorithmic_bytes": alg_bytes, "kernel_ms": round(launch_ms, 5),
+                 "kernel_ms_median": round(float(np.median(launch_times)), 5),
+                 "cold_kernel_ms_median": None if cold_ms is None else round(cold_ms, 5),
+                 "flop_per_byte": round(ai, 1),
+                 "attainable_tflops": round(attainable, 1),
+                 "frac_attainable": round(kernel_tflops / attainable, 4),
+                 "executed_tflops": round(executed_flops(case) / (launch_ms * 1e-3) / 1e12, 3),
                  "kernel": "paged_prefill_persistent<%d,%s>%s" % (case["head_dim"], "fp8" if fp8 else "bf16",
                                                                   " + merge" if args.kv_splits > 1 else "")})
     line = {
@@ -389,7 +506,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config,
                    "query_tokens": tokens, "causal_gflop": round(flops / 1e9, 3),
-                   "kv_splits": args.kv_splits, "out": args.out_dtype if args.out_dtype == "bf16"
+                   "kv_splits": args.kv_splits, "kv_splits_from": "planner" if auto else "argument", "out": args.out_dtype if args.out_dtype == "bf16"
                    else f"mxfp4/{args.o_sf_vec_size}", "parallelism": "none (one GPU)"},
         "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),

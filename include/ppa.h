@@ -365,6 +365,34 @@ int32_t ppa_validate_page_table_csr_host(const ppa_params* p, const int32_t* seq
 size_t ppa_workspace_bytes(const ppa_params* p);
 
 /*
+ * Split-KV planning (host only).  The TensorRT-LLM prepare() dissection page,
+ * in its FlashInfer backend part, routes the decode segment to a split-K
+ * kernel and the prefill segment to the paged-prefill one; here one call
+ * serves both, and this chooses kv_splits for it.
+ *
+ * ppa_plan_kv_splits_model: the cost model, a pure function.  work_items =
+ * (query tiles) x batch x kv heads x head groups of the call; resident = the
+ * workgroups the device holds at once; key_tiles = 64-key tiles of the
+ * longest work item.  With work_items >= resident there is no idle slot and
+ * the answer is 1.  Otherwise it returns the S in [1, max_splits] (S <=
+ * key_tiles / 4, so a chunk keeps at least four tiles) that minimises
+ *   ceil(work_items * S / resident) * (ceil(key_tiles / S) + 3) + S / 2,
+ * i.e. rounds of workgroups times the tiles of a chunk plus a per-chunk
+ * start-up cost, plus the merge's cost per split; the smallest S on ties.
+ * Returns 1 for non-positive inputs.
+ *
+ * ppa_plan_kv_splits: the model applied to the call `p` on the current
+ * device (its compute-unit count times the occupancy of the kernel variant
+ * `p` selects).  The kv_splits field of `p` is ignored; only splits whose
+ * ppa_workspace_bytes fit p->workspace_bytes are considered (1 when
+ * p->workspace is NULL).  Returns the split count (>= 1), or a negative
+ * ppa_status if `p` fails ppa_validate_shapes or the device cannot be
+ * queried.  The caller then sets p->kv_splits to it.
+ */
+int32_t ppa_plan_kv_splits_model(int64_t work_items, int64_t resident, int64_t key_tiles, int32_t max_splits);
+int32_t ppa_plan_kv_splits(const ppa_params* p);
+
+/*
  * The batched paged prefill attention call.  Runs ppa_validate_shapes, then
  * enqueues the kernel on `stream` and returns without waiting.  No host
  * synchronisation, no allocation.  Metadata values are trusted to pass

@@ -199,6 +199,8 @@ def _load():
         "ppa_validate_page_table_csr_host": (c_int32, [P, c_void_p, c_void_p, c_void_p, c_void_p, c_char_p,
                                                        c_size_t]),
         "ppa_workspace_bytes": (c_size_t, [P]),
+        "ppa_plan_kv_splits_model": (c_int32, [c_int64, c_int64, c_int64, c_int32]),
+        "ppa_plan_kv_splits": (c_int32, [P]),
         "ppa_paged_prefill_attention": (c_int32, [P, c_void_p]),
         "ppa_gather_paged_kv": (c_int32, [P, c_int32, c_void_p, c_int64, c_void_p]),
         "ppa_merge_attention_states": (c_int32, [ctypes.POINTER(PpaMergeParams), c_void_p]),
@@ -298,6 +300,21 @@ def ppa_validate_page_table_csr_host(params: PpaParams, seq_lens, kv_indptr, kv_
 
 def ppa_workspace_bytes(params: Optional[PpaParams] = None) -> int:
     return int(_lib.ppa_workspace_bytes(None if params is None else ctypes.byref(params)))
+
+
+def ppa_plan_kv_splits_model(work_items: int, resident: int, key_tiles: int, max_splits: int) -> int:
+    """The split-count cost model (pure; see ppa.h)."""
+    return int(_lib.ppa_plan_kv_splits_model(int(work_items), int(resident), int(key_tiles), int(max_splits)))
+
+
+def ppa_plan_kv_splits(params: PpaParams) -> int:
+    """kv_splits the library picks for this call on the current device
+    (within params.workspace_bytes); raises PpaError on invalid params."""
+    st = int(_lib.ppa_plan_kv_splits(ctypes.byref(params)))
+    if st < 1:
+        _, msg = ppa_validate_shapes(params)
+        raise PpaError(st, msg or ppa_strerror(st))
+    return st
 
 
 # bytes of the optional scheduler workspace (the same for every call)
@@ -580,14 +597,15 @@ def batch_context_with_kv_cache(query: torch.Tensor, kv_cache, workspace_buffer:
                                 out_dtype=None, kv_layout: str = "HND", sinks=None,
                                 validate: bool = False, stream=None, kv_indptr=None, kv_indices=None,
                                 kv_last_page_len=None, lse: Optional[torch.Tensor] = None,
-                                kv_splits: int = 0, o_sf_scale: Optional[float] = None,
+                                kv_splits: Union[int, str] = 0, o_sf_scale: Optional[float] = None,
                                 o_sf_vec_size: Optional[int] = None):
     """Batched paged prefill attention; argument list of the API page
     (without the PDL option), plus the optional flat page table (kv_indptr /
     kv_indices / kv_last_page_len) in place of block_tables, an optional fp32
     ``lse`` [num_tokens, num_qo_heads] output (natural-log softmax
     denominators) and ``kv_splits`` (split-KV; needs a workspace of
-    ``ppa_workspace_bytes`` bytes).  The FP4 output of the API page is given
+    ``ppa_workspace_bytes`` bytes; ``"auto"``: the library's planner picks
+    it from the shapes, the device and the workspace size).  The FP4 output of the API page is given
     as OCP MXFP4: ``out_dtype="mxfp4"`` (or an ``MxFp4Output`` as ``out``)
     with ``o_sf_scale`` (default 1) and ``o_sf_vec_size`` (16 or 32, default
     32) returns an ``MxFp4Output``.  ``validate=True`` also runs the deep
@@ -602,9 +620,15 @@ def batch_context_with_kv_cache(query: torch.Tensor, kv_cache, workspace_buffer:
     if out is None:
         dt = query.dtype if out_dtype is None else out_dtype
         out = torch.empty(query.shape, dtype=dt, device=query.device)
+    auto = isinstance(kv_splits, str)
+    if auto and kv_splits != "auto":
+        raise ValueError(f"kv_splits {kv_splits!r}: an int or 'auto'")
     p = make_params(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_q_len, max_kv_len,
                     bmm1_scale, bmm2_scale, batch_size, cum_seq_lens_q, cum_seq_lens_kv, window_left,
-                    out, kv_layout, sinks, kv_indptr, kv_indices, kv_last_page_len, lse, kv_splits)
+                    out, kv_layout, sinks, kv_indptr, kv_indices, kv_last_page_len, lse, 0 if auto else kv_splits)
+    if auto:
+        with torch.cuda.device(query.device):
+            p.kv_splits = ppa_plan_kv_splits(p)
     if validate:
         st, msg = ppa_validate_metadata_host(p, cum_seq_lens_q, cum_seq_lens_kv, seq_lens, block_tables)
         if st == 0 and p.page_table_form == PPA_PAGE_TABLE_CSR:

@@ -1087,6 +1087,23 @@ hipError_t launch(const AttnArgs& a, int items, hipStream_t stream, bool upage) 
   return upage ? launch_variant<D, FP8, true>(a, items, stream) : launch_variant<D, FP8, false>(a, items, stream);
 }
 
+// Uniform-page staging (the 8 keys a wave copies lie in one page) needs pages
+// of >= 8 tokens whose byte extent fits the 32-bit in-page offsets.
+bool uniform_pages(const ppa_params* p, const CacheView& cv) {
+  const int eb = p->kv_dtype == PPA_DTYPE_FP8_E4M3FN ? 1 : 2;
+  auto extent = [&](int64_t head, int64_t tok) {
+    return (static_cast<int64_t>(p->page_size) * tok + static_cast<int64_t>(p->num_kv_heads) * head + p->head_dim) *
+           eb;
+  };
+  return p->page_size >= 8 && extent(cv.k_head, cv.k_tok) < (int64_t{1} << 31) &&
+         extent(cv.v_head, cv.v_tok) < (int64_t{1} << 31);
+}
+
+template <int D, bool FP8>
+int resident_for(bool upage) {
+  return upage ? resident_workgroups<D, FP8, true>() : resident_workgroups<D, FP8, false>();
+}
+
 }  // namespace
 }  // namespace ppa
 
@@ -1162,15 +1179,7 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
   hipError_t e;
   const bool fp8 = p->kv_dtype == PPA_DTYPE_FP8_E4M3FN;
   const int g = static_cast<int>(grid);
-  // uniform-page staging needs pages of >= 8 tokens whose byte extent fits
-  // the 32-bit in-page offsets
-  const int eb = fp8 ? 1 : 2;
-  auto extent = [&](const PagedPlane& pl) {
-    return (static_cast<int64_t>(p->page_size) * pl.tok_stride +
-            static_cast<int64_t>(p->num_kv_heads) * pl.head_stride + p->head_dim) * eb;
-  };
-  const bool upage = p->page_size >= 8 && extent(a.k) < (int64_t{1} << 31) &&
-                     extent(a.v) < (int64_t{1} << 31);
+  const bool upage = uniform_pages(p, cv);
   if (p->head_dim == 128)
     e = fp8 ? launch<128, true>(a, g, s, upage) : launch<128, false>(a, g, s, upage);
   else
@@ -1198,6 +1207,44 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
     e = launch_merge(m, p->head_dim, s);
   }
   return e == hipSuccess ? PPA_OK : PPA_ERR_HIP;
+}
+
+extern "C" int32_t ppa_plan_kv_splits(const ppa_params* p) {
+  if (p == nullptr) return PPA_ERR_NULL_POINTER;
+  ppa_params q = *p;
+  q.kv_splits = 0;
+  char msg[8];
+  const int32_t st = ppa_validate_shapes(&q, msg, sizeof msg);
+  if (st != PPA_OK) return st;
+  if (q.batch_size == 0 || q.max_q_len == 0 || q.num_tokens == 0 || q.workspace == nullptr) return 1;
+  // the largest split count whose partial state fits the caller's workspace
+  int32_t max_splits = 1;
+  for (int32_t s = 256; s > 1; --s) {
+    q.kv_splits = s;
+    if (ppa_workspace_bytes(&q) <= q.workspace_bytes) {
+      max_splits = s;
+      break;
+    }
+  }
+  CacheView cv;
+  resolve_cache(&q, &cv);
+  const bool upage = uniform_pages(&q, cv);
+  const bool fp8 = q.kv_dtype == PPA_DTYPE_FP8_E4M3FN;
+  const int resident = q.head_dim == 128 ? (fp8 ? resident_for<128, true>(upage) : resident_for<128, false>(upage))
+                                         : (fp8 ? resident_for<64, true>(upage) : resident_for<64, false>(upage));
+  if (resident <= 0) return PPA_ERR_HIP;
+  // work items as the launch counts them, and the key tiles of the longest
+  const int group = q.num_qo_heads / q.num_kv_heads;
+  const int gw = group < 16 ? group : 16;
+  const int tq = 256 / gw;
+  const int64_t items = static_cast<int64_t>((q.max_q_len + tq - 1) / tq) * q.batch_size * q.num_kv_heads *
+                        ((group + gw - 1) / gw);
+  int64_t keys = q.max_kv_len;
+  if (q.window_left >= 0) {
+    const int64_t span = static_cast<int64_t>(q.window_left) + (q.max_q_len < tq ? q.max_q_len : tq);
+    keys = span < keys ? span : keys;
+  }
+  return ppa_plan_kv_splits_model(items, resident, (keys + kBK - 1) / kBK, max_splits);
 }
 
 // ---- KV append: new tokens' K and V into their page slots -------------------

@@ -132,6 +132,24 @@ size_t ppa_workspace_bytes(const ppa_params* p) {
   return bytes;
 }
 
+int32_t ppa_plan_kv_splits_model(int64_t work_items, int64_t resident, int64_t key_tiles, int32_t max_splits) {
+  if (work_items <= 0 || resident <= 0 || key_tiles <= 0 || max_splits <= 1 || work_items >= resident) return 1;
+  int64_t top = key_tiles / 4;
+  if (top > max_splits) top = max_splits;
+  int32_t best = 1;
+  double best_cost = 0.0;
+  for (int64_t s = 1; s <= (top > 1 ? top : 1); ++s) {
+    const int64_t rounds = (work_items * s + resident - 1) / resident;
+    const int64_t chunk = (key_tiles + s - 1) / s;
+    const double cost = static_cast<double>(rounds) * static_cast<double>(chunk + 3) + 0.5 * static_cast<double>(s);
+    if (s == 1 || cost < best_cost) {
+      best_cost = cost;
+      best = static_cast<int32_t>(s);
+    }
+  }
+  return best;
+}
+
 int32_t ppa_validate_shapes(const ppa_params* p, char* msg, size_t msg_len) {
   if (msg != nullptr && msg_len > 0) msg[0] = '\0';
   if (p == nullptr) return fail(PPA_ERR_NULL_POINTER, msg, msg_len, "params is NULL");

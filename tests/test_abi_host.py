@@ -542,3 +542,52 @@ def test_append_validation():
     assert B.ppa_validate_append(p1, a)[0] == E["PPA_ERR_LAYOUT"]
     with pytest.raises(TypeError):
         B.make_append_params(k_new, v_new, slots.to(torch.int32))
+
+
+# --------------------------------------------------------------------------
+# the split-KV planner (host only)
+# --------------------------------------------------------------------------
+
+def _model_by_hand(items, resident, tiles, max_splits):
+    """The cost model as ppa.h states it, evaluated for every S."""
+    if min(items, resident, tiles) <= 0 or max_splits <= 1 or items >= resident:
+        return 1
+    best, best_cost = 1, None
+    for s in range(1, max(1, min(tiles // 4, max_splits)) + 1):
+        cost = -(-items * s // resident) * (-(-tiles // s) + 3) + 0.5 * s
+        if best_cost is None or cost < best_cost:
+            best, best_cost = s, cost
+    return best
+
+
+def test_plan_model_cases():
+    m = B.ppa_plan_kv_splits_model
+    # decode-shaped batch: 16 requests x 8 kv heads = 128 items on 256 CUs,
+    # 8192 keys = 128 tiles: two chunks fill the device (the measured best)
+    assert m(128, 256, 128, 256) == 2
+    # enough work items already: no split
+    assert m(256, 256, 4096, 256) == 1 and m(4096, 256, 32, 256) == 1
+    # too few tiles to give every chunk four, or no room for partial state
+    assert m(8, 256, 7, 256) == 1 and m(8, 256, 512, 1) == 1
+    # one request, 8 kv heads, 32K keys: many chunks, bounded by the workspace
+    assert m(8, 256, 512, 256) > 8 and m(8, 256, 512, 5) == 5
+    for bad in ((0, 256, 10, 8), (8, 0, 10, 8), (8, 256, 0, 8), (-1, 256, 10, 8)):
+        assert m(*bad) == 1
+
+
+def test_plan_model_matches_its_definition():
+    m = B.ppa_plan_kv_splits_model
+    for items in (1, 3, 8, 50, 100, 127, 128, 200, 255):
+        for resident in (64, 256, 512):
+            for tiles in (1, 4, 8, 9, 33, 128, 513):
+                for mx in (1, 2, 3, 16, 256):
+                    assert m(items, resident, tiles, mx) == _model_by_hand(items, resident, tiles, mx), \
+                        (items, resident, tiles, mx)
+
+
+def test_plan_without_workspace_or_with_bad_params():
+    c = _case()
+    assert B.ppa_plan_kv_splits(_params(c)) == 1     # no workspace: nowhere to put partial state
+    with pytest.raises(B.PpaError) as e:
+        B.ppa_plan_kv_splits(_params(c, head_dim=96))
+    assert e.value.status == ERR["PPA_ERR_HEAD_DIM"]

@@ -1,0 +1,57 @@
+"""Host-side figures that bench.py reports (no GPU): the executed-FLOP count
+of the kernel's wave-tiles, checked by brute force over every row's visible
+keys, and the algorithmic byte count's parts."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import bench
+from workloads import make_case, make_custom_case
+
+
+def _brute_tiles(case, rows_wg=256, kbk=64):
+    """Number of (wave, key tile) pairs that hold at least one key some row of
+    the wave may see, counted one row and one key at a time."""
+    G = case["num_qo_heads"] // case["num_kv_heads"]
+    gw = min(G, 16)
+    tq = rows_wg // gw
+    W = case["window_left"]
+    n = 0
+    for q_len, kv_len in zip(case["q_lens"], case["kv_lens"]):
+        prefix = kv_len - q_len
+        for t0 in range(0, q_len, tq):
+            ntok = min(tq, q_len - t0)
+            for w in range(rows_wg // 32):
+                tiles = set()
+                for r in range(w * 32, w * 32 + 32):
+                    tok = r // gw
+                    if tok >= ntok:
+                        continue
+                    pos = prefix + t0 + tok
+                    for k in range(kv_len):
+                        if k <= pos and (W < 0 or pos - k <= W):
+                            tiles.add(k // kbk)
+                n += len(tiles)
+    return n
+
+
+@pytest.mark.parametrize("spec", [
+    dict(num_qo_heads=8, num_kv_heads=2, q_lens=(70, 1, 33), prefix_lens=(5, 40, 0)),
+    dict(num_qo_heads=32, num_kv_heads=2, q_lens=(130, 17), prefix_lens=(0, 200), window_left=40),
+    dict(num_qo_heads=4, num_kv_heads=4, q_lens=(300, 0, 9), prefix_lens=(64, 10, 0), window_left=0),
+    dict(num_qo_heads=24, num_kv_heads=1, q_lens=(90,), prefix_lens=(7,)),
+])
+def test_executed_flops_matches_brute_force(spec):
+    case = make_custom_case(batch=len(spec["q_lens"]), head_dim=64, page_size=16, seed=3, **spec)
+    G = case["num_qo_heads"] // case["num_kv_heads"]
+    n_hg = -(-G // min(G, 16))
+    want = _brute_tiles(case) * case["num_kv_heads"] * n_hg * 4.0 * 32 * 64 * case["head_dim"]
+    assert bench.executed_flops(case) == want
+
+
+@pytest.mark.parametrize("name", ["tiny", "chunked", "swa_sinks"])
+def test_executed_at_least_causal(name):
+    case = make_case(name)
+    causal = 4.0 * case["head_dim"] * case["num_qo_heads"] * bench.causal_pairs(case)
+    assert bench.executed_flops(case) >= causal > 0

@@ -498,3 +498,37 @@ def test_decode_config(splits):
     mx, mean = assert_close(out, want, written, what=f"decode S={splits}")
     err = _lse_close(lse, want_lse, written, f"decode S={splits}")
     _say(f"  decode S={splits}: max {mx:.2e} mean {mean:.2e} lse {err:.2e}")
+
+
+def _planned(d, ws):
+    import paged_kv_prefill_varlen_amd as ppa
+    out = torch.empty_like(d["query"])
+    p = ppa.make_params(d["query"], d["kv_cache"], ws, d["block_tables"], d["seq_lens"], d["max_q_len"],
+                        d["max_kv_len"], d["bmm1_scale"], d["bmm2_scale"], d["batch_size"], d["cum_seq_lens_q"],
+                        d["cum_seq_lens_kv"], d["window_left"], out, d["kv_layout"], d["sinks"])
+    return ppa.ppa_plan_kv_splits(p)
+
+
+def test_planned_kv_splits():
+    """kv_splits="auto": the planner splits the decode-shaped batch (128 work
+    items for the device's resident workgroups) and the result is the oracle's
+    and bitwise the explicit call with the same count; prefill shapes, which
+    already fill the device, stay whole; a workspace with no room for partial
+    state gives no split."""
+    case = make_case("decode")
+    want, written = run_oracle(case)
+    d = to_device(case)
+    ws = split_workspace(d, 64)
+    s = _planned(d, ws)
+    _say(f"  planned kv_splits for decode: {s}")
+    assert 1 < s <= 64
+    auto = run_gpu(d, kv_splits="auto", ws=ws)
+    torch.cuda.synchronize()
+    assert_close(auto, want, written, what="decode auto")
+    explicit = run_gpu(d, kv_splits=s, ws=split_workspace(d, s))
+    torch.cuda.synchronize()
+    assert torch.equal(auto.view(torch.int16), explicit.view(torch.int16))
+    assert _planned(d, split_workspace(d, 1)) == 1
+    for name in ("chunked", "swa_sinks"):
+        dc = to_device(make_case(name))
+        assert _planned(dc, split_workspace(dc, 4)) == 1, name

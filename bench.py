@@ -263,9 +263,9 @@ def traffic_summary(config: str, dirs) -> None:
         "commands": [
             "cd /tmp && export TMPDIR=/tmp",
             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch dir> -o run -- python3 bench.py "
-            f"--steps 2 --warmup 1 --no-cpu --config {config}",
+            f"--steps 2 --warmup 1 --no-cpu --cold-iters 0 --config {config}",
             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write dir> -o run -- python3 bench.py "
-            f"--steps 2 --warmup 1 --no-cpu --config {config}",
+            f"--steps 2 --warmup 1 --no-cpu --cold-iters 0 --config {config}",
             "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <copy dirs> -o run -- "
             "python3 bench.py --copy-calibration",
             f"python3 bench.py --config {config} --traffic-summary <fetch dir> <write dir> <copy fetch dir> "

@@ -161,7 +161,6 @@ __device__ __forceinline__ float pair_sum(float x) {
   return a;
 }
 
-__constant__ int32_t kZeroPageId = 0;
 
 // ---- MXFP4 output (OCP Microscaling FP4) -------------------------------------
 // Elements are encoded by gfx950's scaled FP4 conversion
@@ -506,12 +505,18 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   const int hk = (rest / a.n_hg) % a.num_kv_heads;
   const int hg = rest % a.n_hg;
 
-  // request metadata through the constant address space: scalar loads, one
-  // round trip for all three (the kernel never writes these arrays)
+  // request metadata through the constant address space: scalar loads (the
+  // kernel never writes these arrays), with the request's page-table row
   typedef const __attribute__((address_space(4))) int32_t cint32;
   int q1 = ((cint32*)(a.cu_q))[b + 1];
   int q0 = ((cint32*)(a.cu_q))[b];
   int kv_len = ((cint32*)(a.seq_lens))[b];
+  PageTable pt;
+  request_table(pt, b, a.block_tables, a.bt_row_stride, a.bt_cols, a.kv_indptr, a.kv_indices, a.kv_indices_len);
+  // every one of them is taken here, so all loads go out together: otherwise
+  // the compiler sinks those used only after the early return below past
+  // it, and each costs a serial round trip
+  asm volatile("" : : "s"(q0), "s"(q1), "s"(kv_len), "s"(pt.row), "s"(pt.cols));
   q1 = q1 < a.num_tokens ? q1 : a.num_tokens;
   q0 = q0 < 0 ? 0 : (q0 < q1 ? q0 : q1);
   const int q_len = q1 - q0;
@@ -594,8 +599,6 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     tile_hi = first + ((split + 1) * n) / S - 1;
   }
 
-  PageTable pt;
-  request_table(pt, b, a.block_tables, a.bt_row_stride, a.bt_cols, a.kv_indptr, a.kv_indices, a.kv_indices_len);
   pt.num_pages = a.num_pages;
   pt.page_shift = a.page_shift;
   const int page_mask = (1 << a.page_shift) - 1;
@@ -624,8 +627,9 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     return wave_active && j * kBK <= wkey_hi && j * kBK + kBK - 1 >= wkey_lo;
   };
   auto page_of = [&](int j) { return UPAGE ? page_id_uniform(pt, uniform(j * kBK + 8 * wave)) : 0; };
-  // the same without branches (an empty table reads a constant zero), so
-  // that several lookups share one scalar round trip
+  // the same without branches, so that several lookups share one scalar
+  // round trip: an empty table reads cu_q[0] instead (any readable word
+  // will do: the id is clamped to a valid page before use)
   auto page_of_nb = [&](int j) {
     if (!UPAGE) return 0;
     const int token = uniform(j * kBK + 8 * wave);
@@ -634,7 +638,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     const int last = empty ? 0 : pt.cols - 1;
     col = col < last ? col : last;
     const __attribute__((address_space(4))) int32_t* row =
-        (const __attribute__((address_space(4))) int32_t*)(empty ? &kZeroPageId : pt.row);
+        (const __attribute__((address_space(4))) int32_t*)(empty ? a.cu_q : pt.row);
     int id = row[col];
     id = id < 0 ? 0 : id;
     return id < pt.num_pages ? id : pt.num_pages - 1;

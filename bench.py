@@ -103,6 +103,31 @@ def executed_flops(case, rows_per_workgroup: int = 256, kbk: int = 64, wave_rows
     return float(tiles) * hkv * n_hg * 4.0 * wave_rows * kbk * D
 
 
+def device_info(torch, dev) -> dict:
+    """What the device reports, to re-derive the roofline constants: compute
+    units (torch's device properties), the highest shader clock in the
+    driver's DPM table (sysfs, when readable), and the dense bf16 MFMA peak
+    they imply at 4096 FLOP per CU per clock (the published 2516.6 TFLOP/s is
+    256 CUs x 4096 x 2.4 GHz).  `peak` in the roofline stays the published
+    figure."""
+    import glob
+    import re
+    props = torch.cuda.get_device_properties(dev)
+    cus = int(props.multi_processor_count)
+    sclk = None
+    for path in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
+        try:
+            with open(path) as f:
+                mhz = [int(m) for m in re.findall(r"(\d+)\s*[Mm][Hh]z", f.read())]
+        except OSError:
+            continue
+        if mhz:
+            sclk = max(sclk or 0, max(mhz))
+    return {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": cus,
+            "max_sclk_mhz": sclk,
+            "bf16_peak_tflops_derived": None if sclk is None else round(cus * 4096 * sclk * 1e6 / 1e12, 1)}
+
+
 def cpu_baseline(case, budget_s: float = 12.0):
     """Time the CPU oracle (as it stands) on whole passes over the same batch,
     repeated until about budget_s of work; report causal TFLOP/s."""
@@ -512,6 +537,7 @@ def main():
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": roof,
         "cpu_baseline": None,
+        "device": device_info(torch, dev),
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)

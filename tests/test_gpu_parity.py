@@ -532,3 +532,23 @@ def test_planned_kv_splits():
     for name in ("chunked", "swa_sinks"):
         dc = to_device(make_case(name))
         assert _planned(dc, split_workspace(dc, 4)) == 1, name
+
+
+@pytest.mark.parametrize("name", ["long_prefix", "window_many_tiles", "nan_poison", "fp8_d128",
+                                  "fp8_d64_nhd_window_sinks", "single_token", "bounds_loose"])
+def test_edge_case_planned_splits(name):
+    """kv_splits="auto" on the edge cases: these small batches leave most of
+    the device idle, so the planner splits wherever the keys allow it; the
+    result must match the oracle whatever count it picks."""
+    case = make_custom_case(name=name, batch=len(EDGE[name]["q_lens"]), seed=zlib.crc32(name.encode()) % 10000,
+                            **EDGE[name])
+    want, written = run_oracle(case)
+    d = to_device(case)
+    ws = split_workspace(d, 64)
+    s = _planned(d, ws)
+    _say("edge planned", name, "kv_splits", s)
+    out = run_gpu(d, kv_splits="auto", ws=ws)
+    torch.cuda.synchronize()
+    assert guard_rows_untouched(out, written), "rows outside the requests were written"
+    mx, mean = assert_close(out, want, written, fp8=case["kv_dtype"] != "bf16", what=f"{name} auto S={s}")
+    _say(f"  max {mx:.2e} mean {mean:.2e}")

@@ -189,11 +189,12 @@ def _elf_sections(b: bytes, names) -> dict:
     return out
 
 
-def kernel_code_digest(lib_path: str) -> str:
-    """sha256 over the gfx950 machine code (.text) and kernel descriptors
-    (.rodata) inside the library's offload bundle: ties stored counter
-    readings to the kernels they were taken on.  Host-only changes keep it
-    (the per-file id the compiler embeds lives in other sections)."""
+def kernel_code_digest(lib_path: str, kernel: str) -> str:
+    """sha256 over the gfx950 machine code and kernel descriptor of one
+    kernel of the library (the function symbol containing `kernel` and its
+    `.kd` descriptor, found through the code object's symbol table): ties
+    stored counter readings to the kernel they were taken on.  Host-only
+    changes and changes to other kernels keep it."""
     import hashlib
     import struct
     with open(lib_path, "rb") as f:
@@ -202,17 +203,39 @@ def kernel_code_digest(lib_path: str) -> str:
     if bundle[:24] != b"__CLANG_OFFLOAD_BUNDLE__":
         return ""
     n, = struct.unpack_from("<Q", bundle, 24)
-    pos, h = 32, hashlib.sha256()
+    pos = 32
     for _ in range(n):
         off, size, tlen = struct.unpack_from("<QQQ", bundle, pos)
         triple = bundle[pos + 24: pos + 24 + tlen].decode()
         pos += 24 + tlen
-        if triple.endswith("gfx950"):
-            secs = _elf_sections(bundle[off: off + size], {".text", ".rodata"})
-            for k in sorted(secs):
-                h.update(k.encode())
-                h.update(secs[k])
-    return h.hexdigest()
+        if not triple.endswith("gfx950"):
+            continue
+        obj = bundle[off: off + size]
+        shoff, = struct.unpack_from("<Q", obj, 0x28)
+        shentsize, shnum, shstrndx = struct.unpack_from("<HHH", obj, 0x3A)
+        hdrs = [struct.unpack_from("<IIQQQQIIQQ", obj, shoff + i * shentsize) for i in range(shnum)]
+        names = [obj[hdrs[shstrndx][4] + h[0]: obj.index(b"\0", hdrs[shstrndx][4] + h[0])].decode() for h in hdrs]
+        symtab = hdrs[names.index(".symtab")]
+        strtab = hdrs[symtab[6]]   # sh_link
+        h = hashlib.sha256()
+        found = 0
+        for i in range(symtab[5] // 24):
+            st_name, _, _, shndx, value, sz = struct.unpack_from("<IBBHQQ", obj, symtab[4] + 24 * i)
+            name = obj[strtab[4] + st_name: obj.index(b"\0", strtab[4] + st_name)].decode()
+            if kernel not in name or shndx == 0 or shndx >= len(hdrs) or sz == 0:
+                continue
+            sec = hdrs[shndx]   # symbol value is an address inside this section
+            start = sec[4] + value - sec[3]
+            h.update(name.encode())
+            h.update(obj[start: start + sz])
+            found += 1
+        return h.hexdigest() if found else ""
+    return ""
+
+
+# the kernel the stored counters of a bf16 workload were taken on
+def _kernel_symbol(case) -> str:
+    return "paged_prefill_persistentILi%dELb%dELb1E" % (case["head_dim"], 1 if case["kv_dtype"] != "bf16" else 0)
 
 
 def _library_path() -> str:
@@ -228,7 +251,7 @@ def stored_traffic(config: str):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_code_sha256") != kernel_code_digest(_library_path()):
+    if d.get("kernel_code_sha256") != kernel_code_digest(_library_path(), d.get("kernel_symbol", "?")):
         return None
     return d.get("traffic_bytes")
 
@@ -262,6 +285,8 @@ def traffic_summary(config: str, dirs) -> None:
                  if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
         return v[-last:] if last else v
 
+    from workloads import make_case
+    sym = _kernel_symbol(make_case(config))
     kern = lambda n: "paged_prefill" in n          # noqa: E731
     add = lambda n: "elementwise" in n             # noqa: E731
     fetch = values(dirs[0], "FETCH_SIZE", kern)
@@ -284,7 +309,8 @@ def traffic_summary(config: str, dirs) -> None:
         "read_bytes": int(rd),
         "write_bytes": int(wr),
         "traffic_bytes": int(rd + wr),
-        "kernel_code_sha256": kernel_code_digest(_library_path()),
+        "kernel_symbol": sym,
+        "kernel_code_sha256": kernel_code_digest(_library_path(), sym),
         "commands": [
             "cd /tmp && export TMPDIR=/tmp",
             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch dir> -o run -- python3 bench.py "

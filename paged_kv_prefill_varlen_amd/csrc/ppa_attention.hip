@@ -23,11 +23,11 @@
 //
 // Per 64-key tile
 //   1. staging: each wave copies 8 consecutive keys of K and of V from their
-//      pages into double-buffered LDS, K in natural layout and V transposed
-//      in registers to [dim][key] (fp8 codes are widened to bf16 on the way:
-//      every e4m3fn value is a bf16 value).  With pages of >= 8 tokens a
-//      wave's keys share one page, whose id is read by a scalar load one tile
-//      ahead;
+//      pages into an LDS ring, both in natural [key][dim] layout with 16-byte
+//      chunks XOR swizzled by key: bf16 pages straight into LDS, fp8 codes
+//      through registers, widened to bf16 on the way (every e4m3fn value is a
+//      bf16 value).  With pages of >= 8 tokens a wave's keys share one page,
+//      whose id is read by a scalar load ahead of use;
 //   2. S^T = K Q^T on v_mfma_f32_32x32x16_bf16: keys along M, rows along N,
 //      so a lane holds 32 keys of one row and its partner lane (lane ^ 32) the
 //      other 32: row max / sum need one cross-lane step;
@@ -202,13 +202,9 @@ __device__ __forceinline__ uint32_t mx_pack4(float y0, float y1, float y2, float
 // unpadded rows whose 16-byte chunks are XOR swizzled by key (kswz, vswz), in
 // a four-stage ring consumed two tiles per barrier.  The PV operand, V^T, is
 // read with LDS transpose loads.
-// fp8 cache: staged through registers (widened to bf16 once per workgroup);
-// K in natural layout with the row stride padded by 16 bytes, so the S
-// operand reads, 16 different rows per 16 lanes, hit distinct banks; V as 4
-// consecutive keys x V_DPT dims per lane, transposed in registers to
-// [dim][key], with the 16-byte key chunks of each dim row XOR swizzled by
-// (dim >> 4) & 7 and rows padded by 16 bytes, which keeps both the transposed
-// writes and the MFMA operand reads free of bank conflicts; two stages.
+// fp8 cache: staged through registers (widened to bf16 once per workgroup)
+// into the same swizzled layout, so both caches share the operand reads;
+// two stages.
 template <int D, bool FP8>
 struct Tile {
   static constexpr int EB = FP8 ? 1 : 2;        // bytes per cache element
@@ -224,17 +220,11 @@ struct Tile {
   static constexpr int STAGES = DMA ? 4 : 2;     // LDS ring depth
   static constexpr int K_DW = DMA ? 1 : K_LANE_BYTES / 4;
   static constexpr int V_DW = DMA ? 1 : (4 * V_KEY_BYTES + 3) / 4;
-  static constexpr int KS = DMA ? D : D + 8;
-  static constexpr int VS = kBK + 8;
-  static constexpr int K_ELEMS = kBK * KS;
-  static constexpr int V_ELEMS = DMA ? kBK * D : D * VS;
+  static constexpr int K_ELEMS = kBK * D;   // both: natural [key][dim], swizzled
+  static constexpr int V_ELEMS = kBK * D;
   static_assert(K_PASSES * K_RPI == 8, "K staging map");
 };
 
-__device__ __forceinline__ int vt_offset(int d, int key, int vs) {
-  // element offset of V^T[d][key] in the swizzled layout
-  return d * vs + (((key >> 3) ^ ((d >> 4) & 7)) << 3) + (key & 7);
-}
 
 template <int BYTES>
 __device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src, bool ok) {
@@ -399,53 +389,44 @@ __device__ __forceinline__ void fetch_kv(uint32_t* kraw, uint32_t* vraw, const A
 }
 
 // ---- staging: registers -> LDS ------------------------------------------------
+// fp8 cache: the wave's 8 keys, widened to bf16, into the same natural,
+// swizzled layout the direct copies produce (16-byte chunk c of key row r
+// in slot c ^ kswz(r) for K, c ^ vswz(r) for V), so that both caches share
+// the operand reads.
 template <int D, bool FP8>
 __device__ __forceinline__ void store_kv(const uint32_t* kraw, const uint32_t* vraw, __bf16* klds, __bf16* vlds,
                                          int wave, int lane) {
   using T = Tile<D, FP8>;
-  // K rows
+  if constexpr (!FP8) return;   // the bf16 cache is copied straight into LDS
+  // K: K_CHUNK fp8 codes of row r0 from element chunk * K_CHUNK, i.e. whole
+  // 16-byte bf16 chunks chunk * K_CHUNK / 8 ..
   const int r0 = lane / T::K_TPR;
   const int chunk = lane % T::K_TPR;
   for (int p = 0; p < T::K_PASSES; ++p) {
-    __bf16* dst = klds + (8 * wave + p * T::K_RPI + r0) * T::KS + chunk * T::K_CHUNK;
+    const int row = 8 * wave + p * T::K_RPI + r0;
     const uint32_t* x = kraw + p * (T::K_LOAD / 4);
-    if constexpr (!FP8) {
-      if constexpr (T::K_LOAD == 16) *reinterpret_cast<u32x4*>(dst) = u32x4{x[0], x[1], x[2], x[3]};
-      else *reinterpret_cast<u32x2*>(dst) = u32x2{x[0], x[1]};
-    } else {
-      for (int i = 0; i < T::K_LOAD / 4; ++i) {
-        const u32x2 w = fp8x4_to_bf16x4(x[i]);
-        *reinterpret_cast<u32x2*>(dst + 4 * i) = w;
-      }
+    for (int q = 0; q < T::K_CHUNK / 8; ++q) {
+      const u32x2 a0 = fp8x4_to_bf16x4(x[2 * q]);
+      const u32x2 a1 = fp8x4_to_bf16x4(x[2 * q + 1]);
+      const int c = chunk * (T::K_CHUNK / 8) + q;
+      *reinterpret_cast<u32x4*>(klds + row * D + ((c ^ kswz<D>(row)) << 3)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
     }
   }
-  // V: 4 keys x V_DPT dims -> V_DPT dim rows of 4 keys
+  // V: keys key0 + r (r = 0..3) x dims dg * V_DPT .. + V_DPT - 1 of the lane
   constexpr int PAIRS = T::V_DPT / 2;   // bf16 pairs per key
-  uint32_t w[4][PAIRS];
-  for (int r = 0; r < 4; ++r) {
-    if constexpr (!FP8) {
-      for (int i = 0; i < PAIRS; ++i) w[r][i] = vraw[PAIRS * r + i];
-    } else if constexpr (T::V_KEY_BYTES == 4) {   // 4 fp8 per key
-      const u32x2 x = fp8x4_to_bf16x4(vraw[r]);
-      w[r][0] = x[0];
-      w[r][1] = x[1];
-    } else {                                       // 2 fp8 per key, two keys per dword
-      const uint32_t codes = (vraw[r >> 1] >> (16 * (r & 1))) & 0xffffu;
-      const u32x2 x = fp8x4_to_bf16x4(codes);
-      w[r][0] = x[0];
-    }
-  }
   const int key0 = 8 * wave + 4 * (lane >> 5);
   const int dg = lane & 31;
-  for (int i = 0; i < PAIRS; ++i) {
-    // dim 2i of the lane: low halves of the 4 keys; dim 2i+1: high halves
-    const uint32_t lo01 = (w[0][i] & 0xffffu) | (w[1][i] << 16);
-    const uint32_t lo23 = (w[2][i] & 0xffffu) | (w[3][i] << 16);
-    const uint32_t hi01 = (w[0][i] >> 16) | (w[1][i] & 0xffff0000u);
-    const uint32_t hi23 = (w[2][i] >> 16) | (w[3][i] & 0xffff0000u);
-    const int d = dg * T::V_DPT + 2 * i;
-    *reinterpret_cast<u32x2*>(vlds + vt_offset(d, key0, T::VS)) = u32x2{lo01, lo23};
-    *reinterpret_cast<u32x2*>(vlds + vt_offset(d + 1, key0, T::VS)) = u32x2{hi01, hi23};
+  const int d0 = dg * T::V_DPT;
+  for (int r = 0; r < 4; ++r) {
+    const int key = key0 + r;
+    __bf16* dst = vlds + key * D + (((d0 >> 3) ^ vswz<D>(key)) << 3) + (d0 & 7);
+    if constexpr (T::V_KEY_BYTES == 4) {   // 4 fp8 per key
+      *reinterpret_cast<u32x2*>(dst) = fp8x4_to_bf16x4(vraw[r]);
+    } else {                                // 2 fp8 per key, two keys per dword
+      static_assert(!FP8 || PAIRS == 1, "V staging map");
+      const uint32_t codes = (vraw[r >> 1] >> (16 * (r & 1))) & 0xffffu;
+      *reinterpret_cast<uint32_t*>(dst) = fp8x4_to_bf16x4(codes)[0];
+    }
   }
 }
 
@@ -606,17 +587,13 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   int id_next = 0;   // page id of the wave's keys in the next tile to fetch
 
   const int krow_lane = swap_bits23(col);
-  // V^T operand reads: lane (col, half) reads dims md*32 + col, keys
-  // 16 ks + 8 half .. + 7; in the swizzled layout that key chunk is
-  // 2 (ks ^ md) + (half ^ (col >> 4))
-  const int vrow_base = col * T::VS + ((half ^ (col >> 4)) & 1) * 8;
-  // transpose-load addresses (direct-copy layout): group G = lane / 16,
+  // transpose-load addresses: group G = lane / 16,
   // jj = lane % 16; key 8 (G / 2) + jj / 4 (+ 16 ks, + 4 for the second
   // load), dims md*32 + 16 (G % 2) + 4 (jj % 4), i.e. 16-byte chunk
   // 4 md + 2 (G % 2) + (jj % 4) / 2 at byte 8 (jj % 2) of it, in slot
   // chunk ^ vswz(key) (vswz depends only on jj / 4 here)
   int vt_lane = 0, vt_md[MD];
-  if constexpr (T::DMA) {
+  {
     const int G = lane >> 4, jj = lane & 15;
     const int key = 8 * (G >> 1) + (jj >> 2);
     vt_lane = key * (2 * D) + (jj & 1) * 8;
@@ -665,20 +642,13 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   // S operand, direct-copy layout: lane (col, half) reads K rows krow_lane
   // (+ 32) at chunk 2 s + half, whose slot is (2 s + half) ^ kswz(row); the
   // swizzle key is the same for both rows
-  const int kx = T::DMA ? (kswz<D>(krow_lane) ^ half) : 0;
+  const int kx = kswz<D>(krow_lane) ^ half;
   auto gemm_s = [&](int j) {
     bf16x8 kf[2][KSTEPS];
-    if constexpr (T::DMA) {
-      const __bf16* kbuf = klds[stage(j)] + krow_lane * D;
-      for (int s = 0; s < KSTEPS; ++s)
-        for (int mt = 0; mt < 2; ++mt)
-          kf[mt][s] = *reinterpret_cast<const bf16x8*>(kbuf + mt * 32 * D + ((2 * s) ^ kx) * 8);
-    } else {
-      const __bf16* kbuf = klds[stage(j)] + krow_lane * T::KS + half * 8;
-      for (int s = 0; s < KSTEPS; ++s)
-        for (int mt = 0; mt < 2; ++mt)
-          kf[mt][s] = *reinterpret_cast<const bf16x8*>(kbuf + mt * 32 * T::KS + s * 16);
-    }
+    const __bf16* kbuf = klds[stage(j)] + krow_lane * D;
+    for (int s = 0; s < KSTEPS; ++s)
+      for (int mt = 0; mt < 2; ++mt)
+        kf[mt][s] = *reinterpret_cast<const bf16x8*>(kbuf + mt * 32 * D + ((2 * s) ^ kx) * 8);
     __builtin_amdgcn_sched_barrier(0);
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
@@ -687,27 +657,20 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   };
   auto gemm_pv = [&](int j) {
     bf16x8 vf[MD][4];
-    if constexpr (T::DMA) {
-      // V^T operand by transpose loads: in each 16-lane group, lane jj points
-      // at key +jj/4, dims +4 (jj%4) and receives keys +0..3 of dim +jj; two
-      // loads give the 8 keys 16 ks + 8 half + 0..7 of dim md*32 + col
-      const char* vbuf = reinterpret_cast<const char*>(vlds[stage(j)]) + vt_lane;
-      for (int ks = 0; ks < 4; ++ks)
-        for (int md = 0; md < MD; ++md) {
-          typedef __attribute__((address_space(3))) v4s16 lds_v4s16;
-          const char* p0 = vbuf + vt_md[md] + (16 * ks) * (2 * D);
-          const v4s16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16*)(
-              (__attribute__((address_space(3))) char*)p0));
-          const v4s16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16*)(
-              (__attribute__((address_space(3))) char*)(p0 + 4 * (2 * D))));
-          vf[md][ks] = __builtin_bit_cast(bf16x8, v8s16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        }
-    } else {
-      const __bf16* vbuf = vlds[stage(j)] + vrow_base;
-      for (int ks = 0; ks < 4; ++ks)
-        for (int md = 0; md < MD; ++md)
-          vf[md][ks] = *reinterpret_cast<const bf16x8*>(vbuf + md * 32 * T::VS + ((ks ^ md) & 3) * 16);
-    }
+    // V^T operand by transpose loads: in each 16-lane group, lane jj points
+    // at key +jj/4, dims +4 (jj%4) and receives keys +0..3 of dim +jj; two
+    // loads give the 8 keys 16 ks + 8 half + 0..7 of dim md*32 + col
+    const char* vbuf = reinterpret_cast<const char*>(vlds[stage(j)]) + vt_lane;
+    for (int ks = 0; ks < 4; ++ks)
+      for (int md = 0; md < MD; ++md) {
+        typedef __attribute__((address_space(3))) v4s16 lds_v4s16;
+        const char* p0 = vbuf + vt_md[md] + (16 * ks) * (2 * D);
+        const v4s16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16*)(
+            (__attribute__((address_space(3))) char*)p0));
+        const v4s16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16*)(
+            (__attribute__((address_space(3))) char*)(p0 + 4 * (2 * D))));
+        vf[md][ks] = __builtin_bit_cast(bf16x8, v8s16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      }
     __builtin_amdgcn_sched_barrier(0);
     for (int ks = 0; ks < 4; ++ks)
       for (int md = 0; md < MD; ++md) oacc[md] = mfma32(vf[md][ks], pb[ks], oacc[md]);

@@ -187,7 +187,7 @@ class PpaError(RuntimeError):
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
-            f"HIP library {_LIB_PATH} is not built; run `python -m paged_kv_prefill_varlen_amd.build`")
+            f"HIP library {_LIB_PATH} is not built; run `python paged_kv_prefill_varlen_amd/build.py`")
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.POINTER(PpaParams)
     sigs = {

@@ -1,6 +1,7 @@
 """Build the C-ABI library ``_lib/libppa.so`` in-tree with hipcc for gfx950.
 
-Usage: ``python -m paged_kv_prefill_varlen_amd.build`` (or ``build()``).
+Usage: ``python paged_kv_prefill_varlen_amd/build.py`` (or ``__graft_entry__.build()``).
+It is run as a script because importing the package needs the built library.
 The host validator is plain C++ and the kernels are HIP; both go into one
 shared library.  Packed FP32 instructions are disabled for the device code.
 """

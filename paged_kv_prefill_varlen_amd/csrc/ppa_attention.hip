@@ -655,8 +655,10 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     for (int s = 0; s < KSTEPS; ++s)
       for (int mt = 0; mt < 2; ++mt) sacc[mt] = mfma32(kf[mt][s], qf[s], sacc[mt]);
   };
-  auto gemm_pv = [&](int j) {
-    bf16x8 vf[MD][4];
+  // V^T operand of tile j, read into registers before the softmax of the
+  // tile so that the LDS latency passes under its exponentials
+  bf16x8 vf[MD][4];
+  auto read_v = [&](int j) {
     // V^T operand by transpose loads: in each 16-lane group, lane jj points
     // at key +jj/4, dims +4 (jj%4) and receives keys +0..3 of dim +jj; two
     // loads give the 8 keys 16 ks + 8 half + 0..7 of dim md*32 + col
@@ -672,6 +674,8 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
         vf[md][ks] = __builtin_bit_cast(bf16x8, v8s16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       }
     __builtin_amdgcn_sched_barrier(0);
+  };
+  auto gemm_pv = [&](int j) {
     for (int ks = 0; ks < 4; ++ks)
       for (int md = 0; md < MD; ++md) oacc[md] = mfma32(vf[md][ks], pb[ks], oacc[md]);
   };
@@ -746,11 +750,13 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
       }
       if (wave_tile(j)) {
         gemm_s(j);
+        read_v(j);
         softmax(j);
         gemm_pv(j);
       }
       if (j + 1 <= hi && wave_tile(j + 1)) {
         gemm_s(j + 1);
+        read_v(j + 1);
         softmax(j + 1);
         gemm_pv(j + 1);
       }
@@ -769,6 +775,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
       }
       if (wave_tile(j)) {
         gemm_s(j);
+        read_v(j);
         softmax(j);
         gemm_pv(j);
       }

@@ -235,7 +235,9 @@ def kernel_code_digest(lib_path: str, kernel: str) -> str:
 
 # the kernel the stored counters of a bf16 workload were taken on
 def _kernel_symbol(case) -> str:
-    return "paged_prefill_persistentILi%dELb%dELb1E" % (case["head_dim"], 1 if case["kv_dtype"] != "bf16" else 0)
+    fp8 = case["kv_dtype"] != "bf16"
+    return "paged_prefill_persistentILi%dELb%dELb1ELb%dE" % (case["head_dim"], 1 if fp8 else 0,
+                                                             1 if fp8 and case["head_dim"] == 128 else 0)
 
 
 def _library_path() -> str:
@@ -396,6 +398,9 @@ def main():
     ap.add_argument("--config", default="chunked", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--fp8-compute", choices=["auto", "0", "1"], default="auto",
+                    help="fp8 cache: 1 runs both products on the fp8 MFMA (Q and P rounded to e4m3fn), 0 "
+                         "widens the codes to bf16; auto: 1 at head_dim 128")
     ap.add_argument("--kv-splits", default="auto",
                     help="split-KV chunks per work item (0: none; auto: the library's planner, the default)")
     ap.add_argument("--cold-iters", type=int, default=10,
@@ -451,16 +456,18 @@ def main():
     # device, within a workspace sized for up to 256 splits (at most 256 MiB)
     auto = args.kv_splits == "auto"
     splits = 256 if auto else int(args.kv_splits)
+    f8c = case["kv_dtype"] != "bf16" and (args.fp8_compute == "1" or
+                                          (args.fp8_compute == "auto" and case["head_dim"] == 128))
     p = ppa.make_params(q, kv, None, bt, sl, case["max_q_len"], case["max_kv_len"], case["bmm1_scale"],
                         case["bmm2_scale"], case["batch_size"], cuq, cukv, case["window_left"], out,
-                        case["kv_layout"], sinks, kv_splits=splits)
+                        case["kv_layout"], sinks, kv_splits=splits, fp8_compute=f8c)
     ws_bytes = ppa.ppa_workspace_bytes(p)
     if auto:
         ws_bytes = max(ppa.WORKSPACE_BYTES, min(ws_bytes, 256 << 20))
     workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     p = ppa.make_params(q, kv, workspace, bt, sl, case["max_q_len"], case["max_kv_len"], case["bmm1_scale"],
                         case["bmm2_scale"], case["batch_size"], cuq, cukv, case["window_left"], out,
-                        case["kv_layout"], sinks, kv_splits=0 if auto else splits)
+                        case["kv_layout"], sinks, kv_splits=0 if auto else splits, fp8_compute=f8c)
     if auto:
         p.kv_splits = ppa.ppa_plan_kv_splits(p)
     args.kv_splits = int(p.kv_splits)
@@ -522,20 +529,24 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     kernel_tflops = flops / (launch_ms * 1e-3) / 1e12
     fp8 = case["kv_dtype"] != "bf16"
+    # an fp8 cache at head_dim 128 runs both products on the fp8 MFMA (Q and
+    # P rounded to e4m3fn): the contraction's own peak is the fp8 one
+    mma_fp8 = bool(p.fp8_compute)
+    peak = PEAK_FP8_TFLOPS if mma_fp8 else PEAK_BF16_TFLOPS
     alg_bytes = algorithmic_bytes(case, 2.0 if args.out_dtype == "bf16" else 0.5 + 1.0 / args.o_sf_vec_size)
     # the bound follows the arithmetic intensity: below the ridge
     # (peak FLOP/s over HBM bytes/s) the compulsory bytes bound the kernel
     ai = flops / alg_bytes
-    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     hbm = args.config == "decode" or ai < ridge
-    attainable = min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1e3)
+    attainable = min(peak, ai * PEAK_HBM_GBS / 1e3)
     if hbm:   # the compulsory bytes bound it: report bandwidth against HBM
         kernel_gbs = alg_bytes / (launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(kernel_gbs / PEAK_HBM_GBS, 4), "traffic": None}
     else:
-        roof = {"bound": "mfma", "achieved": round(kernel_tflops, 3), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
+        roof = {"bound": "mfma", "achieved": round(kernel_tflops, 3), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(kernel_tflops / peak, 4),
                 "traffic": stored_traffic(args.config) if args.out_dtype == "bf16" else None}
     roof.update({"algorithmic_bytes": alg_bytes, "kernel_ms": round(launch_ms, 5),
                  "bracketed_launch_ms_median": round(float(np.median(launch_times)), 5),
@@ -544,7 +555,9 @@ def main():
                  "attainable_tflops": round(attainable, 1),
                  "frac_attainable": round(kernel_tflops / attainable, 4),
                  "executed_tflops": round(executed_flops(case) / (launch_ms * 1e-3) / 1e12, 3),
-                 "kernel": "paged_prefill_persistent<%d,%s>%s" % (case["head_dim"], "fp8" if fp8 else "bf16",
+                 "kernel": "paged_prefill_persistent<%d,%s>%s" % (case["head_dim"],
+                                                                  ("fp8 MFMA" if mma_fp8 else "fp8 widened to bf16")
+                                                                  if fp8 else "bf16",
                                                                   " + merge" if args.kv_splits > 1 else "")})
     line = {
         "metric": METRIC,
@@ -557,7 +570,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if mma_fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config,
                    "query_tokens": tokens, "causal_gflop": round(flops / 1e9, 3),
@@ -565,6 +578,7 @@ def main():
                    else f"mxfp4/{args.o_sf_vec_size}", "parallelism": "none (one GPU)"},
         "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "pct_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2) if mma_fp8 else None,
         "roofline": roof,
         "cpu_baseline": None,
         "device": device_info(torch, dev),

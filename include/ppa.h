@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PPA_ABI_VERSION 5
+#define PPA_ABI_VERSION 6
 
 typedef enum ppa_status {
   PPA_OK = 0,
@@ -251,6 +251,20 @@ typedef struct ppa_params {
   int64_t out_sf_strides[2];
   float o_sf_scale;
   int32_t o_sf_vec_size;
+
+  /* Arithmetic for an fp8 cache (TensorRT-LLM attention-backend article,
+     the fp8 KV cache and its fp8 context attention; BASELINE's long-prefix
+     fp8 workload folds the per-tensor scales into bmm1_scale / bmm2_scale).
+       0  each e4m3fn code is widened to bf16 (exact) and both products run
+          on the bf16 MFMA; Q and the softmax weights stay bf16
+       1  head_dim 128 only: Q (after the sign of bmm1_scale) and the
+          softmax weights are rounded to e4m3fn (nearest even, Q saturated
+          at +-448) and both products run on the fp8 MFMA at twice the bf16
+          rate; the row sums add the rounded weights.  Each logit then
+          carries the rounding of its Q elements (unit roundoff 2^-4).
+     Any other value, or 1 with a bf16 cache or head_dim 64, is
+     PPA_ERR_DTYPE. */
+  int32_t fp8_compute;
 } ppa_params;
 
 /*

@@ -14,7 +14,7 @@ from typing import NamedTuple, Optional, Sequence, Tuple, Union
 import numpy as np
 import torch
 
-PPA_ABI_VERSION = 5
+PPA_ABI_VERSION = 6
 
 # enums of ppa.h
 PPA_DTYPE_BF16 = 1
@@ -87,6 +87,7 @@ class PpaParams(ctypes.Structure):
         ("out_sf_strides", c_int64 * 2),
         ("o_sf_scale", c_float),
         ("o_sf_vec_size", c_int32),
+        ("fp8_compute", c_int32),
     ]
 
 
@@ -468,7 +469,7 @@ def make_params(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.
                 kv_layout: str = "HND", sinks=None, kv_indptr: Optional[torch.Tensor] = None,
                 kv_indices: Optional[torch.Tensor] = None,
                 kv_last_page_len: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                kv_splits: int = 0) -> PpaParams:
+                kv_splits: int = 0, fp8_compute: bool = False) -> PpaParams:
     """Fill a PpaParams from torch tensors (the FlashInfer API page's argument
     list).  With kv_indptr / kv_indices the flat (CSR) page table is used and
     block_tables may be None.  Keeps no reference to the tensors: the caller
@@ -573,6 +574,7 @@ def make_params(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.
         p.lse = _ptr(lse)
         p.lse_strides[:] = list(lse.stride())
     p.kv_splits = int(kv_splits)
+    p.fp8_compute = 1 if fp8_compute else 0
     return p
 
 
@@ -598,7 +600,7 @@ def batch_context_with_kv_cache(query: torch.Tensor, kv_cache, workspace_buffer:
                                 validate: bool = False, stream=None, kv_indptr=None, kv_indices=None,
                                 kv_last_page_len=None, lse: Optional[torch.Tensor] = None,
                                 kv_splits: Union[int, str] = 0, o_sf_scale: Optional[float] = None,
-                                o_sf_vec_size: Optional[int] = None):
+                                o_sf_vec_size: Optional[int] = None, fp8_compute: bool = False):
     """Batched paged prefill attention; argument list of the API page
     (without the PDL option), plus the optional flat page table (kv_indptr /
     kv_indices / kv_last_page_len) in place of block_tables, an optional fp32
@@ -608,7 +610,9 @@ def batch_context_with_kv_cache(query: torch.Tensor, kv_cache, workspace_buffer:
     it from the shapes, the device and the workspace size).  The FP4 output of the API page is given
     as OCP MXFP4: ``out_dtype="mxfp4"`` (or an ``MxFp4Output`` as ``out``)
     with ``o_sf_scale`` (default 1) and ``o_sf_vec_size`` (16 or 32, default
-    32) returns an ``MxFp4Output``.  ``validate=True`` also runs the deep
+    32) returns an ``MxFp4Output``.  ``fp8_compute=True`` (fp8 cache,
+    head_dim 128) rounds Q and the softmax weights to e4m3fn and runs both
+    products on the fp8 MFMA.  ``validate=True`` also runs the deep
     metadata check on host copies (a device-to-host sync)."""
     if isinstance(out_dtype, str):
         if out_dtype.lower() != "mxfp4":
@@ -625,7 +629,8 @@ def batch_context_with_kv_cache(query: torch.Tensor, kv_cache, workspace_buffer:
         raise ValueError(f"kv_splits {kv_splits!r}: an int or 'auto'")
     p = make_params(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_q_len, max_kv_len,
                     bmm1_scale, bmm2_scale, batch_size, cum_seq_lens_q, cum_seq_lens_kv, window_left,
-                    out, kv_layout, sinks, kv_indptr, kv_indices, kv_last_page_len, lse, 0 if auto else kv_splits)
+                    out, kv_layout, sinks, kv_indptr, kv_indices, kv_last_page_len, lse, 0 if auto else kv_splits,
+                    fp8_compute)
     if auto:
         with torch.cuda.device(query.device):
             p.kv_splits = ppa_plan_kv_splits(p)

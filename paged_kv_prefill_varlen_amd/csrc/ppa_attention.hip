@@ -59,6 +59,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(8))) int i32x8;   // 32 fp8 codes: one f8f6f4 MFMA operand
 
 constexpr int kBK = 64;            // keys per tile
 constexpr int kWaves = 8;
@@ -119,6 +120,12 @@ struct AttnArgs {
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 32x32x64 MFMA on OCP e4m3fn codes (format 0 for both operands), unit
+// block scales (E8M0 127 = 2^0)
+__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -205,7 +212,7 @@ __device__ __forceinline__ uint32_t mx_pack4(float y0, float y1, float y2, float
 // fp8 cache: staged through registers (widened to bf16 once per workgroup)
 // into the same swizzled layout, so both caches share the operand reads;
 // two stages.
-template <int D, bool FP8>
+template <int D, bool FP8, bool F8M = false>
 struct Tile {
   static constexpr int EB = FP8 ? 1 : 2;        // bytes per cache element
   static constexpr int K_LANE_BYTES = D * EB / 8;              // 8 rows per wave
@@ -220,6 +227,11 @@ struct Tile {
   static constexpr int STAGES = DMA ? 4 : 2;     // LDS ring depth
   static constexpr int K_DW = DMA ? 1 : K_LANE_BYTES / 4;
   static constexpr int V_DW = DMA ? 1 : (4 * V_KEY_BYTES + 3) / 4;
+  // fp8 cache at head_dim 128: QK^T and PV on the fp8 MFMA (Q and P
+  // quantised to e4m3fn); K stays in code bytes [key][dim], V is stored
+  // transposed as code bytes [dim][key]; both in the first half of a stage
+  static constexpr bool F8MMA = F8M;
+  static_assert(!F8M || (FP8 && D == 128), "fp8 MFMA: fp8 cache at head_dim 128");
   static constexpr int K_ELEMS = kBK * D;   // both: natural [key][dim], swizzled
   static constexpr int V_ELEMS = kBK * D;
   static_assert(K_PASSES * K_RPI == 8, "K staging map");
@@ -393,11 +405,36 @@ __device__ __forceinline__ void fetch_kv(uint32_t* kraw, uint32_t* vraw, const A
 // swizzled layout the direct copies produce (16-byte chunk c of key row r
 // in slot c ^ kswz(r) for K, c ^ vswz(r) for V), so that both caches share
 // the operand reads.
-template <int D, bool FP8>
+template <int D, bool FP8, bool F8M>
 __device__ __forceinline__ void store_kv(const uint32_t* kraw, const uint32_t* vraw, __bf16* klds, __bf16* vlds,
                                          int wave, int lane) {
-  using T = Tile<D, FP8>;
+  using T = Tile<D, FP8, F8M>;
   if constexpr (!FP8) return;   // the bf16 cache is copied straight into LDS
+  if constexpr (T::F8MMA) {
+    // K: the lane's 16 codes (dims 16 chunk ..) of row r0, as they are, in
+    // 16-byte slot chunk ^ ((row / 2) mod 8) of the 128-byte row
+    uint8_t* kb8 = reinterpret_cast<uint8_t*>(klds);
+    const int krow = 8 * wave + lane / 8;
+    const int kch = lane % 8;
+    *reinterpret_cast<u32x4*>(kb8 + krow * 128 + ((kch ^ ((krow >> 1) & 7)) << 4)) =
+        u32x4{kraw[0], kraw[1], kraw[2], kraw[3]};
+    // V: keys 8 wave + 4 kgl + r (r = 0..3) x dims 4 dg + q (q = 0..3); as
+    // V^T rows of 64 key bytes in the order the PV operand takes them: key
+    // 8 run + e at byte 32 (run mod 2) + 8 (run / 2) + e; 16-byte slot
+    // chunk ^ ((dim / 4) mod 4)
+    uint8_t* vb8 = reinterpret_cast<uint8_t*>(vlds);
+    const int kgl = lane >> 5, dg = lane & 31;
+    const int pos = 32 * (wave & 1) + 8 * (wave >> 1) + 4 * kgl;
+    for (int q = 0; q < 4; ++q) {
+      // byte q of each key's dword -> one dword of 4 keys for dim 4 dg + q
+      const uint32_t lo = __builtin_amdgcn_perm(vraw[1], vraw[0], 0x0c0c0400u + 0x0101u * q);
+      const uint32_t hi = __builtin_amdgcn_perm(vraw[3], vraw[2], 0x0c0c0400u + 0x0101u * q);
+      const uint32_t w = lo | (hi << 16);
+      const int m = 4 * dg + q;
+      *reinterpret_cast<uint32_t*>(vb8 + m * 64 + ((((pos >> 4) ^ ((m >> 2) & 3))) << 4) + (pos & 15)) = w;
+    }
+    return;
+  }
   // K: K_CHUNK fp8 codes of row r0 from element chunk * K_CHUNK, i.e. whole
   // 16-byte bf16 chunks chunk * K_CHUNK / 8 ..
   const int r0 = lane / T::K_TPR;
@@ -467,9 +504,9 @@ __device__ __forceinline__ void store_mxfp4_row(const f32x16* oacc, float inv, f
 // heaviest query tile first.  Per K/V tile: stage tile j+1 into registers, run
 // S, softmax and PV for tile j from LDS, store tile j+1 into the other LDS
 // buffer, barrier.  Every wave of the workgroup calls this with the same item.
-template <int D, bool FP8, bool UPAGE>
+template <int D, bool FP8, bool UPAGE, bool F8M>
 __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
-  using T = Tile<D, FP8>;
+  using T = Tile<D, FP8, F8M>;
   constexpr int KSTEPS = D / 16;   // MFMA K-steps over head_dim
   constexpr int MD = D / 32;       // 32-wide head_dim tiles of O^T
   __shared__ __attribute__((aligned(16))) __bf16 klds[T::STAGES][T::K_ELEMS];
@@ -553,10 +590,39 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
       qf[s] = __builtin_bit_cast(bf16x8, x);
     }
   };
+  // fp8 MFMA: the B operand of S^T = K Q^T is 32 e4m3fn codes per lane and
+  // 64-dim chunk c, dims 64 c + 32 half + 0..31 in byte order (the K
+  // operand takes the same dims in the same bytes, so the MFMA's own order
+  // of the contraction index within a lane does not matter).  Values beyond
+  // the e4m3fn range saturate at +-448.
+  i32x8 qf8[2];
+  auto load_q8 = [&]() {
+    const uint16_t* qrow = a.q + static_cast<int64_t>(q0 + t0 + (rvalid ? tok : 0)) * a.q_tok +
+                           static_cast<int64_t>(h0 + (rvalid ? hd : 0)) * a.q_head;
+    for (int cc = 0; cc < 2; ++cc) {
+      uint32_t w[16];
+      for (int t = 0; t < 4; ++t) {
+        u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 64 * cc + 32 * half + 8 * t);
+        if (!rvalid) x = u32x4{0, 0, 0, 0};
+        if (negate_q) x ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+        for (int e = 0; e < 4; ++e) w[4 * t + e] = x[e];
+      }
+      for (int jd = 0; jd < 8; ++jd) {
+        float f[4] = {__builtin_bit_cast(float, w[2 * jd] << 16), __builtin_bit_cast(float, w[2 * jd] & 0xffff0000u),
+                      __builtin_bit_cast(float, w[2 * jd + 1] << 16),
+                      __builtin_bit_cast(float, w[2 * jd + 1] & 0xffff0000u)};
+        for (int e = 0; e < 4; ++e) f[e] = __builtin_fminf(__builtin_fmaxf(f[e], -448.f), 448.f);
+        int code = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+        code = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], code, true);
+        qf8[cc][jd] = code;
+      }
+    }
+  };
   // direct-copy path: Q is loaded after the first tile's copies are issued
   // (below), and both are waited for together, so that no later compiler
   // wait for Q covers the prefetched tiles
-  if constexpr (!T::DMA) load_q();
+  if constexpr (T::F8MMA) load_q8();
+  else if constexpr (!T::DMA) load_q();
   // the row's sink logit, read now so that the epilogue does not wait for it
   const float sink = a.sinks ? a.sinks[h0 + (rvalid ? hd : 0)] : 0.f;
 
@@ -637,13 +703,34 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   };
   auto stage_store = [&](int j) {
     const int buf = stage(j);
-    store_kv<D, FP8>(kraw, vraw, klds[buf], vlds[buf], wave, lane);
+    store_kv<D, FP8, F8M>(kraw, vraw, klds[buf], vlds[buf], wave, lane);
   };
   // S operand, direct-copy layout: lane (col, half) reads K rows krow_lane
   // (+ 32) at chunk 2 s + half, whose slot is (2 s + half) ^ kswz(row); the
   // swizzle key is the same for both rows
   const int kx = kswz<D>(krow_lane) ^ half;
   auto gemm_s = [&](int j) {
+    if constexpr (T::F8MMA) {
+      // K operand: row krow_lane (+ 32), bytes 64 c + 32 half .. + 31, i.e.
+      // 16-byte chunks 4 c + 2 half (+ 1) in slots chunk ^ ((row / 2) mod 8)
+      const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(klds[stage(j)]);
+      i32x8 kf8[2][2];
+      for (int mt = 0; mt < 2; ++mt)
+        for (int cc = 0; cc < 2; ++cc) {
+          const int row = krow_lane + 32 * mt;
+          const int c0 = 4 * cc + 2 * half;
+          const u32x4 x0 = *reinterpret_cast<const u32x4*>(kb8 + row * 128 + ((c0 ^ ((row >> 1) & 7)) << 4));
+          const u32x4 x1 = *reinterpret_cast<const u32x4*>(kb8 + row * 128 + (((c0 + 1) ^ ((row >> 1) & 7)) << 4));
+          kf8[mt][cc] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                              (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      sacc[0] = f32x16{};
+      sacc[1] = f32x16{};
+      for (int cc = 0; cc < 2; ++cc)
+        for (int mt = 0; mt < 2; ++mt) sacc[mt] = mfma32_fp8(kf8[mt][cc], qf8[cc], sacc[mt]);
+      return;
+    }
     bf16x8 kf[2][KSTEPS];
     const __bf16* kbuf = klds[stage(j)] + krow_lane * D;
     for (int s = 0; s < KSTEPS; ++s)
@@ -658,7 +745,23 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   // V^T operand of tile j, read into registers before the softmax of the
   // tile so that the LDS latency passes under its exponentials
   bf16x8 vf[MD][4];
+  i32x8 vf8[MD];
   auto read_v = [&](int j) {
+    if constexpr (T::F8MMA) {
+      // V^T operand: dim row md*32 + col, key bytes 32 half .. + 31 (the
+      // order P's bytes take), 16-byte chunks 2 half (+ 1) in slots
+      // chunk ^ ((dim / 4) mod 4)
+      const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(vlds[stage(j)]);
+      for (int md = 0; md < MD; ++md) {
+        const int m = md * 32 + col;
+        const int sw = (m >> 2) & 3;
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(vb8 + m * 64 + (((2 * half) ^ sw) << 4));
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(vb8 + m * 64 + (((2 * half + 1) ^ sw) << 4));
+        vf8[md] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
     // V^T operand by transpose loads: in each 16-lane group, lane jj points
     // at key +jj/4, dims +4 (jj%4) and receives keys +0..3 of dim +jj; two
     // loads give the 8 keys 16 ks + 8 half + 0..7 of dim md*32 + col
@@ -675,7 +778,12 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
       }
     __builtin_amdgcn_sched_barrier(0);
   };
+  i32x8 pf8;
   auto gemm_pv = [&](int j) {
+    if constexpr (T::F8MMA) {
+      for (int md = 0; md < MD; ++md) oacc[md] = mfma32_fp8(vf8[md], pf8, oacc[md]);
+      return;
+    }
     for (int ks = 0; ks < 4; ++ks)
       for (int md = 0; md < MD; ++md) oacc[md] = mfma32(vf[md][ks], pb[ks], oacc[md]);
   };
@@ -707,6 +815,26 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
       for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
     }
     const float mb = m_run == kNegInf ? 0.f : m_run;
+    if constexpr (T::F8MMA) {
+      // P as e4m3fn codes (p <= 2^8 with the lazy maximum: within range),
+      // byte 16 mt + v = element v of sacc[mt]; the row sum adds the
+      // weights decoded back from those codes, so that the numerator and
+      // the denominator see the same rounded weights
+      float sum = l_part;
+      for (int mt = 0; mt < 2; ++mt)
+        for (int q = 0; q < 4; ++q) {
+          float p[4];
+          for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][4 * q + e], c, -mb));
+          int code = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          code = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], code, true);
+          pf8[4 * mt + q] = code;
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(code, true);
+          sum += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+        }
+      l_part = sum;
+      return;
+    }
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float sum = l_part;
     for (int mt = 0; mt < 2; ++mt)
@@ -829,10 +957,10 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
 }
 
 // One workgroup per work item, in heaviest-first order.
-template <int D, bool FP8, bool UPAGE>
+template <int D, bool FP8, bool UPAGE, bool F8M>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void paged_prefill_kernel(AttnArgs a) {
-  attend_item<D, FP8, UPAGE>(a, blockIdx.x);
+  attend_item<D, FP8, UPAGE, F8M>(a, blockIdx.x);
 }
 
 // Persistent workgroups (as many as fit on the device at once) pull work
@@ -843,7 +971,7 @@ void paged_prefill_kernel(AttnArgs a) {
 // pairs) and is served by the workgroups with blockIdx % 8 == x, which the
 // dispatcher places on one XCD, so that K/V stays in one L2.  The last
 // workgroup to finish returns every counter to zero for the next call.
-template <int D, bool FP8, bool UPAGE>
+template <int D, bool FP8, bool UPAGE, bool F8M>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void paged_prefill_persistent(AttnArgs a) {
   __shared__ uint32_t next_item[2];
@@ -856,7 +984,7 @@ void paged_prefill_persistent(AttnArgs a) {
     __syncthreads();
     const uint64_t item = static_cast<uint64_t>(next_item[round & 1]) * nq + queue;
     if (item >= static_cast<uint64_t>(a.n_items)) break;
-    attend_item<D, FP8, UPAGE>(a, static_cast<int>(item));
+    attend_item<D, FP8, UPAGE, F8M>(a, static_cast<int>(item));
   }
   if (threadIdx.x == 0 && atomicAdd(sched + kSchedDone, 1u) == gridDim.x - 1) {
     // every workgroup has made its last fetch: no counter is read again
@@ -1022,7 +1150,7 @@ hipError_t launch_merge(const MergeArgs& m, int head_dim, hipStream_t stream) {
 
 // Workgroups of a persistent kernel that the device holds at once (cached per
 // device and kernel).
-template <int D, bool FP8, bool UPAGE>
+template <int D, bool FP8, bool UPAGE, bool F8M>
 int resident_workgroups() {
   static int cache[64];
   int dev = 0;
@@ -1030,18 +1158,18 @@ int resident_workgroups() {
   if (cache[dev] > 0) return cache[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, paged_prefill_persistent<D, FP8, UPAGE>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, paged_prefill_persistent<D, FP8, UPAGE, F8M>,
                                                    64 * kWaves, 0) != hipSuccess)
     return 0;
   cache[dev] = cus * (per_cu > 0 ? per_cu : 1);
   return cache[dev];
 }
 
-template <int D, bool FP8, bool UPAGE>
+template <int D, bool FP8, bool UPAGE, bool F8M>
 hipError_t launch_variant(AttnArgs a, int items, hipStream_t stream) {
-  const int resident = a.sched ? resident_workgroups<D, FP8, UPAGE>() : 0;
+  const int resident = a.sched ? resident_workgroups<D, FP8, UPAGE, F8M>() : 0;
   if (resident <= 0) {
-    hipLaunchKernelGGL((paged_prefill_kernel<D, FP8, UPAGE>), dim3(items), dim3(64 * kWaves), 0, stream, a);
+    hipLaunchKernelGGL((paged_prefill_kernel<D, FP8, UPAGE, F8M>), dim3(items), dim3(64 * kWaves), 0, stream, a);
     return hipGetLastError();
   }
   const int R = a.batch * a.num_kv_heads * a.n_hg;
@@ -1052,13 +1180,14 @@ hipError_t launch_variant(AttnArgs a, int items, hipStream_t stream) {
     a.n_queues = kSchedQueues;
   }
   a.n_items = items;
-  hipLaunchKernelGGL((paged_prefill_persistent<D, FP8, UPAGE>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
+  hipLaunchKernelGGL((paged_prefill_persistent<D, FP8, UPAGE, F8M>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool F8M = false>
 hipError_t launch(const AttnArgs& a, int items, hipStream_t stream, bool upage) {
-  return upage ? launch_variant<D, FP8, true>(a, items, stream) : launch_variant<D, FP8, false>(a, items, stream);
+  return upage ? launch_variant<D, FP8, true, F8M>(a, items, stream)
+               : launch_variant<D, FP8, false, F8M>(a, items, stream);
 }
 
 // Uniform-page staging (the 8 keys a wave copies lie in one page) needs pages
@@ -1073,9 +1202,9 @@ bool uniform_pages(const ppa_params* p, const CacheView& cv) {
          extent(cv.v_head, cv.v_tok) < (int64_t{1} << 31);
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool F8M = false>
 int resident_for(bool upage) {
-  return upage ? resident_workgroups<D, FP8, true>() : resident_workgroups<D, FP8, false>();
+  return upage ? resident_workgroups<D, FP8, true, F8M>() : resident_workgroups<D, FP8, false, F8M>();
 }
 
 }  // namespace
@@ -1155,7 +1284,8 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
   const int g = static_cast<int>(grid);
   const bool upage = uniform_pages(p, cv);
   if (p->head_dim == 128)
-    e = fp8 ? launch<128, true>(a, g, s, upage) : launch<128, false>(a, g, s, upage);
+    e = !fp8 ? launch<128, false>(a, g, s, upage)
+             : (p->fp8_compute ? launch<128, true, true>(a, g, s, upage) : launch<128, true>(a, g, s, upage));
   else
     e = fp8 ? launch<64, true>(a, g, s, upage) : launch<64, false>(a, g, s, upage);
   if (e == hipSuccess && a.kv_splits > 1) {
@@ -1204,7 +1334,9 @@ extern "C" int32_t ppa_plan_kv_splits(const ppa_params* p) {
   resolve_cache(&q, &cv);
   const bool upage = uniform_pages(&q, cv);
   const bool fp8 = q.kv_dtype == PPA_DTYPE_FP8_E4M3FN;
-  const int resident = q.head_dim == 128 ? (fp8 ? resident_for<128, true>(upage) : resident_for<128, false>(upage))
+  const int resident = q.head_dim == 128 ? (!fp8 ? resident_for<128, false>(upage)
+                                                  : (q.fp8_compute ? resident_for<128, true, true>(upage)
+                                                                   : resident_for<128, true>(upage)))
                                          : (fp8 ? resident_for<64, true>(upage) : resident_for<64, false>(upage));
   if (resident <= 0) return PPA_ERR_HIP;
   // work items as the launch counts them, and the key tiles of the longest

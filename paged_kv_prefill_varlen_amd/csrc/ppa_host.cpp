@@ -169,6 +169,10 @@ int32_t ppa_validate_shapes(const ppa_params* p, char* msg, size_t msg_len) {
     return fail(PPA_ERR_SHAPE, msg, msg_len, "o_sf_scale must be finite and > 0");
   if (p->kv_dtype != PPA_DTYPE_BF16 && p->kv_dtype != PPA_DTYPE_FP8_E4M3FN)
     return fail(PPA_ERR_DTYPE, msg, msg_len, "kv dtype %d: bf16 or fp8 e4m3fn", p->kv_dtype);
+  if (p->fp8_compute != 0 && p->fp8_compute != 1)
+    return fail(PPA_ERR_DTYPE, msg, msg_len, "fp8_compute %d: 0 or 1", p->fp8_compute);
+  if (p->fp8_compute == 1 && (p->kv_dtype != PPA_DTYPE_FP8_E4M3FN || p->head_dim != 128))
+    return fail(PPA_ERR_DTYPE, msg, msg_len, "fp8_compute needs an fp8 e4m3fn cache at head_dim 128");
 
   // enums
   if (p->kv_layout != PPA_KV_LAYOUT_HND && p->kv_layout != PPA_KV_LAYOUT_NHD)
@@ -389,6 +393,10 @@ int32_t ppa_validate_append(const ppa_params* p, const ppa_append_params* a, cha
     return fail(PPA_ERR_ABI, msg, msg_len, "abi_version / struct_size mismatch");
   if (p->kv_dtype != PPA_DTYPE_BF16 && p->kv_dtype != PPA_DTYPE_FP8_E4M3FN)
     return fail(PPA_ERR_DTYPE, msg, msg_len, "kv dtype %d: bf16 or fp8 e4m3fn", p->kv_dtype);
+  if (p->fp8_compute != 0 && p->fp8_compute != 1)
+    return fail(PPA_ERR_DTYPE, msg, msg_len, "fp8_compute %d: 0 or 1", p->fp8_compute);
+  if (p->fp8_compute == 1 && (p->kv_dtype != PPA_DTYPE_FP8_E4M3FN || p->head_dim != 128))
+    return fail(PPA_ERR_DTYPE, msg, msg_len, "fp8_compute needs an fp8 e4m3fn cache at head_dim 128");
   if (a->new_dtype != PPA_DTYPE_BF16)
     return fail(PPA_ERR_DTYPE, msg, msg_len, "new K/V dtype %d: only bf16", a->new_dtype);
   if (p->kv_layout != PPA_KV_LAYOUT_HND && p->kv_layout != PPA_KV_LAYOUT_NHD)

@@ -51,7 +51,7 @@ def split_workspace(dcase: dict, kv_splits: int) -> torch.Tensor:
 
 def run_gpu(dcase: dict, out: torch.Tensor = None, bmm1=None, bmm2=None, stream=None,
             validate=True, schedule="persistent", lse: torch.Tensor = None, kv_splits: int = 0,
-            ws: torch.Tensor = None) -> torch.Tensor:
+            ws: torch.Tensor = None, fp8_compute: bool = False) -> torch.Tensor:
     """schedule: "persistent" (workspace given: balanced persistent workgroups)
     or "grid" (no workspace: one workgroup per work item).  With kv_splits > 1
     a workspace of the needed size is allocated unless ``ws`` is given."""
@@ -74,7 +74,7 @@ def run_gpu(dcase: dict, out: torch.Tensor = None, bmm1=None, bmm2=None, stream=
         window_left=dcase["window_left"], out=out, kv_layout=dcase["kv_layout"],
         sinks=dcase["sinks"], validate=validate, stream=stream, kv_indptr=dcase.get("kv_indptr"),
         kv_indices=dcase.get("kv_indices"), kv_last_page_len=dcase.get("kv_last_page_len"), lse=lse,
-        kv_splits=kv_splits)
+        kv_splits=kv_splits, fp8_compute=fp8_compute)
     return out
 
 

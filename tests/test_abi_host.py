@@ -149,6 +149,16 @@ def test_fp8_kv_and_sinks_pass():
     assert _shapes(p)[0] == OK
 
 
+def test_fp8_compute_flag():
+    """fp8_compute = 1 is accepted with an fp8 cache at head_dim 128 only."""
+    assert _shapes(_params(_case(D=128, kv_dtype=torch.float8_e4m3fn), fp8_compute=1))[0] == OK
+    assert _shapes(_params(_case(D=128, kv_dtype=torch.float8_e4m3fn), fp8_compute=0))[0] == OK
+    for c, v in ((_case(D=128), 1), (_case(D=64, kv_dtype=torch.float8_e4m3fn), 1),
+                 (_case(D=128, kv_dtype=torch.float8_e4m3fn), 2), (_case(D=128, kv_dtype=torch.float8_e4m3fn), -1)):
+        st, msg = _shapes(_params(c, fp8_compute=v))
+        assert st == ERR["PPA_ERR_DTYPE"] and msg, (v, st, msg)
+
+
 SHAPE_DEFECTS = [
     # (name, overrides of ppa_params, expected status)
     ("abi version", dict(abi_version=99), "PPA_ERR_ABI"),

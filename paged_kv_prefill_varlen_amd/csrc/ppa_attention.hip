@@ -779,9 +779,15 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     __builtin_amdgcn_sched_barrier(0);
   };
   i32x8 pf8;
+  // fp8 path: row sums of the rounded weights, as an MFMA of P against an
+  // all-ones operand (e4m3fn 1.0 = 0x38): every element of lane (row, half)
+  // is the row's sum over the tile's 64 keys, exact in fp32
+  f32x16 lacc = {};
+  const int ones8 = 0x38383838;
   auto gemm_pv = [&](int j) {
     if constexpr (T::F8MMA) {
       for (int md = 0; md < MD; ++md) oacc[md] = mfma32_fp8(vf8[md], pf8, oacc[md]);
+      lacc = mfma32_fp8(i32x8{ones8, ones8, ones8, ones8, ones8, ones8, ones8, ones8}, pf8, lacc);
       return;
     }
     for (int ks = 0; ks < 4; ++ks)
@@ -813,14 +819,14 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
       m_run = m_new;
       l_part *= alpha;
       for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
+      if constexpr (T::F8MMA) lacc *= alpha;
     }
     const float mb = m_run == kNegInf ? 0.f : m_run;
     if constexpr (T::F8MMA) {
       // P as e4m3fn codes (p <= 2^8 with the lazy maximum: within range),
-      // byte 16 mt + v = element v of sacc[mt]; the row sum adds the
-      // weights decoded back from those codes, so that the numerator and
+      // byte 16 mt + v = element v of sacc[mt].  The row sums come from the
+      // PV step (an MFMA of these codes against ones), so the numerator and
       // the denominator see the same rounded weights
-      float sum = l_part;
       for (int mt = 0; mt < 2; ++mt)
         for (int q = 0; q < 4; ++q) {
           float p[4];
@@ -828,11 +834,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
           int code = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
           code = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], code, true);
           pf8[4 * mt + q] = code;
-          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
-          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(code, true);
-          sum += (lo[0] + lo[1]) + (hi[0] + hi[1]);
         }
-      l_part = sum;
       return;
     }
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -914,7 +916,8 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
 
   // ---- epilogue -------------------------------------------------------------
   if (!wave_active) return;
-  float l = pair_sum(l_part);
+  // (the fp8 path's sums already cover both lane halves' keys)
+  float l = T::F8MMA ? lacc[0] : pair_sum(l_part);
   if (!rvalid) return;
   const int h = h0 + hd;
   const float mb = m_run == kNegInf ? 0.f : m_run;

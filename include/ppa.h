@@ -252,9 +252,11 @@ typedef struct ppa_params {
   float o_sf_scale;
   int32_t o_sf_vec_size;
 
-  /* Arithmetic for an fp8 cache (TensorRT-LLM attention-backend article,
-     the fp8 KV cache and its fp8 context attention; BASELINE's long-prefix
-     fp8 workload folds the per-tensor scales into bmm1_scale / bmm2_scale).
+  /* Arithmetic for an fp8 cache.  The TokenSpeed backend source casts Q to
+     e4m3fn before the call whenever its KV cache is fp8 (its Q-preparation
+     step), with q_scale 1 folded into bmm1_scale (its scale computation);
+     here Q stays bf16 at the boundary and the kernel may do that rounding
+     itself.
        0  each e4m3fn code is widened to bf16 (exact) and both products run
           on the bf16 MFMA; Q and the softmax weights stay bf16
        1  head_dim 128 only: Q (after the sign of bmm1_scale) and the

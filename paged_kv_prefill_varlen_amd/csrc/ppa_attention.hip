@@ -650,6 +650,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   pt.page_shift = a.page_shift;
   const int page_mask = (1 << a.page_shift) - 1;
   uint32_t kraw[T::K_DW], vraw[T::V_DW];
+  uint32_t kraw2[T::F8MMA ? T::K_DW : 1], vraw2[T::F8MMA ? T::V_DW : 1];   // fp8 MFMA: second tile of a pair
   int id_next = 0;   // page id of the wave's keys in the next tile to fetch
 
   const int krow_lane = swap_bits23(col);
@@ -689,7 +690,15 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   // copy the wave's 8 keys of tile j into registers; `id` is their page id
   // LDS stage of tile j
   auto stage = [&](int j) { return T::DMA ? (j - tile_lo) & 3 : (j - tile_lo) & 1; };
-  auto stage_fetch = [&](int j, int id) {
+  // fp8 MFMA: four 16 KB stages (8 KB of K codes, then 8 KB of V^T codes),
+  // one in each of the four 16 KB bf16 stage buffers; stage s of tile j is
+  // (j - lo) mod 4
+  auto f8k = [&](int j) {
+    const int st = (j - tile_lo) & 3;
+    return st < 2 ? klds[st] : vlds[st - 2];
+  };
+  auto f8v = [&](int j) { return f8k(j) + 4096; };
+  auto stage_fetch = [&](int j, int id, bool second = false) {
     const int kb = j * kBK + 8 * wave;
     const bool fast = UPAGE && j * kBK + kBK <= kv_len;
     if constexpr (T::DMA) {
@@ -697,13 +706,19 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
       if (fast) fetch_kv_lds<D, true>(klds[st], vlds[st], a, pt, id, hk, kb, kv_len, page_mask, wave, lane);
       else fetch_kv_lds<D, false>(klds[st], vlds[st], a, pt, id, hk, kb, kv_len, page_mask, wave, lane);
     } else {
-      if (fast) fetch_kv<D, FP8, true>(kraw, vraw, a, pt, id, hk, kb, kv_len, page_mask, lane);
-      else fetch_kv<D, FP8, false>(kraw, vraw, a, pt, id, hk, kb, kv_len, page_mask, lane);
+      uint32_t* kr = T::F8MMA && second ? kraw2 : kraw;
+      uint32_t* vr = T::F8MMA && second ? vraw2 : vraw;
+      if (fast) fetch_kv<D, FP8, true>(kr, vr, a, pt, id, hk, kb, kv_len, page_mask, lane);
+      else fetch_kv<D, FP8, false>(kr, vr, a, pt, id, hk, kb, kv_len, page_mask, lane);
     }
   };
-  auto stage_store = [&](int j) {
-    const int buf = stage(j);
-    store_kv<D, FP8, F8M>(kraw, vraw, klds[buf], vlds[buf], wave, lane);
+  auto stage_store = [&](int j, bool second = false) {
+    if constexpr (T::F8MMA) {
+      store_kv<D, FP8, F8M>(second ? kraw2 : kraw, second ? vraw2 : vraw, f8k(j), f8v(j), wave, lane);
+    } else {
+      const int buf = stage(j);
+      store_kv<D, FP8, F8M>(kraw, vraw, klds[buf], vlds[buf], wave, lane);
+    }
   };
   // S operand, direct-copy layout: lane (col, half) reads K rows krow_lane
   // (+ 32) at chunk 2 s + half, whose slot is (2 s + half) ^ kswz(row); the
@@ -713,7 +728,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     if constexpr (T::F8MMA) {
       // K operand: row krow_lane (+ 32), bytes 64 c + 32 half .. + 31, i.e.
       // 16-byte chunks 4 c + 2 half (+ 1) in slots chunk ^ ((row / 2) mod 8)
-      const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(klds[stage(j)]);
+      const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(f8k(j));
       i32x8 kf8[2][2];
       for (int mt = 0; mt < 2; ++mt)
         for (int cc = 0; cc < 2; ++cc) {
@@ -751,7 +766,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
       // V^T operand: dim row md*32 + col, key bytes 32 half .. + 31 (the
       // order P's bytes take), 16-byte chunks 2 half (+ 1) in slots
       // chunk ^ ((dim / 4) mod 4)
-      const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(vlds[stage(j)]);
+      const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(f8v(j));
       for (int md = 0; md < MD; ++md) {
         const int m = md * 32 + col;
         const int sw = (m >> 2) & 3;
@@ -890,6 +905,37 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
         softmax(j + 1);
         gemm_pv(j + 1);
       }
+    }
+  } else if (T::F8MMA && tile_lo <= tile_hi) {
+    // fp8 MFMA: four-stage ring, two tiles per barrier; tiles j + 2, j + 3
+    // are fetched into registers before tiles j, j + 1 are computed and
+    // stored after them into the stages of j - 2, j - 1, which every wave
+    // finished reading before the previous barrier
+    const int lo = tile_lo, hi = tile_hi;
+    stage_fetch(lo, page_of(lo));
+    if (lo + 1 <= hi) stage_fetch(lo + 1, page_of(lo + 1), true);
+    stage_store(lo);
+    if (lo + 1 <= hi) stage_store(lo + 1, true);
+    __syncthreads();
+    for (int j = lo; j <= hi; j += 2) {
+      const bool m2 = j + 2 <= hi, m3 = j + 3 <= hi;
+      if (m2) stage_fetch(j + 2, page_of(j + 2));
+      if (m3) stage_fetch(j + 3, page_of(j + 3), true);
+      if (wave_tile(j)) {
+        gemm_s(j);
+        read_v(j);
+        softmax(j);
+        gemm_pv(j);
+      }
+      if (j + 1 <= hi && wave_tile(j + 1)) {
+        gemm_s(j + 1);
+        read_v(j + 1);
+        softmax(j + 1);
+        gemm_pv(j + 1);
+      }
+      if (m2) stage_store(j + 2);
+      if (m3) stage_store(j + 3, true);
+      __syncthreads();
     }
   } else if (tile_lo <= tile_hi) {
     const int lo = tile_lo, hi = tile_hi;

@@ -128,6 +128,98 @@ def device_info(torch, dev) -> dict:
             "bf16_peak_tflops_derived": None if sclk is None else round(cus * 4096 * sclk * 1e6 / 1e12, 1)}
 
 
+def _sysfs_sclk_now():
+    """The shader clock the driver reports as current: the starred line of
+    pp_dpm_sclk (MHz), or None."""
+    import glob
+    import re
+    for path in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                        if m:
+                            return int(m.group(1))
+        except OSError:
+            continue
+    return None
+
+
+def sampled_clock(launch, seconds: float = 1.5):
+    """The shader clock held under sustained load: the kernel is launched
+    back to back for about `seconds` while a host thread samples the
+    driver's current-clock readout every 5 ms (sysfs pp_dpm_sclk, the
+    starred level).  Returns {median, min, max, samples, source} or None
+    when the readout is not available."""
+    import threading
+    import torch
+    samples = []
+    stop = threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            v = _sysfs_sclk_now()
+            if v is not None:
+                samples.append(v)
+            time.sleep(0.005)
+
+    th = threading.Thread(target=sample, daemon=True)
+    t_end = time.perf_counter() + seconds
+    th.start()
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            launch()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    # the first samples can predate the ramp to load
+    tail = samples[len(samples) // 4:] or samples
+    return {"median_mhz": float(np.median(tail)), "min_mhz": int(min(tail)), "max_mhz": int(max(tail)),
+            "samples": len(tail), "source": "sysfs pp_dpm_sclk current level, sampled every 5 ms under "
+                                             "back-to-back launches"}
+
+
+def time_config(config: str, steps: int, warmup: int) -> dict:
+    """A second workload timed like the headline one (launches back to back,
+    HIP events at the two ends of the region), for the extra keys of the
+    bench line."""
+    import torch
+
+    import paged_kv_prefill_varlen_amd as ppa
+    from workloads import make_case
+
+    dev = torch.device("cuda:0")
+    case = make_case(config)
+    q = case["query"].to(dev)
+    kv = case["kv_cache"]
+    kv = tuple(t.to(dev) for t in kv) if isinstance(kv, tuple) else kv.to(dev)
+    out = torch.empty_like(q)
+    ws = torch.zeros(ppa.WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    p = ppa.make_params(q, kv, ws, case["block_tables"].to(dev), case["seq_lens"].to(dev), case["max_q_len"],
+                        case["max_kv_len"], case["bmm1_scale"], case["bmm2_scale"], case["batch_size"],
+                        case["cum_seq_lens_q"].to(dev), case["cum_seq_lens_kv"].to(dev), case["window_left"], out,
+                        case["kv_layout"], None if case["sinks"] is None else case["sinks"].to(dev))
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        ppa.ppa_paged_prefill_attention(p, stream.cuda_stream)
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        ppa.ppa_paged_prefill_attention(p, stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    flops = 4.0 * case["head_dim"] * case["num_qo_heads"] * causal_pairs(case)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": WORKLOAD_TEXT[config], "kernel_ms": round(ms, 5), "causal_gflop": round(flops / 1e9, 3),
+            "tflops": round(tf, 3), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "tokens_per_s": round(sum(case["q_lens"]) / (ms * 1e-3), 1), "steps": steps}
+
+
 def cpu_baseline(case, budget_s: float = 12.0):
     """Time the CPU oracle (as it stands) on whole passes over the same batch,
     repeated until about budget_s of work; report causal TFLOP/s."""
@@ -408,6 +500,10 @@ def main():
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "mxfp4"],
                     help="output: bf16, or MXFP4 codes + E8M0 block scales")
     ap.add_argument("--o-sf-vec-size", type=int, default=32, choices=[16, 32])
+    ap.add_argument("--clock-seconds", type=float, default=1.5,
+                    help="seconds of back-to-back launches while sampling the shader clock (0: skip)")
+    ap.add_argument("--no-llama3", dest="also_llama3", action="store_false",
+                    help="chunked workload: skip timing the Llama-3-8B-shaped batch as well")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=4, metavar="DIR",
@@ -524,6 +620,11 @@ def main():
         cold_ms = float(np.median(cold))
         del scratch
 
+    # the shader clock held under sustained launches of the same call
+    clock = None
+    if args.clock_seconds > 0:
+        clock = sampled_clock(lambda: ppa.ppa_paged_prefill_attention(p, handle), args.clock_seconds)
+
     flops = 4.0 * case["head_dim"] * case["num_qo_heads"] * causal_pairs(case)
     tokens = sum(case["q_lens"])
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -583,6 +684,20 @@ def main():
         "cpu_baseline": None,
         "device": device_info(torch, dev),
     }
+    # peak and fraction at the clock the part held, beside the spec clock
+    # (2.4 GHz) that `peak` uses
+    if clock is not None and roof["bound"] == "mfma":
+        peak_measured = peak * clock["median_mhz"] / 2400.0
+        roof["measured_sclk_mhz"] = clock["median_mhz"]
+        roof["peak_at_measured_clock"] = round(peak_measured, 1)
+        roof["frac_at_measured_clock"] = round(kernel_tflops / peak_measured, 4)
+    line["clock"] = clock
+    # the other reading of the gate's "config 2": the Llama-3-8B-shaped batch
+    if args.config == "chunked" and args.also_llama3:
+        line["llama3_8b"] = time_config("llama3_8b", max(5, args.steps // 2), 3)
+        if clock is not None:
+            line["llama3_8b"]["frac_at_measured_clock"] = round(
+                line["llama3_8b"]["tflops"] / (PEAK_BF16_TFLOPS * clock["median_mhz"] / 2400.0), 4)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(line), flush=True)

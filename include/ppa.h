@@ -23,8 +23,15 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers unless a parameter says "host".
- *     The caller owns every buffer; the library allocates nothing and keeps
- *     no state between calls.
+ *     The caller owns every buffer; the library allocates nothing.  The only
+ *     state it keeps between calls is a per-device cache of the occupancy
+ *     query that sizes the persistent launch (filled on first use, guarded
+ *     against concurrent first calls).
+ *   - Metadata arrays are bare pointers, so their lengths cannot be checked
+ *     here: cum_seq_lens_q, cum_seq_lens_kv and kv_indptr must hold at least
+ *     batch_size + 1 entries, seq_lens and kv_last_page_len at least
+ *     batch_size, block_tables at least batch_size rows.  Shorter arrays are
+ *     read past their end (the Python binding checks these lengths).
  *   - Strides are in ELEMENTS of the tensor they describe.  The innermost
  *     (head_dim) stride must be 1.  The stride of a dimension of size 1 is
  *     ignored.

@@ -462,6 +462,45 @@ def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+def _check_metadata(query, kv_cache, workspace_buffer, block_tables, seq_lens, cum_seq_lens_q, cum_seq_lens_kv,
+                    kv_indptr, kv_indices, kv_last_page_len, out, sinks, lse, batch_size: int) -> None:
+    """Every tensor on query's device, and every metadata array long enough
+    for batch_size requests.  The kernel and the host checker read
+    cum_seq_lens_q[b + 1], seq_lens[b], a block-table row or kv_indptr[b + 1]
+    for every b < batch_size; the C ABI takes bare pointers and cannot see
+    their lengths, so they are checked here."""
+    B = int(batch_size)
+    csr = kv_indptr is not None or kv_indices is not None
+    if B < 0:
+        raise ValueError(f"batch_size must be >= 0, got {B}")
+    dev = query.device
+    tensors = [("seq_lens", seq_lens), ("cum_seq_lens_q", cum_seq_lens_q), ("cum_seq_lens_kv", cum_seq_lens_kv),
+               ("block_tables", block_tables), ("kv_indptr", kv_indptr), ("kv_indices", kv_indices),
+               ("kv_last_page_len", kv_last_page_len), ("workspace_buffer", workspace_buffer), ("lse", lse)]
+    if isinstance(kv_cache, (tuple, list)):
+        tensors += [(f"kv_cache[{i}]", t) for i, t in enumerate(kv_cache) if isinstance(t, torch.Tensor)]
+    else:
+        tensors.append(("kv_cache", kv_cache))
+    if isinstance(out, torch.Tensor):
+        tensors.append(("out", out))
+    elif isinstance(out, MxFp4Output):
+        tensors += [("out.data", out.data), ("out.scale", out.scale)]
+    if isinstance(sinks, torch.Tensor):
+        tensors.append(("sinks", sinks))
+    for name, t in tensors:
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, query on {dev}: every tensor must be on one device")
+    need = [("seq_lens", seq_lens, B), ("cum_seq_lens_q", cum_seq_lens_q, B + 1),
+            ("cum_seq_lens_kv", cum_seq_lens_kv, B + 1)]
+    if csr:
+        need += [("kv_indptr", kv_indptr, B + 1), ("kv_last_page_len", kv_last_page_len, B)]
+    for name, t, n in need:
+        if t is not None and t.numel() < n:
+            raise ValueError(f"{name} has {t.numel()} entries; batch_size {B} needs at least {n}")
+    if not csr and block_tables is not None and block_tables.dim() == 2 and block_tables.shape[0] < B:
+        raise ValueError(f"block_tables has {block_tables.shape[0]} rows; batch_size {B} needs at least {B}")
+
+
 def make_params(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.Tensor],
                 block_tables: Optional[torch.Tensor], seq_lens: torch.Tensor, max_q_len: int, max_kv_len: int,
                 bmm1_scale, bmm2_scale, batch_size: int, cum_seq_lens_q: torch.Tensor,
@@ -474,11 +513,13 @@ def make_params(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.
     list).  With kv_indptr / kv_indices the flat (CSR) page table is used and
     block_tables may be None.  Keeps no reference to the tensors: the caller
     keeps them alive."""
+    if query.dim() != 3:
+        raise ValueError("query must be [num_tokens, num_qo_heads, head_dim]")
+    _check_metadata(query, kv_cache, workspace_buffer, block_tables, seq_lens, cum_seq_lens_q, cum_seq_lens_kv,
+                    kv_indptr, kv_indices, kv_last_page_len, out, sinks, lse, batch_size)
     p = PpaParams()
     p.abi_version = PPA_ABI_VERSION
     p.struct_size = ctypes.sizeof(PpaParams)
-    if query.dim() != 3:
-        raise ValueError("query must be [num_tokens, num_qo_heads, head_dim]")
     p.query = _ptr(query)
     p.query_dtype = _dt(query)
     p.num_tokens, p.num_qo_heads, p.head_dim = (int(x) for x in query.shape)

@@ -44,6 +44,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "ppa.h"
 #include "ppa_internal.h"
 #include "ppa_page_addr.hpp"
@@ -68,6 +70,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kMinScale = 1.17549435e-38f;  // FLT_MIN
+// fp8 arithmetic (fp8_compute): the fewest keys every row of a work item
+// must see for the item to run on the fp8 MFMA
+constexpr int kFp8MinKeys = 1024;
 
 // Scheduler counters in the workspace: kSchedQueues queue heads, then the
 // number of workgroups that have finished.
@@ -618,20 +623,6 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
       }
     }
   };
-  // direct-copy path: Q is loaded after the first tile's copies are issued
-  // (below), and both are waited for together, so that no later compiler
-  // wait for Q covers the prefetched tiles
-  if constexpr (T::F8MMA) load_q8();
-  else if constexpr (!T::DMA) load_q();
-  // the row's sink logit, read now so that the epilogue does not wait for it
-  const float sink = a.sinks ? a.sinks[h0 + (rvalid ? hd : 0)] : 0.f;
-
-  f32x16 oacc[MD];
-  for (int md = 0; md < MD; ++md) oacc[md] = f32x16{};
-  float m_run = kNegInf, l_part = 0.f;
-  f32x16 sacc[2];
-  bf16x8 pb[4];
-
   // ---- K/V tile range of the workgroup -------------------------------------
   const int pos_first = prefix + t0;
   const int pos_last = prefix + t0 + ntok - 1;
@@ -645,6 +636,35 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     tile_lo = first + (split * n) / S;
     tile_hi = first + ((split + 1) * n) / S - 1;
   }
+  if constexpr (T::F8MMA) {
+    // Rounding each softmax weight to e4m3fn (relative error up to 2^-4)
+    // averages out only over many keys: an item runs on the fp8 MFMA only
+    // when every one of its rows sees at least kFp8MinKeys keys inside the
+    // item's key range (the keys common to all of its rows, so a lower
+    // bound for each); otherwise it takes the widened-bf16 arithmetic.
+    const int chunk_lo = tile_lo * kBK;
+    const int chunk_hi = tile_hi * kBK + kBK - 1 < kv_len - 1 ? tile_hi * kBK + kBK - 1 : kv_len - 1;
+    const int common_lo = W >= 0 ? (pos_last - W > chunk_lo ? pos_last - W : chunk_lo) : chunk_lo;
+    const int common_hi = pos_first < chunk_hi ? pos_first : chunk_hi;
+    if (common_hi - common_lo + 1 < kFp8MinKeys) {
+      attend_item<D, FP8, UPAGE, false>(a, item);
+      return;
+    }
+  }
+
+  // direct-copy path: Q is loaded after the first tile's copies are issued
+  // (below), and both are waited for together, so that no later compiler
+  // wait for Q covers the prefetched tiles
+  if constexpr (T::F8MMA) load_q8();
+  else if constexpr (!T::DMA) load_q();
+  // the row's sink logit, read now so that the epilogue does not wait for it
+  const float sink = a.sinks ? a.sinks[h0 + (rvalid ? hd : 0)] : 0.f;
+
+  f32x16 oacc[MD];
+  for (int md = 0; md < MD; ++md) oacc[md] = f32x16{};
+  float m_run = kNegInf, l_part = 0.f;
+  f32x16 sacc[2];
+  bf16x8 pb[4];
 
   pt.num_pages = a.num_pages;
   pt.page_shift = a.page_shift;
@@ -966,7 +986,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   float l = T::F8MMA ? lacc[0] : pair_sum(l_part);
   if (!rvalid) return;
   const int h = h0 + hd;
-  const float mb = m_run == kNegInf ? 0.f : m_run;
+  float mb = m_run == kNegInf ? 0.f : m_run;
   const int64_t trow = q0 + t0 + tok;
   if (S > 1) {
     // partial state of this key chunk (no sink; a row with no key here
@@ -984,9 +1004,20 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     if (half == 0) a.lse_part[prow] = l > 0.f ? mb * kLn2 + __builtin_logf(l) : kNegInf;
     return;
   }
-  if (a.sinks) l += __builtin_amdgcn_exp2f(sink * kLog2e - mb);
+  // the sink joins the denominator relative to max(running max, sink), so
+  // that a sink far above every logit gives l ~ 1 and lse ~ sink instead of
+  // an infinite l; O is scaled by the same factor (1 when the sink is below
+  // the running maximum, and for a -inf sink)
+  float oscale = 1.f;
+  if (a.sinks) {
+    const float s2 = sink * kLog2e;
+    const float m2 = s2 > mb ? s2 : mb;
+    oscale = __builtin_amdgcn_exp2f(mb - m2);
+    l = l * oscale + __builtin_amdgcn_exp2f(s2 - m2);
+    mb = m2;
+  }
   if (a.lse != nullptr && half == 0) a.lse[trow * a.lse_tok + static_cast<int64_t>(h) * a.lse_head] = mb * kLn2 + __builtin_logf(l);
-  const float inv = bmm2 / l;
+  const float inv = (bmm2 * oscale) / l;
   if (a.out_mx != 0) {
     uint8_t* orow8 = reinterpret_cast<uint8_t*>(a.out) + trow * a.o_tok + static_cast<int64_t>(h) * a.o_head;
     uint8_t* sfrow = a.out_sf + trow * a.sf_tok + static_cast<int64_t>(h) * a.sf_head;
@@ -1199,19 +1230,23 @@ hipError_t launch_merge(const MergeArgs& m, int head_dim, hipStream_t stream) {
 
 // Workgroups of a persistent kernel that the device holds at once (cached per
 // device and kernel).
+// The cache is the library's only state: atomic slots, so concurrent first
+// calls on one device at worst run the query twice and store the same value.
 template <int D, bool FP8, bool UPAGE, bool F8M>
 int resident_workgroups() {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] > 0) return cache[dev];
+  const int known = cache[dev].load(std::memory_order_relaxed);
+  if (known > 0) return known;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, paged_prefill_persistent<D, FP8, UPAGE, F8M>,
                                                    64 * kWaves, 0) != hipSuccess)
     return 0;
-  cache[dev] = cus * (per_cu > 0 ? per_cu : 1);
-  return cache[dev];
+  const int value = cus * (per_cu > 0 ? per_cu : 1);
+  cache[dev].store(value, std::memory_order_relaxed);
+  return value;
 }
 
 template <int D, bool FP8, bool UPAGE, bool F8M>

@@ -553,39 +553,105 @@ def pin_e4m3fn_encode():
 def pin_append_then_gather():
     """Appended tokens are what a page gather reads back at their sequence
     positions (bf16: the new values; fp8: the encoded x / scale), tokens with
-    a negative slot are skipped, and every other slot keeps its contents."""
-    case = _tiny(902, q_lens=(5, 3), prefix_lens=(7, 2), batch=2, page_size=4, kv_layout="NHD")
+    a negative slot are skipped, and every other slot keeps its contents.
+    Checked for both page layouts, split and combined caches: the cache is
+    read back by the oracle's gather (the plain token-major copy of the
+    VanillaAttention path), which indexes HND pages as [head, slot] and NHD
+    pages as [slot, head] on its own."""
     rng = np.random.default_rng(903)
-    P = case["page_size"]
-    for kv_dtype, scale in (("bf16", 1.0), ("fp8_e4m3fn", 0.37)):
-        planes = [rng.integers(0, 1 << (16 if kv_dtype == "bf16" else 8),
-                               size=tuple(case["kv_cache"][0].shape)).astype(
-            np.uint16 if kv_dtype == "bf16" else np.uint8) for _ in range(2)]
-        n = sum(case["q_lens"])
-        k_new = torch.randn(n, 2, 8).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-        v_new = torch.randn(n, 2, 8).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-        bt = case["block_tables"].numpy()
-        slots, t = [], 0
-        for b, (q, kv) in enumerate(zip(case["q_lens"], case["kv_lens"])):
-            for i in range(q):
-                pos = kv - q + i
-                slots.append(int(bt[b, pos // P]) * P + pos % P)
-        slots = np.array(slots)
-        slots[2] = -1                      # skipped
-        out = OA.append_paged_kv(planes, "NHD", P, k_new, v_new, slots, kv_dtype, scale, scale)
-        for kv_idx, new in ((0, k_new), (1, v_new)):
-            changed = np.zeros(planes[kv_idx].shape, dtype=bool)
-            for i, loc in enumerate(slots):
-                if loc < 0:
-                    continue
-                got = out[kv_idx][loc // P, loc % P]
+    for n, (layout, form) in enumerate((("NHD", "split"), ("HND", "split"), ("HND", "combined"),
+                                        ("NHD", "combined"))):
+        case = _tiny(902 + 7 * n, q_lens=(5, 3), prefix_lens=(7, 2), batch=2, page_size=4, kv_layout=layout,
+                     num_qo_heads=6, num_kv_heads=3)
+        P = case["page_size"]
+        Hkv = case["num_kv_heads"]
+        pool_shape = tuple(case["kv_cache"][0].shape)
+        for kv_dtype, scale in (("bf16", 1.0), ("fp8_e4m3fn", 0.37)):
+            code_t = np.uint16 if kv_dtype == "bf16" else np.uint8
+            planes = [rng.integers(0, 1 << (16 if kv_dtype == "bf16" else 8), size=pool_shape).astype(code_t)
+                      for _ in range(2)]
+            n_new = sum(case["q_lens"])
+            k_new = torch.randn(n_new, Hkv, 8).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            v_new = torch.randn(n_new, Hkv, 8).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            bt = case["block_tables"].numpy()
+            slots, owner = [], []
+            for b, (q, kv) in enumerate(zip(case["q_lens"], case["kv_lens"])):
+                for i in range(q):
+                    pos = kv - q + i
+                    slots.append(int(bt[b, pos // P]) * P + pos % P)
+                    owner.append((b, pos))
+            slots = np.array(slots)
+            slots[2] = -1                      # skipped
+            out = OA.append_paged_kv(planes, layout, P, k_new, v_new, slots, kv_dtype, scale, scale)
+            decode = OA.decode_bf16 if kv_dtype == "bf16" else OA.decode_e4m3fn
+            if form == "split":
+                before = (decode(planes[0]), decode(planes[1]))
+                after = (decode(out[0]), decode(out[1]))
+            else:   # one tensor with the K / V planes in dim 1
+                before = decode(np.stack(planes, axis=1))
+                after = decode(np.stack(out, axis=1))
+            for kv_idx, new in ((0, k_new), (1, v_new)):
                 if kv_dtype == "bf16":
-                    assert np.array_equal(got, new[i])
+                    want_new = OA.decode_bf16(new)
                 else:
-                    x = OA.decode_bf16(new[i]).astype(np.float32) / np.float32(scale)
-                    assert np.array_equal(got, OA.encode_e4m3fn(x))
-                changed[loc // P, loc % P] = True
-            assert np.array_equal(out[kv_idx][~changed], planes[kv_idx][~changed])
+                    want_new = OA.decode_e4m3fn(OA.encode_e4m3fn(
+                        OA.decode_bf16(new).astype(np.float32) / np.float32(scale)))
+                for b, kv in enumerate(case["kv_lens"]):
+                    got = OA.gather_paged_kv(after, bt[b], kv_idx, kv, P, layout)
+                    old = OA.gather_paged_kv(before, bt[b], kv_idx, kv, P, layout)
+                    written = np.zeros(kv, dtype=bool)
+                    for i, (ob, pos) in enumerate(owner):
+                        if ob != b or slots[i] < 0:
+                            continue
+                        assert _same(got[pos], want_new[i]), (layout, form, kv_dtype, kv_idx, b, pos)
+                        written[pos] = True
+                    assert _same(got[~written], old[~written]), (layout, form, kv_dtype, kv_idx, b)
+                # slots no request reaches keep their codes
+            for kv_idx in range(2):
+                changed = np.zeros(planes[kv_idx].shape, dtype=bool)
+                for loc in slots:
+                    if loc < 0:
+                        continue
+                    if layout == "HND":
+                        changed[loc // P, :, loc % P] = True
+                    else:
+                        changed[loc // P, loc % P] = True
+                assert np.array_equal(out[kv_idx][~changed], planes[kv_idx][~changed]), (layout, form, kv_dtype)
+
+
+def pin_attention_rows_match_the_batched_call():
+    """The row-sampling entry (used to check full-size runs one (token, q
+    head) pair at a time) gives, for every row of tiny batches, what the
+    batched call gives and what the key-by-key brute force gives: padded and
+    flat page tables, empty requests (repeated cum_seq_lens_q entries),
+    window with sinks, GQA groups of 1, 2 and 3, both layouts."""
+    variants = [
+        dict(),
+        dict(num_qo_heads=3, num_kv_heads=3, q_lens=(4, 0, 2), prefix_lens=(0, 5, 1)),
+        dict(num_qo_heads=6, num_kv_heads=2, window_left=2, sinks=True, page_size=2),
+        dict(q_lens=(0, 3, 0, 4), prefix_lens=(2, 1, 0, 6), batch=4, kv_layout="NHD", kv_form="combined",
+             window_left=3, sinks=True),
+        dict(q_lens=(6, 0, 2), prefix_lens=(1, 3, 9), flat=True),
+    ]
+    for n, var in enumerate(variants):
+        var = dict(var)
+        flat = var.pop("flat", False)
+        case = _tiny(950 + n, **var)
+        if flat:
+            case = to_flat_page_table(case, slack=2, lead=3, seed=951)
+        full, written = _run(case)
+        brute = None if flat else _brute_force(case)
+        a = oracle_inputs(case)
+        cu = case["cum_seq_lens_q"].numpy()
+        rows = [(t, h) for t in range(int(cu[-1])) for h in range(case["num_qo_heads"])]
+        got = OA.attention_rows(rows=rows, **a)
+        for r, (t, h) in enumerate(rows):
+            assert written[t], (var, t)
+            err = np.max(np.abs(got[r] - full[t, h]))
+            assert err <= 1e-12, f"attention_rows != batched call {var} row {(t, h)}: {err}"
+            if brute is not None:
+                err = np.max(np.abs(got[r] - brute[t, h]))
+                assert err <= 1e-12, f"attention_rows != brute force {var} row {(t, h)}: {err}"
 
 
 # --------------------------------------------------------------------------
@@ -733,4 +799,5 @@ ALL_PINS = [
     pin_merge_identities,
     pin_e4m3fn_encode,
     pin_append_then_gather,
+    pin_attention_rows_match_the_batched_call,
 ]

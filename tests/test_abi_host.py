@@ -601,3 +601,73 @@ def test_plan_without_workspace_or_with_bad_params():
     with pytest.raises(B.PpaError) as e:
         B.ppa_plan_kv_splits(_params(c, head_dim=96))
     assert e.value.status == ERR["PPA_ERR_HEAD_DIM"]
+
+
+# --------------------------------------------------------------------------
+# metadata lengths and devices (checked by the binding: the C ABI takes bare
+# pointers and reads batch_size + 1 offsets, batch_size lengths and
+# batch_size table rows)
+# --------------------------------------------------------------------------
+
+def _short(t, n):
+    return t[:n].clone()
+
+
+def test_make_params_rejects_short_metadata():
+    c = _case()   # batch of 3
+    args = lambda **o: dict(dict(query=c["q"], kv_cache=c["kv"], workspace_buffer=None, block_tables=c["bt"],
+                                 seq_lens=c["sl"], max_q_len=c["max_q"], max_kv_len=c["max_kv"], bmm1_scale=0.125,
+                                 bmm2_scale=1.0, batch_size=c["B"], cum_seq_lens_q=c["cuq"],
+                                 cum_seq_lens_kv=c["cukv"], window_left=-1, out=c["out"], kv_layout=c["layout"]),
+                            **o)
+    B.make_params(**args())   # the full-length arrays pass
+    for name, bad in (("seq_lens", _short(c["sl"], 2)), ("cum_seq_lens_q", _short(c["cuq"], 3)),
+                      ("cum_seq_lens_kv", _short(c["cukv"], 3)), ("block_tables", _short(c["bt"], 2))):
+        with pytest.raises(ValueError, match=name):
+            B.make_params(**args(**{name: bad}))
+    # a batch_size larger than the arrays: the reading ASan flagged in the
+    # host checker before this check existed
+    with pytest.raises(ValueError):
+        B.make_params(**args(batch_size=4))
+    with pytest.raises(ValueError, match="batch_size"):
+        B.make_params(**args(batch_size=-1))
+    ptr, idx, last = _csr(c)
+    B.make_params(**args(block_tables=None, kv_indptr=ptr, kv_indices=idx, kv_last_page_len=last))
+    with pytest.raises(ValueError, match="kv_indptr"):
+        B.make_params(**args(block_tables=None, kv_indptr=_short(ptr, 3), kv_indices=idx))
+    with pytest.raises(ValueError, match="kv_last_page_len"):
+        B.make_params(**args(block_tables=None, kv_indptr=ptr, kv_indices=idx, kv_last_page_len=_short(last, 2)))
+
+
+def test_make_params_rejects_tensors_on_another_device():
+    c = _case()
+    meta = lambda t: torch.empty(t.shape, dtype=t.dtype, device="meta")
+    base = dict(query=c["q"], kv_cache=c["kv"], workspace_buffer=None, block_tables=c["bt"], seq_lens=c["sl"],
+                max_q_len=c["max_q"], max_kv_len=c["max_kv"], bmm1_scale=0.125, bmm2_scale=1.0, batch_size=c["B"],
+                cum_seq_lens_q=c["cuq"], cum_seq_lens_kv=c["cukv"], window_left=-1, out=c["out"],
+                kv_layout=c["layout"])
+    for name in ("block_tables", "seq_lens", "cum_seq_lens_q", "cum_seq_lens_kv", "out"):
+        with pytest.raises(ValueError, match="device"):
+            B.make_params(**dict(base, **{name: meta(base[name])}))
+    with pytest.raises(ValueError, match="device"):
+        B.make_params(**dict(base, kv_cache=(c["kv"][0], meta(c["kv"][1]))))
+    with pytest.raises(ValueError, match="device"):
+        B.make_params(**dict(base, workspace_buffer=torch.zeros(256, dtype=torch.uint8, device="meta")))
+
+
+def test_host_checkers_stay_inside_documented_lengths_under_asan(tmp_path):
+    """The host checkers, built with AddressSanitizer, read each metadata
+    array only within the length ppa.h documents (exact-size heap copies)."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    exe = tmp_path / "validate_bounds"
+    src = os.path.join(ROOT, "tests", "host_asan", "validate_bounds.cpp")
+    host = os.path.join(ROOT, "paged_kv_prefill_varlen_amd", "csrc", "ppa_host.cpp")
+    subprocess.run([gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer",
+                    "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "paged_kv_prefill_varlen_amd", "csrc"),
+                    src, host, "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and "ERROR: AddressSanitizer" not in r.stderr, r.stdout + r.stderr

@@ -1,10 +1,11 @@
 """GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
 
-Small and edge-case workloads are compared element by element over every
-written row; the full-size workloads are compared on sampled rows that the
-oracle computes one at a time, plus properties that hold at any size (no
-NaN, untouched guard rows).  Tolerances: bf16 output max |err| <= 2e-2 and
-mean |err| <= 2e-3; fp8 KV max |err| <= 6e-2.
+Every workload, the full-size ones included, is compared element by element
+over every written row (max and mean over all of them); the full-size
+workloads are also compared first on sampled rows that the oracle computes
+one at a time, as a fast pre-check, plus properties that hold at any size
+(no NaN, untouched guard rows).  Tolerances: bf16 output max |err| <= 2e-2
+and mean |err| <= 2e-3; fp8 KV max |err| <= 6e-2.
 """
 from __future__ import annotations
 
@@ -199,6 +200,76 @@ def test_full_size_config_sampled(name):
     assert err.max() <= tol
     if case["kv_dtype"] == "bf16":
         assert err.mean() <= 2e-3
+
+
+def oracle_by_kv_head(case):
+    """The oracle's output for a whole workload, computed one (request, kv
+    head) at a time with the oracle's own gather and per-request attention,
+    printing a line after each request so a long run shows its progress."""
+    import oracle.paged_attention as OA
+    a = oracle_inputs(case)
+    q, cu, sl = a["query"], a["cum_seq_lens_q"], a["seq_lens"]
+    Hq = q.shape[1]
+    Hkv = case["num_kv_heads"]
+    G = Hq // Hkv
+    out = np.full(q.shape, np.nan)
+    written = np.zeros(q.shape[0], dtype=bool)
+    for b in range(len(sl)):
+        q0, q1, kv_len = int(cu[b]), int(cu[b + 1]), int(sl[b])
+        if q1 == q0:
+            continue
+        pages = OA.request_pages(b, a["block_tables"], a["kv_indptr"], a["kv_indices"])
+        k = OA.gather_paged_kv(a["kv_cache"], pages, 0, kv_len, a["page_size"], a["kv_layout"])
+        v = OA.gather_paged_kv(a["kv_cache"], pages, 1, kv_len, a["page_size"], a["kv_layout"])
+        for hk in range(Hkv):
+            heads = slice(hk * G, (hk + 1) * G)
+            sinks = None if a["sinks"] is None else a["sinks"][heads]
+            out[q0:q1, heads] = OA.attention_one_request(q[q0:q1, heads], k[:, hk:hk + 1], v[:, hk:hk + 1],
+                                                         a["bmm1_scale"], a["bmm2_scale"], a["window_left"], sinks)
+        written[q0:q1] = True
+        _say(f"  oracle: request {b + 1}/{len(sl)} ({q1 - q0} rows over {kv_len} keys)")
+    return out, written
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", ["llama3_8b", "swa_sinks", "fp8_long_prefix"])
+def test_full_size_config_full(name):
+    """Every written element of the full-size workload against the oracle,
+    in the launch configuration the bench times (persistent schedule); the
+    long-prefix fp8 workload in both arithmetics (widened bf16, the default,
+    and fp8 MFMA, the bench setting)."""
+    case = make_case(name)
+    _say("full, every element:", name, "tokens", sum(case["q_lens"]))
+    d = to_device(case)
+    fp8 = case["kv_dtype"] != "bf16"
+    outs = {"default": run_gpu(d)}
+    if fp8:
+        outs["fp8_compute"] = run_gpu(d, fp8_compute=True)
+    torch.cuda.synchronize()
+    want, written = oracle_by_kv_head(case)
+    for what, out in outs.items():
+        assert guard_rows_untouched(out, written)
+        mx, mean = assert_close(out, want, written, fp8=fp8, what=f"{name} {what}")
+        _say(f"  {name} {what}: max {mx:.2e} mean {mean:.2e} over {int(written.sum()) * case['num_qo_heads']} rows")
+
+
+def test_sink_far_above_the_logits():
+    """Sinks 100 above every logit: the denominator is dominated by the sink,
+    the output tends to 0 and the log-denominator to the sink; both stay
+    finite, unsplit and split."""
+    case = make_custom_case(name="big_sink", batch=2, num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                            q_lens=(70, 33), prefix_lens=(20, 300), sinks=True, seed=612)
+    case["sinks"] = case["sinks"] + 100.0
+    want, written = run_oracle(case)
+    want_lse = run_oracle_lse(case)
+    d = to_device(case)
+    for splits in (0, 3):
+        lse = torch.full(tuple(d["query"].shape[:2]), float("nan"), dtype=torch.float32, device="cuda")
+        out = run_gpu(d, lse=lse, kv_splits=splits)
+        torch.cuda.synchronize()
+        mx, mean = assert_close(out, want, written, what=f"big sink S={splits}")
+        err = _lse_close(lse, want_lse, written, f"big sink S={splits}")
+        _say(f"  big sink S={splits}: max {mx:.2e} lse err {err:.2e}")
 
 
 # --------------------------------------------------------------------------

@@ -151,6 +151,62 @@ MUTANTS["partial_ignores_key_range"] = ("partial_state",
                                         lambda q, k, v, b1, b2, w, k0, k1: _orig_partial(q, k, v, b1, b2, w, 0,
                                                                                          k.shape[0]))
 
+_orig_append = OA.append_paged_kv
+
+
+def _rows_lookup_left(query, kv_cache, kv_layout, block_tables, seq_lens, cum_seq_lens_q, page_size,
+                      bmm1_scale, bmm2_scale, window_left, sinks, rows, kv_indptr=None, kv_indices=None):
+    # the row-sampling entry with its request lookup taken on the wrong side
+    # of the boundary: a row at the first token of a request (and every row
+    # after an empty request) is computed as a row of an earlier request
+    num_qo_heads = query.shape[1]
+    cu = np.asarray(cum_seq_lens_q)
+    res = np.empty((len(rows), query.shape[2]))
+    for n, (t, h) in enumerate(rows):
+        b = max(int(np.searchsorted(cu, t, side="left") - 1), 0)
+        q0, kv_len = int(cu[b]), int(seq_lens[b])
+        q_len = int(cu[b + 1]) - q0
+        i = min(t - q0, q_len - 1)
+        pages = OA.request_pages(b, block_tables, kv_indptr, kv_indices)
+        k = OA.gather_paged_kv(kv_cache, pages, 0, kv_len, page_size, kv_layout)
+        v = OA.gather_paged_kv(kv_cache, pages, 1, kv_len, page_size, kv_layout)
+        hk = OA._kv_head(h, num_qo_heads, k.shape[1])
+        valid = OA._valid_mask(q_len, kv_len, window_left)[i:i + 1]
+        s = bmm1_scale * (query[t:t + 1, h, :] @ k[:, hk, :].T)
+        sink = None if sinks is None else float(sinks[h])
+        res[n] = bmm2_scale * OA._softmax_weighted_sum(s, valid, v[:, hk, :], sink)[0]
+    return res
+
+
+def _append_hnd_as_nhd(planes, kv_layout, page_size, k_new_codes, v_new_codes, slot_mapping, kv_dtype,
+                       k_scale=1.0, v_scale=1.0):
+    # an HND page addressed as if its memory were [slot, head, dim]: the
+    # page reshaped instead of indexed [head, slot], so tokens land in the
+    # wrong (head, slot) cells without any shape error
+    if kv_layout != "HND":
+        return _orig_append(planes, kv_layout, page_size, k_new_codes, v_new_codes, slot_mapping, kv_dtype,
+                            k_scale, v_scale)
+    out = [np.array(p, copy=True) for p in planes]
+    for kv_idx, (new, scale) in enumerate(((k_new_codes, k_scale), (v_new_codes, v_scale))):
+        dst = out[min(kv_idx, len(out) - 1)]
+        if kv_dtype == "bf16":
+            vals = np.asarray(new, dtype=np.uint16)
+        else:
+            vals = OA.encode_e4m3fn(OA.decode_bf16(new).astype(np.float32) / np.float32(scale))
+        for i, loc in enumerate(np.asarray(slot_mapping)):
+            if loc < 0:
+                continue
+            pid, slot = int(loc) // page_size, int(loc) % page_size
+            H, P, D = dst.shape[1:]
+            page = dst[pid].reshape(P, H, D)
+            page[slot] = vals[i]
+            dst[pid] = page.reshape(H, P, D)
+    return out
+
+
+MUTANTS["rows_request_lookup_off_by_one"] = ("attention_rows", _rows_lookup_left)
+MUTANTS["append_hnd_as_nhd"] = ("append_paged_kv", _append_hnd_as_nhd)
+
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch):

@@ -26,7 +26,8 @@
  *     The caller owns every buffer; the library allocates nothing.  The only
  *     state it keeps between calls is a per-device cache of the occupancy
  *     query that sizes the persistent launch (filled on first use, guarded
- *     against concurrent first calls).
+ *     against concurrent first calls), plus the per-device scratch address of
+ *     the no-allocation entry point below.
  *   - Metadata arrays are bare pointers, so their lengths cannot be checked
  *     here: cum_seq_lens_q, cum_seq_lens_kv and kv_indptr must hold at least
  *     batch_size + 1 entries, seq_lens and kv_last_page_len at least
@@ -424,6 +425,27 @@ int32_t ppa_plan_kv_splits(const ppa_params* p);
  * and table columns are clamped, query rows are bounded by num_tokens).
  */
 int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream);
+
+/*
+ * The same call for callers that cannot allocate or own a workspace (code
+ * under HIP graph capture, serving loops that forbid hipMalloc): instead of
+ * p->workspace, which must be NULL here (else PPA_ERR_WORKSPACE), the
+ * library uses a scratch array of ppa_noalloc_scratch_bytes() (16 MiB) in
+ * device memory that it owns, one per device, held until the process ends.
+ * Calls whose ppa_workspace_bytes(p) exceeds that size (split-KV with many
+ * partial rows) return PPA_ERR_WORKSPACE.  The persistent schedule always
+ * runs; each call first clears the scheduler counters with a small kernel
+ * on `stream`.  The scratch keeps the last call's contents, and every call
+ * on one device shares it: calls that overlap in time on one device (on
+ * different streams, or from different threads) race.  Otherwise as
+ * ppa_paged_prefill_attention: no host synchronisation and no allocation
+ * (the first call on a device looks up the array's address).
+ */
+int32_t ppa_paged_prefill_attention_noalloc(const ppa_params* p, void* stream);
+
+/* Size in bytes of the per-device scratch array of the no-allocation entry
+   point. */
+size_t ppa_noalloc_scratch_bytes(void);
 
 /*
  * Combine partial attention states (see ppa_merge_params); enqueued on

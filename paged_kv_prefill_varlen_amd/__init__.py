@@ -13,6 +13,7 @@ from .binding import (PPA_ABI_VERSION, PPA_DTYPE_MXFP4, WORKSPACE_BYTES, MxFp4Ou
                       ppa_merge_attention_states, ppa_validate_append,
                       ppa_merge_params_size, PpaParams, batch_context_with_kv_cache,  # noqa: F401
                       library_path, make_params, ppa_abi_version, ppa_gather_paged_kv,
-                      ppa_paged_prefill_attention, ppa_params_size, ppa_strerror,
+                      ppa_paged_prefill_attention, ppa_paged_prefill_attention_noalloc, ppa_noalloc_scratch_bytes,
+                      ppa_params_size, ppa_strerror,
                       ppa_validate_metadata_host, ppa_validate_page_table_csr_host, ppa_validate_shapes,
                       ppa_workspace_bytes, ppa_plan_kv_splits, ppa_plan_kv_splits_model)

@@ -203,6 +203,8 @@ def _load():
         "ppa_plan_kv_splits_model": (c_int32, [c_int64, c_int64, c_int64, c_int32]),
         "ppa_plan_kv_splits": (c_int32, [P]),
         "ppa_paged_prefill_attention": (c_int32, [P, c_void_p]),
+        "ppa_paged_prefill_attention_noalloc": (c_int32, [P, c_void_p]),
+        "ppa_noalloc_scratch_bytes": (c_size_t, []),
         "ppa_gather_paged_kv": (c_int32, [P, c_int32, c_void_p, c_int64, c_void_p]),
         "ppa_merge_attention_states": (c_int32, [ctypes.POINTER(PpaMergeParams), c_void_p]),
         "ppa_merge_params_size": (c_size_t, []),
@@ -337,6 +339,21 @@ def ppa_paged_prefill_attention(params: PpaParams, stream: Union[int, "torch.cud
     if st != 0:
         _, msg = ppa_validate_shapes(params)
         raise PpaError(st, msg)
+
+
+def ppa_paged_prefill_attention_noalloc(params: PpaParams, stream: Union[int, "torch.cuda.Stream", None] = None,
+                                        device: Optional[torch.device] = None) -> None:
+    """The no-allocation entry point: params.workspace must be None; the
+    library's per-device scratch array serves as the workspace."""
+    h = _stream_handle(device or torch.device("cuda"), stream)
+    st = _lib.ppa_paged_prefill_attention_noalloc(ctypes.byref(params), c_void_p(h))
+    if st != 0:
+        _, msg = ppa_validate_shapes(params)
+        raise PpaError(st, msg)
+
+
+def ppa_noalloc_scratch_bytes() -> int:
+    return int(_lib.ppa_noalloc_scratch_bytes())
 
 
 def ppa_gather_paged_kv(params: PpaParams, kv_idx: int, dst: torch.Tensor, stream=None) -> None:
@@ -641,7 +658,8 @@ def batch_context_with_kv_cache(query: torch.Tensor, kv_cache, workspace_buffer:
                                 validate: bool = False, stream=None, kv_indptr=None, kv_indices=None,
                                 kv_last_page_len=None, lse: Optional[torch.Tensor] = None,
                                 kv_splits: Union[int, str] = 0, o_sf_scale: Optional[float] = None,
-                                o_sf_vec_size: Optional[int] = None, fp8_compute: bool = False):
+                                o_sf_vec_size: Optional[int] = None, fp8_compute: bool = False,
+                                noalloc: bool = False):
     """Batched paged prefill attention; argument list of the API page
     (without the PDL option), plus the optional flat page table (kv_indptr /
     kv_indices / kv_last_page_len) in place of block_tables, an optional fp32
@@ -654,7 +672,9 @@ def batch_context_with_kv_cache(query: torch.Tensor, kv_cache, workspace_buffer:
     32) returns an ``MxFp4Output``.  ``fp8_compute=True`` (fp8 cache,
     head_dim 128) rounds Q and the softmax weights to e4m3fn and runs both
     products on the fp8 MFMA.  ``validate=True`` also runs the deep
-    metadata check on host copies (a device-to-host sync)."""
+    metadata check on host copies (a device-to-host sync).  ``noalloc=True``
+    calls the no-allocation entry point (``workspace_buffer`` must be None:
+    the library's per-device scratch array takes its place)."""
     if isinstance(out_dtype, str):
         if out_dtype.lower() != "mxfp4":
             raise ValueError(f"out_dtype {out_dtype!r}: the FP4 output here is 'mxfp4' (OCP MX, E8M0 scales)")
@@ -681,5 +701,8 @@ def batch_context_with_kv_cache(query: torch.Tensor, kv_cache, workspace_buffer:
             st, msg = ppa_validate_page_table_csr_host(p, seq_lens, kv_indptr, kv_indices, kv_last_page_len)
         if st != 0:
             raise PpaError(st, msg)
-    ppa_paged_prefill_attention(p, stream, query.device)
+    if noalloc:
+        ppa_paged_prefill_attention_noalloc(p, stream, query.device)
+    else:
+        ppa_paged_prefill_attention(p, stream, query.device)
     return out

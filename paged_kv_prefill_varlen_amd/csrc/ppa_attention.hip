@@ -45,6 +45,7 @@
 #include <stdlib.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "ppa.h"
 #include "ppa_internal.h"
@@ -1230,8 +1231,9 @@ hipError_t launch_merge(const MergeArgs& m, int head_dim, hipStream_t stream) {
 
 // Workgroups of a persistent kernel that the device holds at once (cached per
 // device and kernel).
-// The cache is the library's only state: atomic slots, so concurrent first
-// calls on one device at worst run the query twice and store the same value.
+// The cache is the library's only state besides the no-allocation entry
+// point's scratch address: atomic slots, so concurrent first calls on one
+// device at worst run the query twice and store the same value.
 template <int D, bool FP8, bool UPAGE, bool F8M>
 int resident_workgroups() {
   static std::atomic<int> cache[64];
@@ -1396,6 +1398,65 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
   }
   return e == hipSuccess ? PPA_OK : PPA_ERR_HIP;
 }
+
+// ---- no-allocation entry point ------------------------------------------------
+// For callers that cannot allocate (graph capture, serving loops that forbid
+// hipMalloc): the workspace (the persistent schedule's counters and the
+// split-KV partial states) comes from a file-scope device array instead of
+// the caller.  Each device holds its own copy for the life of the process;
+// every call on a device shares it, so calls that overlap in time on one
+// device race.
+namespace ppa {
+namespace {
+
+constexpr size_t kScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The array's device address, looked up once per device with that device
+// current (the host-side name is only a stand-in for the symbol).
+void* scratch_address(int dev) {
+  static std::mutex lock;
+  static void* addr[64];
+  if (dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> guard(lock);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
+
+// The scheduler counters must start at zero: a fill kernel, not a memset
+// node, so that the call stays correct under graph replay.
+__global__ __launch_bounds__(64) void clear_counters(uint32_t* c) { c[threadIdx.x] = 0u; }
+
+}  // namespace
+}  // namespace ppa
+
+extern "C" int32_t ppa_paged_prefill_attention_noalloc(const ppa_params* p, void* stream) {
+  if (p == nullptr) return PPA_ERR_NULL_POINTER;
+  if (p->workspace != nullptr) return PPA_ERR_WORKSPACE;   // the library's scratch takes its place
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PPA_ERR_HIP;
+  void* ptr = scratch_address(dev);
+  if (ptr == nullptr) return PPA_ERR_HIP;
+  // the scratch stands in for the workspace: the shape check then also
+  // rejects split-KV states larger than it
+  ppa_params q = *p;
+  q.workspace = ptr;
+  q.workspace_bytes = kScratchBytes;
+  char msg[8];
+  const int32_t st = ppa_validate_shapes(&q, msg, sizeof msg);
+  if (st != PPA_OK) return st;
+  if (q.batch_size == 0 || q.max_q_len == 0 || q.num_tokens == 0) return PPA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(clear_counters, dim3(1), dim3(64), 0, s, static_cast<uint32_t*>(ptr));
+  if (hipGetLastError() != hipSuccess) return PPA_ERR_HIP;
+  return ppa_paged_prefill_attention(&q, stream);
+}
+
+extern "C" size_t ppa_noalloc_scratch_bytes(void) { return ppa::kScratchBytes; }
 
 extern "C" int32_t ppa_plan_kv_splits(const ppa_params* p) {
   if (p == nullptr) return PPA_ERR_NULL_POINTER;

@@ -15,8 +15,8 @@
 //   a K/V tile staged once in LDS serves every head of the group and the
 //   causal boundary of a 32-row MFMA tile spans only 32 / GW tokens.  Each
 //   wave owns 32 rows (one MFMA column tile); two waves share a SIMD.
-//   The grid is 1-D and ordered heaviest-first: blockIdx / R picks the query
-//   tile from the last (longest causal span) to the first, blockIdx % R picks
+//   Work items are ordered heaviest-first: item / R counts query tiles back
+//   from each request's last one (its longest causal span), item % R picks
 //   (request, kv head, head group).  With R a multiple of 8, every tile of one
 //   (request, kv head) lands on the same XCD (blocks go round-robin over the
 //   8 XCDs), so its K/V stays in one L2.
@@ -314,6 +314,9 @@ __device__ __forceinline__ void fetch_kv_lds(__bf16* kt, __bf16* vt, const AttnA
   constexpr int RPI = 64 / TPR;   // rows per copy instruction
   const uint8_t* kbase = a.k.base;
   const uint8_t* vbase = a.v.base;
+  // the lane's offsets are recomputed at every call: hoisted out of the
+  // loops that call this, they would be held in registers the whole time
+  asm volatile("" : "+v"(lane));
   if (FAST) {
     kbase += (static_cast<int64_t>(id) * a.k.page_stride + static_cast<int64_t>(hk) * a.k.head_stride) * 2;
     vbase += (static_cast<int64_t>(id) * a.v.page_stride + static_cast<int64_t>(hk) * a.v.head_stride) * 2;
@@ -506,6 +509,76 @@ __device__ __forceinline__ void store_mxfp4_row(const f32x16* oacc, float inv, f
   }
 }
 
+// Final scale of one row's O (lane; no key split): bmm2 over the softmax
+// denominator with the sink's term; writes the row's log-sum-exp when asked.
+// The sink joins the denominator relative to max(running max, sink), so that
+// a sink far above every logit gives l ~ 1 and lse ~ sink instead of an
+// infinite l; O is scaled by the same factor (1 when the sink is below the
+// running maximum, and for a -inf sink).  Contraction off, as in store_row.
+__device__ __forceinline__ float row_scale(const AttnArgs& a, float l, float m_run, float sink, int h, int64_t trow,
+                                           int half, float bmm2) {
+#pragma clang fp contract(off)
+  float mb = m_run == kNegInf ? 0.f : m_run;
+  float oscale = 1.f;
+  if (a.sinks) {
+    const float s2 = sink * kLog2e;
+    const float m2 = s2 > mb ? s2 : mb;
+    oscale = __builtin_amdgcn_exp2f(mb - m2);
+    l = l * oscale + __builtin_amdgcn_exp2f(s2 - m2);
+    mb = m2;
+  }
+  if (a.lse != nullptr && half == 0)
+    a.lse[trow * a.lse_tok + static_cast<int64_t>(h) * a.lse_head] = mb * kLn2 + __builtin_logf(l);
+  return (bmm2 * oscale) / l;
+}
+
+// Epilogue of one row (lane): the row's final output, or in split mode its
+// partial state.  l is the row's denominator over the keys it saw (both lane
+// halves), m_run its running maximum in log2 units, oacc its unnormalized O
+// (this lane's half of the dims).  Contraction is off so that every kernel
+// that inlines this rounds the same operations the same way (the persistent
+// and the one-item-per-workgroup schedules give identical bits).
+template <int D>
+__device__ __forceinline__ void store_row(const AttnArgs& a, const f32x16 (&oacc)[D / 32], float l, float m_run,
+                                          float sink, int h, int64_t trow, int split, int half, float bmm2) {
+#pragma clang fp contract(off)
+  constexpr int MD = D / 32;
+  float mb = m_run == kNegInf ? 0.f : m_run;
+  if (a.kv_splits > 1) {
+    // partial state of this key chunk (no sink; a row with no key here
+    // gets 0 and -inf): output normalized over the chunk, log-denominator
+    const float pinv = l > 0.f ? bmm2 / l : 0.f;
+    const int64_t prow = (static_cast<int64_t>(split) * a.num_tokens + trow) * a.num_qo_heads + h;
+    float* dst = a.o_part + prow * D;
+    for (int md = 0; md < MD; ++md)
+      for (int g = 0; g < 4; ++g) {
+        const int d = md * 32 + 8 * g + 4 * half;
+        typedef __attribute__((ext_vector_type(4))) float f32x4;
+        *reinterpret_cast<f32x4*>(dst + d) = f32x4{oacc[md][4 * g] * pinv, oacc[md][4 * g + 1] * pinv,
+                                                   oacc[md][4 * g + 2] * pinv, oacc[md][4 * g + 3] * pinv};
+      }
+    if (half == 0) a.lse_part[prow] = l > 0.f ? mb * kLn2 + __builtin_logf(l) : kNegInf;
+    return;
+  }
+  const float inv = row_scale(a, l, m_run, sink, h, trow, half, bmm2);
+  if (a.out_mx != 0) {
+    uint8_t* orow8 = reinterpret_cast<uint8_t*>(a.out) + trow * a.o_tok + static_cast<int64_t>(h) * a.o_head;
+    uint8_t* sfrow = a.out_sf + trow * a.sf_tok + static_cast<int64_t>(h) * a.sf_head;
+    if (a.out_mx == 16) store_mxfp4_row<D, 16>(oacc, inv, a.o_sf_scale, orow8, sfrow, half);
+    else store_mxfp4_row<D, 32>(oacc, inv, a.o_sf_scale, orow8, sfrow, half);
+    return;
+  }
+  uint16_t* orow = a.out + trow * a.o_tok + static_cast<int64_t>(h) * a.o_head;
+  for (int md = 0; md < MD; ++md) {
+    for (int g = 0; g < 4; ++g) {
+      const int d = md * 32 + 8 * g + 4 * half;
+      const u32x2 w = u32x2{pack_bf16(oacc[md][4 * g] * inv, oacc[md][4 * g + 1] * inv),
+                            pack_bf16(oacc[md][4 * g + 2] * inv, oacc[md][4 * g + 3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + d) = w;
+    }
+  }
+}
+
 // One work item: `item` = (query tile, request, kv head, head group), counted
 // heaviest query tile first.  Per K/V tile: stage tile j+1 into registers, run
 // S, softmax and PV for tile j from LDS, store tile j+1 into the other LDS
@@ -519,12 +592,14 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   __shared__ __attribute__((aligned(16))) __bf16 vlds[T::STAGES][T::V_ELEMS];
 
   // ---- which work item --------------------------------------------------
-  // item = (query tile from the last, key chunk, request, kv head, head group)
+  // item = (query tile counted from the request's last one, key chunk,
+  // request, kv head, head group): the last tiles of all requests (the
+  // longest causal spans) come first whatever the requests' lengths
   const int R = a.batch * a.num_kv_heads * a.n_hg;
   const int S = a.kv_splits;
   const int rest = item % R;
   const int split = (item / R) % S;
-  const int qt = a.n_qt - 1 - item / R / S;
+  const int qk = item / R / S;
   const int b = rest / (a.num_kv_heads * a.n_hg);
   const int hk = (rest / a.n_hg) % a.num_kv_heads;
   const int hg = rest % a.n_hg;
@@ -537,16 +612,36 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   int kv_len = ((cint32*)(a.seq_lens))[b];
   PageTable pt;
   request_table(pt, b, a.block_tables, a.bt_row_stride, a.bt_cols, a.kv_indptr, a.kv_indices, a.kv_indices_len);
+  // Without a window, the first key chunk of an item starts at tile 0, so
+  // with the padded table the page ids of the wave's keys in tiles 0..3 are
+  // known before the request's lengths: they load in the same scalar batch
+  // (raw ids, clamped when used; ids past the request's last page are read
+  // from inside the table row and never used).
+  const bool spec_ids = UPAGE && T::DMA && a.kv_indptr == nullptr && a.window_left < 0 && split == 0;
+  int sid[4] = {0, 0, 0, 0};
+  if (spec_ids) {
+    const bool empty = a.bt_cols <= 0;
+    const int last = empty ? 0 : a.bt_cols - 1;
+    cint32* row = (cint32*)(empty ? a.cu_q : pt.row);
+    const int w = uniform(static_cast<int>(threadIdx.x >> 6));
+    for (int i = 0; i < 4; ++i) {
+      int cl = (i * kBK + 8 * w) >> a.page_shift;
+      cl = cl < last ? cl : last;
+      sid[i] = row[cl];
+    }
+  }
   // every one of them is taken here, so all loads go out together: otherwise
   // the compiler sinks those used only after the early return below past
   // it, and each costs a serial round trip
-  asm volatile("" : : "s"(q0), "s"(q1), "s"(kv_len), "s"(pt.row), "s"(pt.cols));
+  asm volatile("" : : "s"(q0), "s"(q1), "s"(kv_len), "s"(pt.row), "s"(pt.cols), "s"(sid[0]), "s"(sid[1]),
+               "s"(sid[2]), "s"(sid[3]));
   q1 = q1 < a.num_tokens ? q1 : a.num_tokens;
   q0 = q0 < 0 ? 0 : (q0 < q1 ? q0 : q1);
   const int q_len = q1 - q0;
   kv_len = kv_len < 0 ? 0 : kv_len;
+  const int qt = (q_len + a.tq - 1) / a.tq - 1 - qk;
+  if (qt < 0) return;
   const int t0 = qt * a.tq;
-  if (t0 >= q_len) return;
   const int ntok = q_len - t0 < a.tq ? q_len - t0 : a.tq;
   const int prefix = kv_len - q_len;
   const int h0 = hk * a.group + hg * a.gw;
@@ -636,21 +731,6 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     const int first = tile_lo;
     tile_lo = first + (split * n) / S;
     tile_hi = first + ((split + 1) * n) / S - 1;
-  }
-  if constexpr (T::F8MMA) {
-    // Rounding each softmax weight to e4m3fn (relative error up to 2^-4)
-    // averages out only over many keys: an item runs on the fp8 MFMA only
-    // when every one of its rows sees at least kFp8MinKeys keys inside the
-    // item's key range (the keys common to all of its rows, so a lower
-    // bound for each); otherwise it takes the widened-bf16 arithmetic.
-    const int chunk_lo = tile_lo * kBK;
-    const int chunk_hi = tile_hi * kBK + kBK - 1 < kv_len - 1 ? tile_hi * kBK + kBK - 1 : kv_len - 1;
-    const int common_lo = W >= 0 ? (pos_last - W > chunk_lo ? pos_last - W : chunk_lo) : chunk_lo;
-    const int common_hi = pos_first < chunk_hi ? pos_first : chunk_hi;
-    if (common_hi - common_lo + 1 < kFp8MinKeys) {
-      attend_item<D, FP8, UPAGE, false>(a, item);
-      return;
-    }
   }
 
   // direct-copy path: Q is loaded after the first tile's copies are issued
@@ -898,10 +978,14 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     // of tiles j - 2 and j - 1 (read before it), which receive j + 2, j + 3
     const int lo = tile_lo, hi = tile_hi;
     auto clampt = [&](int j) { return j <= hi ? j : hi; };
-    const int id0 = page_of_nb(lo);
-    const int id1 = page_of_nb(clampt(lo + 1));
-    int idn0 = page_of_nb(clampt(lo + 2));
-    int idn1 = page_of_nb(clampt(lo + 3));
+    auto spec_id = [&](int i) {
+      const int id = sid[i] < 0 ? 0 : sid[i];
+      return id < pt.num_pages ? id : pt.num_pages - 1;
+    };
+    const int id0 = spec_ids ? spec_id(0) : page_of_nb(lo);
+    const int id1 = spec_ids ? spec_id(1) : page_of_nb(clampt(lo + 1));
+    int idn0 = spec_ids ? spec_id(2) : page_of_nb(clampt(lo + 2));
+    int idn1 = spec_ids ? spec_id(3) : page_of_nb(clampt(lo + 3));
     load_q();
     stage_fetch(lo, id0);
     if (lo + 1 <= hi) stage_fetch(lo + 1, id1);
@@ -986,62 +1070,70 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   // (the fp8 path's sums already cover both lane halves' keys)
   float l = T::F8MMA ? lacc[0] : pair_sum(l_part);
   if (!rvalid) return;
-  const int h = h0 + hd;
-  float mb = m_run == kNegInf ? 0.f : m_run;
-  const int64_t trow = q0 + t0 + tok;
-  if (S > 1) {
-    // partial state of this key chunk (no sink; a row with no key here
-    // gets 0 and -inf): output normalized over the chunk, log-denominator
-    const float pinv = l > 0.f ? bmm2 / l : 0.f;
-    const int64_t prow = (static_cast<int64_t>(split) * a.num_tokens + trow) * a.num_qo_heads + h;
-    float* dst = a.o_part + prow * D;
-    for (int md = 0; md < MD; ++md)
-      for (int g = 0; g < 4; ++g) {
-        const int d = md * 32 + 8 * g + 4 * half;
-        typedef __attribute__((ext_vector_type(4))) float f32x4;
-        *reinterpret_cast<f32x4*>(dst + d) = f32x4{oacc[md][4 * g] * pinv, oacc[md][4 * g + 1] * pinv,
-                                                   oacc[md][4 * g + 2] * pinv, oacc[md][4 * g + 3] * pinv};
-      }
-    if (half == 0) a.lse_part[prow] = l > 0.f ? mb * kLn2 + __builtin_logf(l) : kNegInf;
-    return;
+  store_row<D>(a, oacc, l, m_run, sink, h0 + hd, q0 + t0 + tok, split, half, bmm2);
+}
+
+// fp8 arithmetic (fp8_compute): rounding each softmax weight to e4m3fn
+// (relative error up to 2^-4) averages out only over many keys, so an item
+// runs on the fp8 MFMA only when every one of its rows sees at least
+// kFp8MinKeys keys inside the item's key range (the keys common to all its
+// rows, a lower bound for each); otherwise it takes the widened-bf16
+// arithmetic.  The item geometry follows attend_item's decode.
+__device__ __forceinline__ bool fp8_item(const AttnArgs& a, const int item) {
+  const int R = a.batch * a.num_kv_heads * a.n_hg;
+  const int S = a.kv_splits;
+  const int split = (item / R) % S;
+  const int qk = item / R / S;
+  const int b = (item % R) / (a.num_kv_heads * a.n_hg);
+  typedef const __attribute__((address_space(4))) int32_t cint32;
+  int q1 = ((cint32*)(a.cu_q))[b + 1];
+  int q0 = ((cint32*)(a.cu_q))[b];
+  int kv_len = ((cint32*)(a.seq_lens))[b];
+  q1 = q1 < a.num_tokens ? q1 : a.num_tokens;
+  q0 = q0 < 0 ? 0 : (q0 < q1 ? q0 : q1);
+  kv_len = kv_len < 0 ? 0 : kv_len;
+  const int q_len = q1 - q0;
+  const int qt = (q_len + a.tq - 1) / a.tq - 1 - qk;
+  if (qt < 0) return false;   // nothing to do: either path returns at once
+  const int t0 = qt * a.tq;
+  const int ntok = q_len - t0 < a.tq ? q_len - t0 : a.tq;
+  const int W = a.window_left;
+  const int pos_first = kv_len - q_len + t0;
+  const int pos_last = pos_first + ntok - 1;
+  const int key_hi = pos_last < kv_len - 1 ? pos_last : kv_len - 1;
+  const int key_lo = W >= 0 ? (pos_first - W > 0 ? pos_first - W : 0) : 0;
+  int tile_lo = key_lo / kBK;
+  int tile_hi = key_hi >= 0 ? key_hi / kBK : -1;
+  if (S > 1 && tile_hi >= tile_lo) {
+    const int n = tile_hi - tile_lo + 1;
+    const int first = tile_lo;
+    tile_lo = first + (split * n) / S;
+    tile_hi = first + ((split + 1) * n) / S - 1;
   }
-  // the sink joins the denominator relative to max(running max, sink), so
-  // that a sink far above every logit gives l ~ 1 and lse ~ sink instead of
-  // an infinite l; O is scaled by the same factor (1 when the sink is below
-  // the running maximum, and for a -inf sink)
-  float oscale = 1.f;
-  if (a.sinks) {
-    const float s2 = sink * kLog2e;
-    const float m2 = s2 > mb ? s2 : mb;
-    oscale = __builtin_amdgcn_exp2f(mb - m2);
-    l = l * oscale + __builtin_amdgcn_exp2f(s2 - m2);
-    mb = m2;
-  }
-  if (a.lse != nullptr && half == 0) a.lse[trow * a.lse_tok + static_cast<int64_t>(h) * a.lse_head] = mb * kLn2 + __builtin_logf(l);
-  const float inv = (bmm2 * oscale) / l;
-  if (a.out_mx != 0) {
-    uint8_t* orow8 = reinterpret_cast<uint8_t*>(a.out) + trow * a.o_tok + static_cast<int64_t>(h) * a.o_head;
-    uint8_t* sfrow = a.out_sf + trow * a.sf_tok + static_cast<int64_t>(h) * a.sf_head;
-    if (a.out_mx == 16) store_mxfp4_row<D, 16>(oacc, inv, a.o_sf_scale, orow8, sfrow, half);
-    else store_mxfp4_row<D, 32>(oacc, inv, a.o_sf_scale, orow8, sfrow, half);
-    return;
-  }
-  uint16_t* orow = a.out + trow * a.o_tok + static_cast<int64_t>(h) * a.o_head;
-  for (int md = 0; md < MD; ++md) {
-    for (int g = 0; g < 4; ++g) {
-      const int d = md * 32 + 8 * g + 4 * half;
-      const u32x2 w = u32x2{pack_bf16(oacc[md][4 * g] * inv, oacc[md][4 * g + 1] * inv),
-                            pack_bf16(oacc[md][4 * g + 2] * inv, oacc[md][4 * g + 3] * inv)};
-      *reinterpret_cast<u32x2*>(orow + d) = w;
-    }
+  const int chunk_lo = tile_lo * kBK;
+  const int chunk_hi = tile_hi * kBK + kBK - 1 < kv_len - 1 ? tile_hi * kBK + kBK - 1 : kv_len - 1;
+  const int common_lo = W >= 0 ? (pos_last - W > chunk_lo ? pos_last - W : chunk_lo) : chunk_lo;
+  const int common_hi = pos_first < chunk_hi ? pos_first : chunk_hi;
+  return common_hi - common_lo + 1 >= kFp8MinKeys;
+}
+
+template <int D, bool FP8, bool UPAGE, bool F8M>
+__device__ __forceinline__ void run_item(const AttnArgs& a, const int item) {
+  if constexpr (F8M) {
+    if (fp8_item(a, item)) attend_item<D, FP8, UPAGE, true>(a, item);
+    else attend_item<D, FP8, UPAGE, false>(a, item);
+  } else {
+    attend_item<D, FP8, UPAGE, false>(a, item);
   }
 }
+
+
 
 // One workgroup per work item, in heaviest-first order.
 template <int D, bool FP8, bool UPAGE, bool F8M>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void paged_prefill_kernel(AttnArgs a) {
-  attend_item<D, FP8, UPAGE, F8M>(a, blockIdx.x);
+  run_item<D, FP8, UPAGE, F8M>(a, blockIdx.x);
 }
 
 // Persistent workgroups (as many as fit on the device at once) pull work
@@ -1065,7 +1157,7 @@ void paged_prefill_persistent(AttnArgs a) {
     __syncthreads();
     const uint64_t item = static_cast<uint64_t>(next_item[round & 1]) * nq + queue;
     if (item >= static_cast<uint64_t>(a.n_items)) break;
-    attend_item<D, FP8, UPAGE, F8M>(a, static_cast<int>(item));
+    run_item<D, FP8, UPAGE, F8M>(a, static_cast<int>(item));
   }
   if (threadIdx.x == 0 && atomicAdd(sched + kSchedDone, 1u) == gridDim.x - 1) {
     // every workgroup has made its last fetch: no counter is read again
@@ -1333,7 +1425,7 @@ extern "C" int32_t ppa_paged_prefill_attention(const ppa_params* p, void* stream
   a.group = p->num_qo_heads / p->num_kv_heads;
   a.gw = a.group < 16 ? a.group : 16;
   a.n_hg = (a.group + a.gw - 1) / a.gw;
-  a.tq = 256 / a.gw;
+  a.tq = 32 * kWaves / a.gw;
   a.n_qt = (p->max_q_len + a.tq - 1) / a.tq;
   a.window_left = p->window_left;
   a.bmm1 = p->bmm1_scale;
@@ -1487,7 +1579,7 @@ extern "C" int32_t ppa_plan_kv_splits(const ppa_params* p) {
   // work items as the launch counts them, and the key tiles of the longest
   const int group = q.num_qo_heads / q.num_kv_heads;
   const int gw = group < 16 ? group : 16;
-  const int tq = 256 / gw;
+  const int tq = 32 * kWaves / gw;
   const int64_t items = static_cast<int64_t>((q.max_q_len + tq - 1) / tq) * q.batch_size * q.num_kv_heads *
                         ((group + gw - 1) / gw);
   int64_t keys = q.max_kv_len;

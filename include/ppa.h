@@ -382,6 +382,34 @@ int32_t ppa_validate_page_table_csr_host(const ppa_params* p, const int32_t* seq
                                          const int32_t* kv_indptr, const int32_t* kv_indices,
                                          const int32_t* kv_last_page_len, char* msg, size_t msg_len);
 
+/*
+ * The same checks on the DEVICE arrays of `p` (TensorRT-LLM attention-
+ * backend article: the self-check step of its FlashInfer section and the
+ * row-count check of its block-offset section ask for bad metadata to fail
+ * loudly; the attention call itself only clamps).  Runs ppa_validate_shapes
+ * on the host, then enqueues three small kernels on `stream` and returns
+ * without waiting; no allocation.  They evaluate every rule of
+ * ppa_validate_metadata_host (cum_seq_lens_kv only when not NULL) and, for
+ * the CSR form, of ppa_validate_page_table_csr_host (kv_last_page_len only
+ * when not NULL), and write the FIRST violated rule in that order
+ * (ppa_validate_metadata_host's rules, then the CSR ones) to `result`:
+ *   result[0]  PPA_OK, PPA_ERR_LENGTHS, PPA_ERR_TABLE or PPA_ERR_METADATA,
+ *              the code the host functions return for that rule
+ *   result[1]  the index of the request the rule concerns, or -1 for a rule
+ *              on the whole batch (cum_seq_lens_q[0], its last entry,
+ *              cum_seq_lens_kv[0], kv_indptr[0], kv_indptr[batch_size])
+ * `result` is caller-owned device memory of two int32, 8-byte aligned (it
+ * holds a 64-bit key while the kernels run); read it after the stream has
+ * passed this call.  The metadata arrays must have the lengths ppa_params
+ * states (batch_size + 1 / batch_size entries); table entries are read only
+ * inside a request's own row or index slice, and only after the bounds that
+ * make the read valid have passed.  Returns a ppa_validate_shapes error,
+ * PPA_ERR_NULL_POINTER (result NULL), PPA_ERR_ALIGNMENT (result not 8-byte
+ * aligned) or PPA_ERR_HIP (launch failure); otherwise PPA_OK, whatever the
+ * metadata holds.
+ */
+int32_t ppa_validate_metadata_device(const ppa_params* p, int32_t* result, void* stream);
+
 /* Bytes of workspace a call needs: 256 for the balanced schedule's counters,
    plus the partial outputs and log-sum-exps of split-KV (kv_splits > 1:
    kv_splits * num_tokens * num_qo_heads * (head_dim + 1) * 4 bytes, each

@@ -16,4 +16,5 @@ from .binding import (PPA_ABI_VERSION, PPA_DTYPE_MXFP4, WORKSPACE_BYTES, MxFp4Ou
                       ppa_paged_prefill_attention, ppa_paged_prefill_attention_noalloc, ppa_noalloc_scratch_bytes,
                       ppa_params_size, ppa_strerror,
                       ppa_validate_metadata_host, ppa_validate_page_table_csr_host, ppa_validate_shapes,
+                      ppa_validate_metadata_device, check_metadata_device,
                       ppa_workspace_bytes, ppa_plan_kv_splits, ppa_plan_kv_splits_model)

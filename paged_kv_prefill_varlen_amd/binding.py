@@ -199,6 +199,7 @@ def _load():
         "ppa_validate_metadata_host": (c_int32, [P, c_void_p, c_void_p, c_void_p, c_void_p, c_char_p, c_size_t]),
         "ppa_validate_page_table_csr_host": (c_int32, [P, c_void_p, c_void_p, c_void_p, c_void_p, c_char_p,
                                                        c_size_t]),
+        "ppa_validate_metadata_device": (c_int32, [P, c_void_p, c_void_p]),
         "ppa_workspace_bytes": (c_size_t, [P]),
         "ppa_plan_kv_splits_model": (c_int32, [c_int64, c_int64, c_int64, c_int32]),
         "ppa_plan_kv_splits": (c_int32, [P]),
@@ -330,6 +331,31 @@ def _stream_handle(device: torch.device, stream) -> int:
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def ppa_validate_metadata_device(params: PpaParams, result: torch.Tensor,
+                                 stream: Union[int, "torch.cuda.Stream", None] = None) -> None:
+    """Enqueue the device-side metadata check (ppa.h).  ``result`` is an
+    int32 device tensor of two elements, 8-byte aligned; once the stream has
+    passed the call it holds (status, request index or -1)."""
+    if not (isinstance(result, torch.Tensor) and result.is_cuda and result.dtype == torch.int32
+            and result.numel() >= 2 and result.is_contiguous()):
+        raise ValueError("result must be a contiguous int32 device tensor of at least two elements")
+    h = _stream_handle(result.device, stream)
+    st = _lib.ppa_validate_metadata_device(ctypes.byref(params), c_void_p(result.data_ptr()), c_void_p(h))
+    if st != 0:
+        _, msg = ppa_validate_shapes(params)
+        raise PpaError(st, msg or "result pointer")
+
+
+def check_metadata_device(params: PpaParams, device: Optional[torch.device] = None,
+                          stream: Union[int, "torch.cuda.Stream", None] = None) -> Tuple[int, int]:
+    """Run ppa_validate_metadata_device and wait for it: (status, request)."""
+    result = torch.empty(2, dtype=torch.int32, device=device or torch.device("cuda"))
+    ppa_validate_metadata_device(params, result, stream)
+    torch.cuda.synchronize(result.device)
+    st, req = (int(x) for x in result.cpu())
+    return st, req
 
 
 def ppa_paged_prefill_attention(params: PpaParams, stream: Union[int, "torch.cuda.Stream", None] = None,

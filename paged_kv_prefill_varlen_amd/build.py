@@ -20,7 +20,7 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libppa.so")
 ARCH = os.environ.get("PPA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["ppa_host.cpp", "ppa_attention.hip"]
+SOURCES = ["ppa_host.cpp", "ppa_attention.hip", "ppa_validate.hip"]
 HEADERS = ["ppa_internal.h", "ppa_page_addr.hpp"]
 
 DEVICE_FLAGS = [

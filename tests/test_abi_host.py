@@ -55,7 +55,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for need in ("ppa_paged_prefill_attention", "ppa_validate_shapes", "ppa_validate_metadata_host",
-                 "ppa_workspace_bytes", "ppa_strerror", "ppa_gather_paged_kv"):
+                 "ppa_validate_metadata_device", "ppa_workspace_bytes", "ppa_strerror", "ppa_gather_paged_kv"):
         assert need in names
 
 
@@ -287,6 +287,19 @@ def test_metadata_ignores_columns_past_a_request():
     bt[0, 1] = -7
     bt[1, 1] = 10 ** 6
     assert _meta(_params(c), c, bt=bt)[0] == OK
+
+
+def test_device_metadata_check_rejects_arguments_on_the_host():
+    # the entry point validates shapes and its result pointer before any
+    # launch: these return without touching a device
+    c = _case()
+    dev_check = B._lib.ppa_validate_metadata_device
+    good = ctypes.c_void_p(1 << 20)   # never dereferenced on these paths
+    assert dev_check(ctypes.byref(_params(c, head_dim=96)), good, None) == ERR["PPA_ERR_HEAD_DIM"]
+    assert dev_check(ctypes.byref(_params(c, cum_seq_lens_q=None)), good, None) == ERR["PPA_ERR_NULL_POINTER"]
+    assert dev_check(ctypes.byref(_params(c)), None, None) == ERR["PPA_ERR_NULL_POINTER"]
+    assert dev_check(ctypes.byref(_params(c)), ctypes.c_void_p((1 << 20) + 4), None) == ERR["PPA_ERR_ALIGNMENT"]
+    assert dev_check(None, good, None) == ERR["PPA_ERR_NULL_POINTER"]
 
 
 def test_cum_seq_lens_kv_optional():

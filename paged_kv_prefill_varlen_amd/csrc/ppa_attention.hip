@@ -909,7 +909,9 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     for (int ks = 0; ks < 4; ++ks)
       for (int md = 0; md < MD; ++md) oacc[md] = mfma32(vf[md][ks], pb[ks], oacc[md]);
   };
-  auto softmax = [&](int j) {
+  // mask (boundary tiles only), the tile's row maximum and the lazy rescale
+  // of the running state; returns the exponent offset of the tile's weights
+  auto softmax_max = [&](int j) {
     const int k0 = j * kBK;
     const bool need_mask = (k0 + kBK - 1 > wpos_first) || (W >= 0 && k0 < wpos_last - W) ||
                            (k0 + kBK > kv_len);
@@ -937,7 +939,28 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
       for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
       if constexpr (T::F8MMA) lacc *= alpha;
     }
-    const float mb = m_run == kNegInf ? 0.f : m_run;
+    return m_run == kNegInf ? 0.f : m_run;
+  };
+  // bf16 weights of the 32 keys of S block mt into the PV operand (K-steps
+  // 2 mt, 2 mt + 1), their row sums added to `sum`
+  auto exp_half = [&](int mt, float mb, float& sum) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    for (int sh = 0; sh < 2; ++sh) {
+      bf16x2 w[4];
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][8 * sh + 2 * e], c, -mb));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][8 * sh + 2 * e + 1], c, -mb));
+        w[e] = __builtin_convertvector(f32x2{p0, p1}, bf16x2);   // round to nearest even
+        // row sums of the bf16 weights the PV product uses.  (The packed
+        // value is fed to v_dot2 directly; reading it back out of a 4-dword
+        // vector first was miscompiled - every dot2 got the same operand.)
+        sum = __builtin_amdgcn_fdot2_f32_bf16(w[e], ones, sum, false);
+      }
+      pb[2 * mt + sh] = bf16x8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
+    }
+  };
+  auto softmax = [&](int j) {
+    const float mb = softmax_max(j);
     if constexpr (T::F8MMA) {
       // P as e4m3fn codes (p <= 2^8 with the lazy maximum: within range),
       // byte 16 mt + v = element v of sacc[mt].  The row sums come from the
@@ -953,22 +976,9 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
         }
       return;
     }
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float sum = l_part;
-    for (int mt = 0; mt < 2; ++mt)
-      for (int sh = 0; sh < 2; ++sh) {
-        bf16x2 w[4];
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][8 * sh + 2 * e], c, -mb));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][8 * sh + 2 * e + 1], c, -mb));
-          w[e] = __builtin_convertvector(f32x2{p0, p1}, bf16x2);   // round to nearest even
-          // row sums of the bf16 weights the PV product uses.  (The packed
-          // value is fed to v_dot2 directly; reading it back out of a 4-dword
-          // vector first was miscompiled - every dot2 got the same operand.)
-          sum = __builtin_amdgcn_fdot2_f32_bf16(w[e], ones, sum, false);
-        }
-        pb[2 * mt + sh] = bf16x8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
-      }
+    exp_half(0, mb, sum);
+    exp_half(1, mb, sum);
     l_part = sum;
   };
 

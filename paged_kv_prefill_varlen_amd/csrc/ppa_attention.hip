@@ -63,6 +63,7 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((ext_vector_type(8))) int i32x8;   // 32 fp8 codes: one f8f6f4 MFMA operand
+typedef __attribute__((ext_vector_type(2))) int v2i32;
 
 constexpr int kBK = 64;            // keys per tile
 constexpr int kWaves = 8;
@@ -342,6 +343,40 @@ __device__ __forceinline__ void fetch_kv_lds(__bf16* kt, __bf16* vt, const AttnA
   }
 }
 
+// fp8 cache at head_dim 128, fp8 MFMA arithmetic: the wave's keys
+// [kb, kb + 8) of K and of V, as stored (e4m3fn codes, 128-byte rows), into
+// the tile's K and V stages, 16-byte chunk c of key row r in slot
+// c ^ ((r / 2) mod 8).  One copy instruction per plane moves the wave's
+// 1 KB: lane i writes row i / 8, slot i mod 8, so it loads the global
+// chunk (i mod 8) ^ ((row / 2) mod 8).  Fast and general paths as in
+// fetch_kv_lds.
+template <bool FAST>
+__device__ __forceinline__ void fetch_kv_lds_f8(uint8_t* kt, uint8_t* vt, const AttnArgs& a, const PageTable& pt,
+                                                int id, int hk, int kb, int kv_len, int page_mask, int wave,
+                                                int lane) {
+  asm volatile("" : "+v"(lane));   // recomputed per call, as in fetch_kv_lds
+  const int rl = lane >> 3;                       // key of the wave, 0..7
+  const int row = 8 * wave + rl;                  // key of the tile
+  const int c = (lane & 7) ^ ((row >> 1) & 7);    // global chunk of the lane's slot
+  const uint32_t kdst = lds_addr(kt + 8 * wave * 128);
+  const uint32_t vdst = lds_addr(vt + 8 * wave * 128);
+  if (FAST) {
+    const uint8_t* kbase =
+        a.k.base + static_cast<int64_t>(id) * a.k.page_stride + static_cast<int64_t>(hk) * a.k.head_stride;
+    const uint8_t* vbase =
+        a.v.base + static_cast<int64_t>(id) * a.v.page_stride + static_cast<int64_t>(hk) * a.v.head_stride;
+    const int slot = (kb & page_mask) + rl;
+    lds_copy16(kdst, kbase, static_cast<uint32_t>(slot * static_cast<int>(a.k.tok_stride) + c * 16));
+    lds_copy16(vdst, vbase, static_cast<uint32_t>(slot * static_cast<int>(a.v.tok_stride) + c * 16));
+  } else {
+    const int key = kb + rl;
+    const int k = key < kv_len ? key : kv_len - 1;
+    const int pid = page_id(pt, k);
+    lds_copy16(kdst, token_row<1>(a.k, pid, page_mask, k, hk, c * 16));
+    lds_copy16(vdst, token_row<1>(a.v, pid, page_mask, k, hk, c * 16));
+  }
+}
+
 // s_waitcnt vmcnt(n) (expcnt and lgkmcnt not waited on), n < 16.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -419,31 +454,7 @@ __device__ __forceinline__ void store_kv(const uint32_t* kraw, const uint32_t* v
                                          int wave, int lane) {
   using T = Tile<D, FP8, F8M>;
   if constexpr (!FP8) return;   // the bf16 cache is copied straight into LDS
-  if constexpr (T::F8MMA) {
-    // K: the lane's 16 codes (dims 16 chunk ..) of row r0, as they are, in
-    // 16-byte slot chunk ^ ((row / 2) mod 8) of the 128-byte row
-    uint8_t* kb8 = reinterpret_cast<uint8_t*>(klds);
-    const int krow = 8 * wave + lane / 8;
-    const int kch = lane % 8;
-    *reinterpret_cast<u32x4*>(kb8 + krow * 128 + ((kch ^ ((krow >> 1) & 7)) << 4)) =
-        u32x4{kraw[0], kraw[1], kraw[2], kraw[3]};
-    // V: keys 8 wave + 4 kgl + r (r = 0..3) x dims 4 dg + q (q = 0..3); as
-    // V^T rows of 64 key bytes in the order the PV operand takes them: key
-    // 8 run + e at byte 32 (run mod 2) + 8 (run / 2) + e; 16-byte slot
-    // chunk ^ ((dim / 4) mod 4)
-    uint8_t* vb8 = reinterpret_cast<uint8_t*>(vlds);
-    const int kgl = lane >> 5, dg = lane & 31;
-    const int pos = 32 * (wave & 1) + 8 * (wave >> 1) + 4 * kgl;
-    for (int q = 0; q < 4; ++q) {
-      // byte q of each key's dword -> one dword of 4 keys for dim 4 dg + q
-      const uint32_t lo = __builtin_amdgcn_perm(vraw[1], vraw[0], 0x0c0c0400u + 0x0101u * q);
-      const uint32_t hi = __builtin_amdgcn_perm(vraw[3], vraw[2], 0x0c0c0400u + 0x0101u * q);
-      const uint32_t w = lo | (hi << 16);
-      const int m = 4 * dg + q;
-      *reinterpret_cast<uint32_t*>(vb8 + m * 64 + ((((pos >> 4) ^ ((m >> 2) & 3))) << 4) + (pos & 15)) = w;
-    }
-    return;
-  }
+  static_assert(!T::F8MMA, "the fp8 MFMA path copies K and V straight into LDS");
   // K: K_CHUNK fp8 codes of row r0 from element chunk * K_CHUNK, i.e. whole
   // 16-byte bf16 chunks chunk * K_CHUNK / 8 ..
   const int r0 = lane / T::K_TPR;
@@ -736,8 +747,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   // direct-copy path: Q is loaded after the first tile's copies are issued
   // (below), and both are waited for together, so that no later compiler
   // wait for Q covers the prefetched tiles
-  if constexpr (T::F8MMA) load_q8();
-  else if constexpr (!T::DMA) load_q();
+  if constexpr (!T::DMA && !T::F8MMA) load_q();
   // the row's sink logit, read now so that the epilogue does not wait for it
   const float sink = a.sinks ? a.sinks[h0 + (rvalid ? hd : 0)] : 0.f;
 
@@ -751,7 +761,6 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   pt.page_shift = a.page_shift;
   const int page_mask = (1 << a.page_shift) - 1;
   uint32_t kraw[T::K_DW], vraw[T::V_DW];
-  uint32_t kraw2[T::F8MMA ? T::K_DW : 1], vraw2[T::F8MMA ? T::V_DW : 1];   // fp8 MFMA: second tile of a pair
   int id_next = 0;   // page id of the wave's keys in the next tile to fetch
 
   const int krow_lane = swap_bits23(col);
@@ -766,6 +775,18 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     const int key = 8 * (G >> 1) + (jj >> 2);
     vt_lane = key * (2 * D) + (jj & 1) * 8;
     for (int md = 0; md < MD; ++md) vt_md[md] = ((4 * md + 2 * (G & 1) + ((jj & 3) >> 1)) ^ vswz<D>(key)) * 16;
+  }
+
+  // fp8 MFMA V^T transpose loads (read_v): group G = lane / 16, jj =
+  // lane % 16 points at key 8 (G / 2) + jj / 2 (+ 16 r), 16-byte chunk
+  // 2 md + G mod 2 at byte 8 (jj mod 2), in slot chunk ^ ((key / 2) mod 8)
+  // ((key / 2) mod 8 does not depend on r)
+  int vt8_lane = 0, vt8_md[MD];
+  if constexpr (T::F8MMA) {
+    const int G = lane >> 4, jj = lane & 15;
+    vt8_lane = (8 * (G >> 1) + (jj >> 1)) * 128 + 8 * (jj & 1);
+    const int sw = (4 * (G >> 1) + (jj >> 2)) & 7;
+    for (int md = 0; md < MD; ++md) vt8_md[md] = ((2 * md + (G & 1)) ^ sw) * 16;
   }
 
   auto wave_tile = [&](int j) {
@@ -799,24 +820,25 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     return st < 2 ? klds[st] : vlds[st - 2];
   };
   auto f8v = [&](int j) { return f8k(j) + 4096; };
-  auto stage_fetch = [&](int j, int id, bool second = false) {
+  auto stage_fetch = [&](int j, int id) {
     const int kb = j * kBK + 8 * wave;
     const bool fast = UPAGE && j * kBK + kBK <= kv_len;
-    if constexpr (T::DMA) {
+    if constexpr (T::F8MMA) {
+      uint8_t* kt = reinterpret_cast<uint8_t*>(f8k(j));
+      uint8_t* vt = reinterpret_cast<uint8_t*>(f8v(j));
+      if (fast) fetch_kv_lds_f8<true>(kt, vt, a, pt, id, hk, kb, kv_len, page_mask, wave, lane);
+      else fetch_kv_lds_f8<false>(kt, vt, a, pt, id, hk, kb, kv_len, page_mask, wave, lane);
+    } else if constexpr (T::DMA) {
       const int st = stage(j);
       if (fast) fetch_kv_lds<D, true>(klds[st], vlds[st], a, pt, id, hk, kb, kv_len, page_mask, wave, lane);
       else fetch_kv_lds<D, false>(klds[st], vlds[st], a, pt, id, hk, kb, kv_len, page_mask, wave, lane);
     } else {
-      uint32_t* kr = T::F8MMA && second ? kraw2 : kraw;
-      uint32_t* vr = T::F8MMA && second ? vraw2 : vraw;
-      if (fast) fetch_kv<D, FP8, true>(kr, vr, a, pt, id, hk, kb, kv_len, page_mask, lane);
-      else fetch_kv<D, FP8, false>(kr, vr, a, pt, id, hk, kb, kv_len, page_mask, lane);
+      if (fast) fetch_kv<D, FP8, true>(kraw, vraw, a, pt, id, hk, kb, kv_len, page_mask, lane);
+      else fetch_kv<D, FP8, false>(kraw, vraw, a, pt, id, hk, kb, kv_len, page_mask, lane);
     }
   };
-  auto stage_store = [&](int j, bool second = false) {
-    if constexpr (T::F8MMA) {
-      store_kv<D, FP8, F8M>(second ? kraw2 : kraw, second ? vraw2 : vraw, f8k(j), f8v(j), wave, lane);
-    } else {
+  auto stage_store = [&](int j) {
+    if constexpr (!T::F8MMA) {
       const int buf = stage(j);
       store_kv<D, FP8, F8M>(kraw, vraw, klds[buf], vlds[buf], wave, lane);
     }
@@ -864,16 +886,21 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
   i32x8 vf8[MD];
   auto read_v = [&](int j) {
     if constexpr (T::F8MMA) {
-      // V^T operand: dim row md*32 + col, key bytes 32 half .. + 31 (the
-      // order P's bytes take), 16-byte chunks 2 half (+ 1) in slots
-      // chunk ^ ((dim / 4) mod 4)
-      const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(f8v(j));
+      // V^T operand by 8-bit transpose loads from V as stored ([key][128
+      // bytes]): in each 16-lane group G, lanes 2e and 2e + 1 point at the
+      // two 8-byte halves of 16 bytes of key row k0 + e, and lane jj
+      // receives byte jj of those 8 rows.  With k0 = 16 r + 8 (G / 2) and the
+      // 16 bytes at dim 32 md + 16 (G mod 2), lane (col, half) receives, for
+      // r = 0..3, keys 16 r + 8 half + 0..7 of dim 32 md + col: the byte
+      // order of P in the B operand
+      typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+      const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(f8v(j)) + vt8_lane;
       for (int md = 0; md < MD; ++md) {
-        const int m = md * 32 + col;
-        const int sw = (m >> 2) & 3;
-        const u32x4 x0 = *reinterpret_cast<const u32x4*>(vb8 + m * 64 + (((2 * half) ^ sw) << 4));
-        const u32x4 x1 = *reinterpret_cast<const u32x4*>(vb8 + m * 64 + (((2 * half + 1) ^ sw) << 4));
-        vf8[md] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+        v2i32 x[4];
+        for (int r = 0; r < 4; ++r)
+          x[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(
+              (__attribute__((address_space(3))) const uint8_t*)(vb8 + vt8_md[md] + 2048 * r)));
+        vf8[md] = i32x8{x[0][0], x[0][1], x[1][0], x[1][1], x[2][0], x[2][1], x[3][0], x[3][1]};
       }
       __builtin_amdgcn_sched_barrier(0);
       return;
@@ -1022,20 +1049,28 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
       }
     }
   } else if (T::F8MMA && tile_lo <= tile_hi) {
-    // fp8 MFMA: four-stage ring, two tiles per barrier; tiles j + 2, j + 3
-    // are fetched into registers before tiles j, j + 1 are computed and
-    // stored after them into the stages of j - 2, j - 1, which every wave
-    // finished reading before the previous barrier
+    // fp8 MFMA: K and V codes copied straight into a four-stage ring of
+    // 16 KB stages (8 KB of K, then 8 KB of V), two tiles per barrier, as
+    // for the bf16 cache: the barrier publishes tiles j, j + 1 and frees
+    // the stages of j - 2, j - 1 (read before it), which receive j + 2, j + 3
     const int lo = tile_lo, hi = tile_hi;
-    stage_fetch(lo, page_of(lo));
-    if (lo + 1 <= hi) stage_fetch(lo + 1, page_of(lo + 1), true);
-    stage_store(lo);
-    if (lo + 1 <= hi) stage_store(lo + 1, true);
-    __syncthreads();
+    auto clampt = [&](int j) { return j <= hi ? j : hi; };
+    const int id0 = page_of_nb(lo);
+    const int id1 = page_of_nb(clampt(lo + 1));
+    int idn0 = page_of_nb(clampt(lo + 2));
+    int idn1 = page_of_nb(clampt(lo + 3));
+    stage_fetch(lo, id0);
+    if (lo + 1 <= hi) stage_fetch(lo + 1, id1);
+    load_q8();   // after the first copies: its conversion waits for its loads
     for (int j = lo; j <= hi; j += 2) {
-      const bool m2 = j + 2 <= hi, m3 = j + 3 <= hi;
-      if (m2) stage_fetch(j + 2, page_of(j + 2));
-      if (m3) stage_fetch(j + 3, page_of(j + 3), true);
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (j + 2 <= hi) stage_fetch(j + 2, idn0);
+      if (j + 3 <= hi) stage_fetch(j + 3, idn1);
+      if (j + 4 <= hi) {
+        idn0 = page_of_nb(j + 4);
+        idn1 = page_of_nb(clampt(j + 5));
+      }
       if (wave_tile(j)) {
         gemm_s(j);
         read_v(j);
@@ -1048,9 +1083,6 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
         softmax(j + 1);
         gemm_pv(j + 1);
       }
-      if (m2) stage_store(j + 2);
-      if (m3) stage_store(j + 3, true);
-      __syncthreads();
     }
   } else if (tile_lo <= tile_hi) {
     const int lo = tile_lo, hi = tile_hi;

@@ -75,6 +75,16 @@ constexpr float kMinScale = 1.17549435e-38f;  // FLT_MIN
 // fp8 arithmetic (fp8_compute): the fewest keys every row of a work item
 // must see for the item to run on the fp8 MFMA
 constexpr int kFp8MinKeys = 1024;
+#ifndef PPA_LATEV64
+#define PPA_LATEV64 1
+#endif
+// bf16 cache at head_dim 64: the V^T operand is read after the softmax, so
+// that S and V^T are never live together; the kernel then fits 128 VGPRs
+// and two workgroups share a CU
+template <int D>
+constexpr bool kLateV = PPA_LATEV64 && D == 64;
+template <int D, bool FP8>
+constexpr int kWavesPerEU = (!FP8 && kLateV<D>) ? 4 : 2;
 
 // Scheduler counters in the workspace: kSchedQueues queue heads, then the
 // number of workgroups that have finished.
@@ -1037,14 +1047,16 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
       }
       if (wave_tile(j)) {
         gemm_s(j);
-        read_v(j);
+        if (!kLateV<D>) read_v(j);
         softmax(j);
+        if (kLateV<D>) read_v(j);
         gemm_pv(j);
       }
       if (j + 1 <= hi && wave_tile(j + 1)) {
         gemm_s(j + 1);
-        read_v(j + 1);
+        if (!kLateV<D>) read_v(j + 1);
         softmax(j + 1);
+        if (kLateV<D>) read_v(j + 1);
         gemm_pv(j + 1);
       }
     }
@@ -1173,7 +1185,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const int item) {
 
 // One workgroup per work item, in heaviest-first order.
 template <int D, bool FP8, bool UPAGE, bool F8M>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<D, FP8>, kWavesPerEU<D, FP8>)))
 void paged_prefill_kernel(AttnArgs a) {
   run_item<D, FP8, UPAGE, F8M>(a, blockIdx.x);
 }
@@ -1187,7 +1199,7 @@ void paged_prefill_kernel(AttnArgs a) {
 // dispatcher places on one XCD, so that K/V stays in one L2.  The last
 // workgroup to finish returns every counter to zero for the next call.
 template <int D, bool FP8, bool UPAGE, bool F8M>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<D, FP8>, kWavesPerEU<D, FP8>)))
 void paged_prefill_persistent(AttnArgs a) {
   __shared__ uint32_t next_item[2];
   const uint32_t nq = static_cast<uint32_t>(a.n_queues);

@@ -75,14 +75,11 @@ constexpr float kMinScale = 1.17549435e-38f;  // FLT_MIN
 // fp8 arithmetic (fp8_compute): the fewest keys every row of a work item
 // must see for the item to run on the fp8 MFMA
 constexpr int kFp8MinKeys = 1024;
-#ifndef PPA_LATEV64
-#define PPA_LATEV64 1
-#endif
 // bf16 cache at head_dim 64: the V^T operand is read after the softmax, so
 // that S and V^T are never live together; the kernel then fits 128 VGPRs
 // and two workgroups share a CU
 template <int D>
-constexpr bool kLateV = PPA_LATEV64 && D == 64;
+constexpr bool kLateV = D == 64;
 template <int D, bool FP8>
 constexpr int kWavesPerEU = (!FP8 && kLateV<D>) ? 4 : 2;
 

@@ -24,10 +24,11 @@
 // Per 64-key tile
 //   1. staging: each wave copies 8 consecutive keys of K and of V from their
 //      pages into an LDS ring, both in natural [key][dim] layout with 16-byte
-//      chunks XOR swizzled by key: bf16 pages straight into LDS, fp8 codes
-//      through registers, widened to bf16 on the way (every e4m3fn value is a
-//      bf16 value).  With pages of >= 8 tokens a wave's keys share one page,
-//      whose id is read by a scalar load ahead of use;
+//      chunks XOR swizzled by key: bf16 pages straight into LDS; fp8 codes
+//      straight into LDS for the fp8 MFMA arithmetic, or through registers,
+//      widened to bf16 on the way, for the widened one (every e4m3fn value
+//      is a bf16 value).  With pages of >= 8 tokens a wave's keys share one
+//      page, whose id is read by a scalar load ahead of use;
 //   2. S^T = K Q^T on v_mfma_f32_32x32x16_bf16: keys along M, rows along N,
 //      so a lane holds 32 keys of one row and its partner lane (lane ^ 32) the
 //      other 32: row max / sum need one cross-lane step;
@@ -223,9 +224,10 @@ __device__ __forceinline__ uint32_t mx_pack4(float y0, float y1, float y2, float
 // unpadded rows whose 16-byte chunks are XOR swizzled by key (kswz, vswz), in
 // a four-stage ring consumed two tiles per barrier.  The PV operand, V^T, is
 // read with LDS transpose loads.
-// fp8 cache: staged through registers (widened to bf16 once per workgroup)
-// into the same swizzled layout, so both caches share the operand reads;
-// two stages.
+// fp8 cache, widened arithmetic: staged through registers (widened to bf16
+// once per workgroup) into the same swizzled layout, so both caches share
+// the operand reads; two stages.  fp8 cache, fp8 MFMA arithmetic: the codes
+// copied like the bf16 tiles (fetch_kv_lds_f8), four stages.
 template <int D, bool FP8, bool F8M = false>
 struct Tile {
   static constexpr int EB = FP8 ? 1 : 2;        // bytes per cache element
@@ -242,8 +244,8 @@ struct Tile {
   static constexpr int K_DW = DMA ? 1 : K_LANE_BYTES / 4;
   static constexpr int V_DW = DMA ? 1 : (4 * V_KEY_BYTES + 3) / 4;
   // fp8 cache at head_dim 128: QK^T and PV on the fp8 MFMA (Q and P
-  // quantised to e4m3fn); K stays in code bytes [key][dim], V is stored
-  // transposed as code bytes [dim][key]; both in the first half of a stage
+  // quantised to e4m3fn); K and V stay in code bytes [key][dim], 8 KB each,
+  // one 16 KB stage of the ring per bf16 stage buffer
   static constexpr bool F8MMA = F8M;
   static_assert(!F8M || (FP8 && D == 128), "fp8 MFMA: fp8 cache at head_dim 128");
   static constexpr int K_ELEMS = kBK * D;   // both: natural [key][dim], swizzled

@@ -464,6 +464,7 @@ def make_append_params(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: t
             setattr(a, f"{name}_scale", 0.0)
         else:
             setattr(a, f"{name}_scale", float(val))
+    a._refs = (k_new, v_new, slot_mapping, k_scale, v_scale)   # the pointers' tensors, kept alive
     return a
 
 
@@ -554,8 +555,11 @@ def make_params(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.
                 kv_splits: int = 0, fp8_compute: bool = False) -> PpaParams:
     """Fill a PpaParams from torch tensors (the FlashInfer API page's argument
     list).  With kv_indptr / kv_indices the flat (CSR) page table is used and
-    block_tables may be None.  Keeps no reference to the tensors: the caller
-    keeps them alive."""
+    block_tables may be None.  The returned PpaParams holds device pointers
+    and keeps references to the tensors they point into (attribute
+    ``_refs``), so that a params object launched later never reads memory
+    the allocator has handed to another tensor; a copy of the struct
+    (``from_buffer_copy``) does not carry them."""
     if query.dim() != 3:
         raise ValueError("query must be [num_tokens, num_qo_heads, head_dim]")
     _check_metadata(query, kv_cache, workspace_buffer, block_tables, seq_lens, cum_seq_lens_q, cum_seq_lens_kv,
@@ -659,6 +663,8 @@ def make_params(query: torch.Tensor, kv_cache, workspace_buffer: Optional[torch.
         p.lse_strides[:] = list(lse.stride())
     p.kv_splits = int(kv_splits)
     p.fp8_compute = 1 if fp8_compute else 0
+    p._refs = (query, kv_cache, workspace_buffer, block_tables, seq_lens, cum_seq_lens_q, cum_seq_lens_kv, out,
+               sinks, kv_indptr, kv_indices, kv_last_page_len, lse, bmm1_scale, bmm2_scale)
     return p
 
 

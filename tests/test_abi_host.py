@@ -289,6 +289,26 @@ def test_metadata_ignores_columns_past_a_request():
     assert _meta(_params(c), c, bt=bt)[0] == OK
 
 
+def test_params_keep_their_tensors_alive():
+    # the struct holds raw device pointers: make_params keeps the tensors
+    # they point into, so params built from temporaries stay valid
+    import gc
+    import weakref
+    c = _case()
+    sl = c["sl"].clone()
+    cuq = c["cuq"].clone()
+    watch = [weakref.ref(sl), weakref.ref(cuq)]
+    p = B.make_params(c["q"], c["kv"], None, c["bt"], sl, c["max_q"], c["max_kv"], 0.125, 1.0, c["B"],
+                      cuq, c["cukv"], c["W"], c["out"], c["layout"], None)
+    del sl, cuq
+    gc.collect()
+    assert all(w() is not None for w in watch)
+    assert p.seq_lens == watch[0]().data_ptr() and p.cum_seq_lens_q == watch[1]().data_ptr()
+    del p
+    gc.collect()
+    assert all(w() is None for w in watch)
+
+
 def test_device_metadata_check_rejects_arguments_on_the_host():
     # the entry point validates shapes and its result pointer before any
     # launch: these return without touching a device

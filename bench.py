@@ -146,23 +146,61 @@ def _sysfs_sclk_now():
     return None
 
 
+_SMI = {"handle": None, "tried": False}
+
+
+def _smi_gfxclk_now():
+    """The graphics clock the power-management firmware reports now, averaged
+    over the XCDs (amdsmi gpu_metrics current_gfxclks, MHz), or None.  Unlike
+    the DPM level in pp_dpm_sclk (the clock the driver asks for), this follows
+    the clock the part actually runs at under load."""
+    if not _SMI["tried"]:
+        _SMI["tried"] = True
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            _SMI["handle"] = handles[0] if handles else None
+            _SMI["mod"] = amdsmi
+        except Exception:
+            _SMI["handle"] = None
+    if _SMI["handle"] is None:
+        return None
+    try:
+        m = _SMI["mod"].amdsmi_get_gpu_metrics_info(_SMI["handle"])
+    except Exception:
+        return None
+    clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float))]
+    if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
+        clks = [m["current_gfxclk"]]
+    return float(np.mean(clks)) if clks else None
+
+
 def sampled_clock(launch, seconds: float = 1.5):
     """The shader clock held under sustained load: the kernel is launched
-    back to back for about `seconds` while a host thread samples the
-    driver's current-clock readout every 5 ms (sysfs pp_dpm_sclk, the
-    starred level).  Returns {median, min, max, samples, source} or None
-    when the readout is not available."""
+    back to back for about `seconds` while a host thread samples the clock
+    every 10 ms: the firmware's per-XCD graphics clock (amdsmi gpu_metrics)
+    when it is readable, else the driver's current DPM level (sysfs
+    pp_dpm_sclk, the starred line).  The firmware's figure refreshes with a
+    lag, so samples from the first 40% of the window and idle readings
+    (< 500 MHz) are dropped.  Returns {median, min, max, samples, source,
+    dpm_level_median} or None when no readout is available."""
     import threading
     import torch
     samples = []
+    dpm = []
     stop = threading.Event()
+    use_smi = _smi_gfxclk_now() is not None
 
     def sample():
         while not stop.is_set():
-            v = _sysfs_sclk_now()
+            v = _smi_gfxclk_now() if use_smi else _sysfs_sclk_now()
             if v is not None:
                 samples.append(v)
-            time.sleep(0.005)
+            d = _sysfs_sclk_now()
+            if d is not None:
+                dpm.append(d)
+            time.sleep(0.010)
 
     th = threading.Thread(target=sample, daemon=True)
     t_end = time.perf_counter() + seconds
@@ -173,19 +211,23 @@ def sampled_clock(launch, seconds: float = 1.5):
         torch.cuda.synchronize()
     stop.set()
     th.join()
-    if not samples:
-        return None
     # the first samples can predate the ramp to load
-    tail = samples[len(samples) // 4:] or samples
-    return {"median_mhz": float(np.median(tail)), "min_mhz": int(min(tail)), "max_mhz": int(max(tail)),
-            "samples": len(tail), "source": "sysfs pp_dpm_sclk current level, sampled every 5 ms under "
-                                             "back-to-back launches"}
+    tail = [v for v in samples[(2 * len(samples)) // 5:] if v >= 500] or samples
+    if not tail:
+        return None
+    dtail = dpm[len(dpm) // 4:] or dpm
+    return {"median_mhz": round(float(np.median(tail)), 1), "min_mhz": round(float(min(tail)), 1),
+            "max_mhz": round(float(max(tail)), 1), "samples": len(tail),
+            "source": ("amdsmi gpu_metrics current_gfxclks (mean over the XCDs)" if use_smi
+                       else "sysfs pp_dpm_sclk current level") + ", sampled every 10 ms under back-to-back launches",
+            "dpm_level_median_mhz": float(np.median(dtail)) if dtail else None}
 
 
-def time_config(config: str, steps: int, warmup: int) -> dict:
+def time_config(config: str, steps: int, warmup: int, clock_seconds: float = 0.0) -> dict:
     """A second workload timed like the headline one (launches back to back,
     HIP events at the two ends of the region), for the extra keys of the
-    bench line."""
+    bench line; with clock_seconds > 0, also the clock it holds (sampled_clock)
+    and its fraction of the peak at that clock."""
     import torch
 
     import paged_kv_prefill_varlen_amd as ppa
@@ -215,9 +257,15 @@ def time_config(config: str, steps: int, warmup: int) -> dict:
     ms = e0.elapsed_time(e1) / steps
     flops = 4.0 * case["head_dim"] * case["num_qo_heads"] * causal_pairs(case)
     tf = flops / (ms * 1e-3) / 1e12
-    return {"workload": WORKLOAD_TEXT[config], "kernel_ms": round(ms, 5), "causal_gflop": round(flops / 1e9, 3),
-            "tflops": round(tf, 3), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-            "tokens_per_s": round(sum(case["q_lens"]) / (ms * 1e-3), 1), "steps": steps}
+    res = {"workload": WORKLOAD_TEXT[config], "kernel_ms": round(ms, 5), "causal_gflop": round(flops / 1e9, 3),
+           "tflops": round(tf, 3), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+           "tokens_per_s": round(sum(case["q_lens"]) / (ms * 1e-3), 1), "steps": steps}
+    if clock_seconds > 0:
+        clock = sampled_clock(lambda: ppa.ppa_paged_prefill_attention(p, stream.cuda_stream), clock_seconds)
+        res["clock"] = clock
+        if clock is not None:
+            res["frac_at_measured_clock"] = round(tf / (PEAK_BF16_TFLOPS * clock["median_mhz"] / 2400.0), 4)
+    return res
 
 
 def cpu_baseline(case, budget_s: float = 12.0):
@@ -500,7 +548,7 @@ def main():
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "mxfp4"],
                     help="output: bf16, or MXFP4 codes + E8M0 block scales")
     ap.add_argument("--o-sf-vec-size", type=int, default=32, choices=[16, 32])
-    ap.add_argument("--clock-seconds", type=float, default=1.5,
+    ap.add_argument("--clock-seconds", type=float, default=2.0,
                     help="seconds of back-to-back launches while sampling the shader clock (0: skip)")
     ap.add_argument("--no-llama3", dest="also_llama3", action="store_false",
                     help="chunked workload: skip timing the Llama-3-8B-shaped batch as well")
@@ -694,10 +742,8 @@ def main():
     line["clock"] = clock
     # the other reading of the gate's "config 2": the Llama-3-8B-shaped batch
     if args.config == "chunked" and args.also_llama3:
-        line["llama3_8b"] = time_config("llama3_8b", max(5, args.steps // 2), 3)
-        if clock is not None:
-            line["llama3_8b"]["frac_at_measured_clock"] = round(
-                line["llama3_8b"]["tflops"] / (PEAK_BF16_TFLOPS * clock["median_mhz"] / 2400.0), 4)
+        # (its own clock: it draws more power than the headline batch)
+        line["llama3_8b"] = time_config("llama3_8b", max(5, args.steps // 2), 3, args.clock_seconds)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(line), flush=True)

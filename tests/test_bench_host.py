@@ -55,3 +55,58 @@ def test_executed_at_least_causal(name):
     case = make_case(name)
     causal = 4.0 * case["head_dim"] * case["num_qo_heads"] * bench.causal_pairs(case)
     assert bench.executed_flops(case) >= causal > 0
+
+
+def _fake_clock_run(monkeypatch, smi_values, dpm_values, seconds=0.3):
+    """sampled_clock against scripted readouts: the firmware's per-XCD clock
+    (None: not readable) and the driver's DPM level, with launches that do
+    nothing and a synchronize that returns at once."""
+    import sys
+    import types
+
+    smi = iter(smi_values)
+    dpm = iter(dpm_values)
+    last = {"smi": None, "dpm": None}
+
+    def smi_now():
+        try:
+            last["smi"] = next(smi)
+        except StopIteration:
+            pass
+        return last["smi"]
+
+    def dpm_now():
+        try:
+            last["dpm"] = next(dpm)
+        except StopIteration:
+            pass
+        return last["dpm"]
+
+    fake_torch = types.SimpleNamespace(cuda=types.SimpleNamespace(synchronize=lambda *a: None))
+    monkeypatch.setitem(sys.modules, "torch", fake_torch)
+    monkeypatch.setattr(bench, "_smi_gfxclk_now", smi_now)
+    monkeypatch.setattr(bench, "_sysfs_sclk_now", dpm_now)
+    return bench.sampled_clock(lambda: None, seconds)
+
+
+def test_clock_sample_prefers_firmware_clock_and_drops_the_ramp(monkeypatch):
+    # the firmware's figure lags: idle readings first, then the loaded clock;
+    # the first 40 % of the window and readings below 500 MHz are dropped
+    smi = [2100.0] + [95.0] * 10 + [2094.0] * 1000
+    r = _fake_clock_run(monkeypatch, smi, [2109] * 1000)
+    assert r is not None
+    assert r["source"].startswith("amdsmi")
+    assert r["median_mhz"] == pytest.approx(2094.0)
+    assert r["min_mhz"] >= 500
+    assert r["dpm_level_median_mhz"] == pytest.approx(2109.0)
+
+
+def test_clock_sample_falls_back_to_the_dpm_level(monkeypatch):
+    r = _fake_clock_run(monkeypatch, [None] * 1000, [2372] * 1000)
+    assert r is not None
+    assert r["source"].startswith("sysfs pp_dpm_sclk")
+    assert r["median_mhz"] == pytest.approx(2372.0)
+
+
+def test_clock_sample_without_any_readout(monkeypatch):
+    assert _fake_clock_run(monkeypatch, [None] * 1000, [None] * 1000) is None

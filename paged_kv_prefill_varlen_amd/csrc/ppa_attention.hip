@@ -930,16 +930,18 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
       }
     __builtin_amdgcn_sched_barrier(0);
   };
-  i32x8 pf8;
+  i32x8 pf8 = {};
   // fp8 path: row sums of the rounded weights, as an MFMA of P against an
   // all-ones operand (e4m3fn 1.0 = 0x38): every element of lane (row, half)
   // is the row's sum over the tile's 64 keys, exact in fp32
   f32x16 lacc = {};
-  const int ones8 = 0x38383838;
+  __shared__ __attribute__((aligned(16))) int ones_lds[8];
   auto gemm_pv = [&](int j) {
     if constexpr (T::F8MMA) {
       for (int md = 0; md < MD; ++md) oacc[md] = mfma32_fp8(vf8[md], pf8, oacc[md]);
-      lacc = mfma32_fp8(i32x8{ones8, ones8, ones8, ones8, ones8, ones8, ones8, ones8}, pf8, lacc);
+      // (the all-ones operand is read from LDS: held in registers it is
+      // rebuilt with eight moves per tile, VALU slots this path is short of)
+      lacc = mfma32_fp8(*reinterpret_cast<const i32x8*>(ones_lds), pf8, lacc);
       return;
     }
     for (int ks = 0; ks < 4; ++ks)
@@ -1006,7 +1008,11 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
         for (int q = 0; q < 4; ++q) {
           float p[4];
           for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][4 * q + e], c, -mb));
-          int code = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          // (the first conversion keeps the upper half of its "old" operand,
+          // which the second overwrites: any value will do, and the previous
+          // tile's code, already in the register the MFMA operand needs,
+          // costs no copy)
+          int code = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pf8[4 * mt + q], false);
           code = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], code, true);
           pf8[4 * mt + q] = code;
         }
@@ -1073,6 +1079,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int item) {
     stage_fetch(lo, id0);
     if (lo + 1 <= hi) stage_fetch(lo + 1, id1);
     load_q8();   // after the first copies: its conversion waits for its loads
+    if (threadIdx.x < 8) ones_lds[threadIdx.x] = 0x38383838;   // e4m3fn 1.0 x 4, published by the first barrier
     for (int j = lo; j <= hi; j += 2) {
       wait_vmcnt<0>();
       __syncthreads();

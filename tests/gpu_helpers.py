@@ -102,3 +102,18 @@ def assert_close(got, want, rows, fp8=False, what=""):
     if not fp8:
         assert mean <= TOL_BF16_MEAN, f"{what}: mean |err| {mean:.3e} > {TOL_BF16_MEAN}"
     return mx, mean
+
+
+# lse = log(sum of bf16-rounded weights) + max: the rounding of each weight
+# (relative 2^-9) bounds the sum's relative error, so |d lse| <= ~2e-3.
+TOL_LSE = 5e-3
+
+
+def lse_close(lse, want, written, what=""):
+    """Max |lse - oracle| over the written rows, asserted <= TOL_LSE."""
+    got = lse.detach().cpu().numpy()[written]
+    w = want[written]
+    assert np.isfinite(got).all(), f"{what}: non-finite lse"
+    err = np.abs(got - w).max() if got.size else 0.0
+    assert err <= TOL_LSE, f"{what}: lse max |err| {err:.3e}"
+    return err

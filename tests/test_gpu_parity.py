@@ -17,8 +17,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (assert_close, errors, guard_rows_untouched, run_gpu, split_workspace, to_device,
-                         workspace)
+from gpu_helpers import (assert_close, errors, guard_rows_untouched, lse_close, run_gpu, split_workspace,
+                         to_device, workspace)
 from oracle.case_io import decode_tensor, oracle_inputs, run_oracle, run_oracle_lse, run_oracle_rows
 from workloads import make_case, make_custom_case
 from workloads.cases import relayout, to_flat_page_table
@@ -268,7 +268,7 @@ def test_sink_far_above_the_logits():
         out = run_gpu(d, lse=lse, kv_splits=splits)
         torch.cuda.synchronize()
         mx, mean = assert_close(out, want, written, what=f"big sink S={splits}")
-        err = _lse_close(lse, want_lse, written, f"big sink S={splits}")
+        err = lse_close(lse, want_lse, written, f"big sink S={splits}")
         _say(f"  big sink S={splits}: max {mx:.2e} lse err {err:.2e}")
 
 
@@ -439,10 +439,6 @@ def test_flat_page_table_gather():
 # log-sum-exp output, split-KV and the merge of partial states
 # --------------------------------------------------------------------------
 
-# lse = log(sum of bf16-rounded weights) + max: the rounding of each weight
-# (relative 2^-9) bounds the sum's relative error, so |d lse| <= ~2e-3.
-TOL_LSE = 5e-3
-
 LSE_CASES = ["g2_d64_nhd_combined", "g8_window0_sinks", "g16_window63_sinks", "empty_requests",
              "long_prefix", "window_many_tiles", "neg_bmm1", "zero_bmm1", "fp8_d64_nhd_window_sinks"]
 
@@ -450,15 +446,6 @@ LSE_CASES = ["g2_d64_nhd_combined", "g8_window0_sinks", "g16_window63_sinks", "e
 def _edge(name):
     return make_custom_case(name=name, batch=len(EDGE[name]["q_lens"]), seed=zlib.crc32(name.encode()) % 10000,
                             **EDGE[name])
-
-
-def _lse_close(lse, want, written, what):
-    got = lse.detach().cpu().numpy()[written]
-    w = want[written]
-    assert np.isfinite(got).all(), f"{what}: non-finite lse"
-    err = np.abs(got - w).max() if got.size else 0.0
-    assert err <= TOL_LSE, f"{what}: lse max |err| {err:.3e}"
-    return err
 
 
 @pytest.mark.parametrize("name", LSE_CASES)
@@ -472,7 +459,7 @@ def test_lse_output(name):
     plain = run_gpu(d)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), plain.view(torch.int16)), "lse output changed the output"
-    err = _lse_close(lse, want_lse, written, name)
+    err = lse_close(lse, want_lse, written, name)
     assert torch.isnan(lse.cpu()[~torch.from_numpy(written)]).all(), "lse written outside the requests"
     _say(f"  {name}: lse max err {err:.2e}")
 
@@ -494,7 +481,7 @@ def test_split_kv(name, splits):
     torch.cuda.synchronize()
     assert guard_rows_untouched(out, written)
     mx, mean = assert_close(out, want, written, fp8=case["kv_dtype"] != "bf16", what=f"{name} S={splits}")
-    err = _lse_close(lse, want_lse, written, f"{name} S={splits}")
+    err = lse_close(lse, want_lse, written, f"{name} S={splits}")
     _say(f"  {name} S={splits}: max {mx:.2e} mean {mean:.2e} lse {err:.2e}")
 
 
@@ -567,7 +554,7 @@ def test_decode_config(splits):
     out = run_gpu(d, lse=lse, kv_splits=splits)
     torch.cuda.synchronize()
     mx, mean = assert_close(out, want, written, what=f"decode S={splits}")
-    err = _lse_close(lse, want_lse, written, f"decode S={splits}")
+    err = lse_close(lse, want_lse, written, f"decode S={splits}")
     _say(f"  decode S={splits}: max {mx:.2e} mean {mean:.2e} lse {err:.2e}")
 
 

@@ -9,6 +9,9 @@ bf16 or fp8 (e4m3fn) caches and, for a third of the seeds, split-KV with two
 or three chunks.  Every written row is compared with the oracle at the
 stated tolerances, rows outside the requests must stay untouched, and the
 persistent and one-workgroup-per-item schedules must agree bit for bit.
+The log-sum-exp output is checked against the oracle's on every seed (and,
+with split-KV, the merged one too); asking for it must not change a bit of
+the output.
 """
 from __future__ import annotations
 
@@ -18,8 +21,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import assert_close, guard_rows_untouched, run_gpu, to_device, workspace
-from oracle.case_io import run_oracle
+from gpu_helpers import assert_close, guard_rows_untouched, lse_close, run_gpu, to_device, workspace
+from oracle.case_io import run_oracle, run_oracle_lse
 from workloads import make_custom_case
 
 pytestmark = pytest.mark.gpu
@@ -57,17 +60,25 @@ def test_random_config_parity(seed):
                                                   "kv_layout", "kv_form", "kv_dtype", "window_left", "sinks")},
           case["q_lens"], case["kv_lens"], "splits", splits, file=sys.stderr, flush=True)
     want, written = run_oracle(case)
+    want_lse = run_oracle_lse(case)
     d = to_device(case)
     fp8 = case["kv_dtype"] != "bf16"
     out = run_gpu(d)
     grid = run_gpu(d, schedule="grid")
+    lse = torch.full(tuple(d["query"].shape[:2]), float("nan"), dtype=torch.float32, device="cuda")
+    with_lse = run_gpu(d, lse=lse)
     torch.cuda.synchronize()
     assert guard_rows_untouched(out, written), "rows outside the requests were written"
     assert_close(out, want, written, fp8=fp8, what=spec["name"])
     assert torch.equal(out.view(torch.int16), grid.view(torch.int16)), "persistent != grid schedule"
+    assert torch.equal(out.view(torch.int16), with_lse.view(torch.int16)), "the lse output changed the output"
+    lse_close(lse, want_lse, written, spec["name"])
+    assert torch.isnan(lse.cpu()[~torch.from_numpy(written)]).all(), "lse written outside the requests"
     assert not workspace().any(), "scheduler workspace not returned to zero"
     if splits:
-        sp = run_gpu(d, kv_splits=splits)
+        sp_lse = torch.full_like(lse, float("nan"))
+        sp = run_gpu(d, kv_splits=splits, lse=sp_lse)
         torch.cuda.synchronize()
         assert guard_rows_untouched(sp, written), "split-KV wrote rows outside the requests"
         assert_close(sp, want, written, fp8=fp8, what=f"{spec['name']} kv_splits={splits}")
+        lse_close(sp_lse, want_lse, written, f"{spec['name']} kv_splits={splits}")

@@ -29,6 +29,9 @@ PPA_PAGE_TABLE_PADDED = 0
 PPA_PAGE_TABLE_CSR = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
+# The in-tree build by default; PPA_LIBRARY names another build of the same
+# C ABI (e.g. to time two builds of the kernels against each other).  Either
+# way the call goes to a HIP library: there is no other implementation.
 _LIB_PATH = os.environ.get("PPA_LIBRARY", os.path.join(_HERE, "_lib", "libppa.so"))
 
 

@@ -506,6 +506,9 @@ template <int D, int VEC>
 __device__ __forceinline__ void store_mxfp4_row(const f32x16* oacc, float inv, float g, uint8_t* orow,
                                                 uint8_t* sfrow, int half) {
   constexpr int GB = VEC / 8;   // 8-dim groups per block
+  // codes[G]: this lane's four codes (16 bits) of 8-dim group G of the row,
+  // i.e. dims 8 G + 4 half .. + 3
+  uint32_t codes[D / 8];
   for (int b = 0; b < D / VEC; ++b) {
     const int md = b * VEC / 32;
     const int g0 = (b * VEC % 32) / 8;
@@ -520,12 +523,28 @@ __device__ __forceinline__ void store_mxfp4_row(const f32x16* oacc, float inv, f
     const uint32_t sb = mx_scale_byte(amax);
     const float sc = mx_scale_operand(sb);
     for (int gg = 0; gg < GB; ++gg) {
-      uint32_t w = mx_pack4(y[gg][0], y[gg][1], y[gg][2], y[gg][3], sc);
-      w = sb == 255u ? 0u : w;
-      const int d = md * 32 + 8 * (g0 + gg) + 4 * half;
-      *reinterpret_cast<uint16_t*>(orow + d / 2) = static_cast<uint16_t>(w);
+      const uint32_t w = mx_pack4(y[gg][0], y[gg][1], y[gg][2], y[gg][3], sc);
+      codes[b * GB + gg] = sb == 255u ? 0u : (w & 0xffffu);
     }
     if (half == 0) sfrow[b] = static_cast<uint8_t>(sb);
+  }
+  // Each 64-dim chunk (32 bytes of the row): half 0 stores groups 0-3 and
+  // half 1 groups 4-7, each group whole (its two halves' codes side by
+  // side), as one 16-byte store per lane instead of eight 2-byte ones.  The
+  // lanes exchange (own group k, own group k + 4) words with their partner
+  // (v_permlane32_swap: lanes 32-63 of the first register with lanes 0-31
+  // of the second, so that each lane ends with its partner's word in one of
+  // them).
+  for (int c = 0; c < D / 64; ++c) {
+    uint32_t res[4];
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t x = codes[8 * c + k] | (codes[8 * c + k + 4] << 16);
+      uint32_t r0 = x, r1 = x;
+      asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(r0), "+v"(r1));
+      const uint32_t partner = half ? r0 : r1;
+      res[k] = half ? ((partner >> 16) | (x & 0xffff0000u)) : ((x & 0xffffu) | (partner << 16));
+    }
+    *reinterpret_cast<u32x4*>(orow + c * 32 + 16 * half) = u32x4{res[0], res[1], res[2], res[3]};
   }
 }
 

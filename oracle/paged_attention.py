@@ -259,7 +259,7 @@ def append_paged_kv(planes, kv_layout: str, page_size: int, k_new_codes: np.ndar
 # normalized output and log-denominator over a subset of the keys; merging
 # weights each part by exp(lse_part - lse_total).  Read from the sibling
 # decode call of the TokenSpeed backend source (the decode path of the
-# TRT-LLM MHA backend) and the split-KV row of the survey; the sink, a term
+# TRT-LLM MHA backend), which splits the key set and merges; the sink, a term
 # of the denominator only (API page, parameter sinks), is added once, at
 # the merge.
 

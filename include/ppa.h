@@ -483,7 +483,7 @@ size_t ppa_noalloc_scratch_bytes(void);
  */
 int32_t ppa_merge_attention_states(const ppa_merge_params* m, void* stream);
 
-/* sizeof(ppa_merge_params) of this build, for bindings. */
+/* sizeof(ppa_merge_params) of this library, for bindings. */
 size_t ppa_merge_params_size(void);
 
 /*
@@ -502,7 +502,7 @@ int32_t ppa_validate_append(const ppa_params* cache, const ppa_append_params* a,
  */
 int32_t ppa_append_paged_kv(const ppa_params* cache, const ppa_append_params* a, void* stream);
 
-/* sizeof(ppa_append_params) of this build, for bindings. */
+/* sizeof(ppa_append_params) of this library, for bindings. */
 size_t ppa_append_params_size(void);
 
 /*

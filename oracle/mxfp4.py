@@ -5,7 +5,7 @@ dense one (FlashInfer API page for trtllm_batch_context_with_kv_cache,
 parameters ``out``, ``out_dtype`` (the FP4 string), ``o_sf_scale`` - a scale
 applied to the output's scale factors - and ``o_sf_vec_size`` - the number of
 elements one scale factor covers).  The pages name NVIDIA's FP4 format and
-define nothing further; this build re-targets the output to the OCP
+define nothing further; this library re-targets the output to the OCP
 Microscaling (MX) FP4 format that gfx950 supports, and takes these readings:
 
 * element format E2M1: 1 sign, 2 exponent bits (bias 1), 1 mantissa bit, no

@@ -136,6 +136,63 @@ def test_edge_case_parity(name):
     assert not workspace().any(), "scheduler workspace not returned to zero"
 
 
+# Pools larger than 4 GiB: the used pages copied to the top of the pool, so
+# that every page the kernels read starts past byte 2^32 of its plane.
+POOL_4G_CASES = {
+    "hnd_combined_bf16_d128": dict(num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=16, kv_layout="HND",
+                                   kv_form="combined", q_lens=(150, 70), prefix_lens=(200, 0)),
+    "nhd_split_fp8_d128": dict(num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=32, kv_layout="NHD",
+                               kv_form="split", kv_dtype="fp8_e4m3fn", q_lens=(300, 40), prefix_lens=(100, 500)),
+    "nhd_split_bf16_d64_window": dict(num_qo_heads=16, num_kv_heads=2, head_dim=64, page_size=8, kv_layout="NHD",
+                                      kv_form="split", window_left=90, sinks=True, q_lens=(200,),
+                                      prefix_lens=(150,)),
+}
+
+
+def _pool_above_4gib(pool: torch.Tensor):
+    """A pool of more than 4 GiB whose top pages hold `pool`'s pages; returns
+    it and the page-id offset of the copy."""
+    page_bytes = pool[0].numel() * pool.element_size()
+    off = (1 << 32) // page_bytes + 7
+    big = torch.empty((off + pool.shape[0],) + tuple(pool.shape[1:]), dtype=pool.dtype, device=pool.device)
+    big[off:] = pool
+    return big, off
+
+
+@pytest.mark.parametrize("name", sorted(POOL_4G_CASES))
+def test_pages_beyond_4gib(name):
+    """Page ids whose byte offsets lie past 4 GiB of the pool (page addresses
+    are formed in 64 bits): the output equals, bit for bit, that of the same
+    pages at the bottom of a small pool, and the oracle's within tolerance.
+    The fp8 cache at head_dim 128 is also run on the fp8 MFMA."""
+    spec = POOL_4G_CASES[name]
+    case = make_custom_case(name=name, batch=len(spec["q_lens"]), seed=zlib.crc32(name.encode()) % 10000, **spec)
+    _say("pool > 4 GiB", name, case["q_lens"], case["kv_lens"])
+    want, written = run_oracle(case)
+    d = to_device(case)
+    kv = d["kv_cache"]
+    if isinstance(kv, tuple):
+        (bk, off), (bv, off_v) = _pool_above_4gib(kv[0]), _pool_above_4gib(kv[1])
+        assert off == off_v
+        big_kv = (bk, bv)
+    else:
+        big_kv, off = _pool_above_4gib(kv)
+    big = dict(d, kv_cache=big_kv, block_tables=d["block_tables"] + off)
+    fp8_mma = [False, True] if case["kv_dtype"] != "bf16" and case["head_dim"] == 128 else [False]
+    for f8 in fp8_mma:
+        small_out = run_gpu(d, fp8_compute=f8)
+        out = run_gpu(big, fp8_compute=f8)
+        torch.cuda.synchronize()
+        assert guard_rows_untouched(out, written), "rows outside the requests were written"
+        assert torch.equal(out.view(torch.int16), small_out.view(torch.int16)), "pool offset changed the output"
+        if not f8:
+            mx, mean = assert_close(out, want, written, fp8=case["kv_dtype"] != "bf16", what=name)
+            _say(f"  max {mx:.2e} mean {mean:.2e}")
+    assert not workspace().any(), "scheduler workspace not returned to zero"
+    del big, big_kv
+    torch.cuda.empty_cache()
+
+
 def test_tiny_config_full():
     case = make_case("tiny")
     want, written = run_oracle(case)

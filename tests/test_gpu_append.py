@@ -126,3 +126,49 @@ def test_append_device_scales_and_then_attend():
     torch.cuda.synchronize()
     assert guard_rows_untouched(out, written)
     assert_close(out, want, written, fp8=True, what="append then attend")
+
+
+def _pool_above_4gib(pool: torch.Tensor):
+    """A pool of more than 4 GiB whose top pages hold `pool`'s pages; returns
+    it and the page-id offset of the copy."""
+    page_bytes = pool[0].numel() * pool.element_size()
+    off = (1 << 32) // page_bytes + 7
+    big = torch.empty((off + pool.shape[0],) + tuple(pool.shape[1:]), dtype=pool.dtype, device=pool.device)
+    big[off:] = pool
+    return big, off
+
+
+@pytest.mark.parametrize("name", ["bf16_hnd_split_d128_p16", "fp8_nhd_combined_d64_p1"])
+def test_append_beyond_4gib(name):
+    """Slots in pages whose byte offsets lie past 4 GiB of the pool (the page
+    address is formed in 64 bits): the appended pages hold exactly the
+    oracle's bytes."""
+    import paged_kv_prefill_varlen_amd as ppa
+    var = VARIANTS[name]
+    case = make_custom_case(name=name, batch=2, num_qo_heads=4, num_kv_heads=2, q_lens=(40, 90),
+                            prefix_lens=(30, 17), seed=zlib.crc32(name.encode()) % 10000 + 1, **var)
+    fp8 = var.get("kv_dtype") == "fp8_e4m3fn"
+    slots = _slots(case)
+    n = len(slots)
+    k_new = _new_values(n, 2, var["head_dim"], 3, crafted=fp8)
+    v_new = _new_values(n, 2, var["head_dim"], 4, crafted=fp8)
+    want = append_paged_kv(_planes_codes(case["kv_cache"]), var["kv_layout"], var["page_size"], as_codes(k_new),
+                           as_codes(v_new), slots, "fp8" if fp8 else "bf16", 1.0, 1.0)
+    d = to_device(case)
+    kv = d["kv_cache"]
+    if isinstance(kv, tuple):
+        (bk, off), (bv, off_v) = _pool_above_4gib(kv[0]), _pool_above_4gib(kv[1])
+        assert off == off_v
+        big = (bk, bv)
+    else:
+        big, off = _pool_above_4gib(kv)
+    _say("append, pool > 4 GiB", name, "page offset", off)
+    big_slots = torch.from_numpy(slots + off * var["page_size"]).cuda()
+    ppa.append_paged_kv_cache(k_new.cuda(), v_new.cuda(), big_slots, big, var["kv_layout"], 1.0, 1.0)
+    torch.cuda.synchronize()
+    top = tuple(t[off:].cpu() for t in big) if isinstance(big, tuple) else big[off:].cpu()
+    got = _planes_codes(top)
+    for kv_idx in range(2):
+        assert np.array_equal(got[kv_idx], want[kv_idx]), f"{name} plane {kv_idx}: appended bytes differ"
+    del big
+    torch.cuda.empty_cache()

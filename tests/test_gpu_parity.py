@@ -92,6 +92,8 @@ EDGE = {
                            q_lens=(0, 50, 0, 3), prefix_lens=(30, 0, 0, 0), extra_tokens=5),
     "page_size_1": dict(num_qo_heads=8, num_kv_heads=2, head_dim=64, page_size=1,
                         q_lens=(70,), prefix_lens=(10,)),
+    "page_size_65536": dict(num_qo_heads=8, num_kv_heads=2, head_dim=64, page_size=65536, kv_layout="NHD",
+                            q_lens=(300, 50), prefix_lens=(2000, 0), spare_pages=1),
     "page_size_128": dict(num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=128,
                           q_lens=(129,), prefix_lens=(300,)),
     "single_token": dict(num_qo_heads=4, num_kv_heads=4, head_dim=128, page_size=16,

@@ -92,6 +92,11 @@ EDGE = {
                            q_lens=(0, 50, 0, 3), prefix_lens=(30, 0, 0, 0), extra_tokens=5),
     "page_size_1": dict(num_qo_heads=8, num_kv_heads=2, head_dim=64, page_size=1,
                         q_lens=(70,), prefix_lens=(10,)),
+    "g128_mqa_eight_head_groups": dict(num_qo_heads=128, num_kv_heads=1, head_dim=128, page_size=32,
+                                       q_lens=(90, 17), prefix_lens=(150, 300)),
+    "batch_300_short": dict(num_qo_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
+                            q_lens=tuple((7 * i) % 13 for i in range(300)),
+                            prefix_lens=tuple((11 * i) % 41 for i in range(300))),
     "page_size_65536": dict(num_qo_heads=8, num_kv_heads=2, head_dim=64, page_size=65536, kv_layout="NHD",
                             q_lens=(300, 50), prefix_lens=(2000, 0), spare_pages=1),
     "page_size_128": dict(num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=128,

@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (assert_close, errors, guard_rows_untouched, lse_close, run_gpu, split_workspace,
+from gpu_helpers import (GUARD, assert_close, errors, guard_rows_untouched, lse_close, run_gpu, split_workspace,
                          to_device, workspace)
 from oracle.case_io import decode_tensor, oracle_inputs, run_oracle, run_oracle_lse, run_oracle_rows
 from workloads import make_case, make_custom_case
@@ -198,6 +198,42 @@ def test_pages_beyond_4gib(name):
     assert not workspace().any(), "scheduler workspace not returned to zero"
     del big, big_kv
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+def test_strided_query_output_and_table(layout):
+    """Q as a view into a fused QKV buffer (token stride (Hq + 2 Hkv) D), the
+    output as a view with a padded head stride, the block table as a column
+    slice of a wider table: the same bits as the dense tensors, the padding
+    untouched, and the oracle's output within tolerance."""
+    name = f"strided_{layout}"
+    case = make_custom_case(name=name, batch=3, num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                            kv_layout=layout, q_lens=(70, 0, 131), prefix_lens=(40, 9, 200),
+                            seed=zlib.crc32(name.encode()) % 10000)
+    _say("strided views", name, case["q_lens"], case["kv_lens"])
+    want, written = run_oracle(case)
+    d = to_device(case)
+    q = d["query"]
+    T, Hq, D = q.shape
+    Hkv = case["num_kv_heads"]
+    qkv = torch.randn((T, Hq + 2 * Hkv, D), device=q.device).to(q.dtype)
+    qkv[:, :Hq] = q
+    q_view = qkv[:, :Hq]
+    out_buf = torch.full((T, Hq, D + 8), GUARD, dtype=torch.int16, device=q.device)
+    out_view = out_buf[:, :, :D].view(torch.bfloat16)
+    bt = d["block_tables"]
+    bt_wide = torch.full((bt.shape[0], bt.shape[1] + 3), 1 << 30, dtype=bt.dtype, device=bt.device)
+    bt_wide[:, :bt.shape[1]] = bt
+    bt_view = bt_wide[:, :bt.shape[1]]
+    assert not q_view.is_contiguous() and not out_view.is_contiguous() and not bt_view.is_contiguous()
+    dense = run_gpu(d)
+    strided = run_gpu(dict(d, query=q_view, block_tables=bt_view), out=out_view)
+    torch.cuda.synchronize()
+    dense_raw = dense.view(torch.int16)
+    assert torch.equal(out_buf[:, :, :D], dense_raw), "strided views changed the output"
+    assert bool((out_buf[:, :, D:] == GUARD).all()), "the output's head padding was written"
+    mx, mean = assert_close(dense, want, written, what=name)
+    _say(f"  max {mx:.2e} mean {mean:.2e}")
 
 
 def test_tiny_config_full():
